@@ -1,0 +1,23 @@
+"""Frame-wise Gated DeltaNet forward scan for AMD MI355X (gfx950).
+
+The compute path is libgdn.so (HIP kernels behind the C ABI in include/gdn.h);
+``api`` marshals torch tensors across it.  ``inputs`` draws seeded synthetic
+workloads and is importable without a GPU.
+"""
+from . import inputs  # noqa: F401
+
+__all__ = ["frame_scan_fwd", "frame_step", "profile_begin", "profile_end", "workspace_size",
+           "make_desc", "GdnError", "inputs"]
+
+
+def __getattr__(name):
+    # The HIP binding loads on first use so that CPU-only tools (the input
+    # recipe, the oracle tests) can import the package without a GPU.
+    if name in ("frame_scan_fwd", "frame_step", "profile_begin", "profile_end",
+                "workspace_size", "make_desc", "alloc_workspace"):
+        from . import api
+        return getattr(api, name)
+    if name == "GdnError":
+        from ._lib import GdnError
+        return GdnError
+    raise AttributeError(name)

@@ -1,0 +1,341 @@
+// C ABI of the frame-wise GDN forward scan: argument checks, launch planning
+// and kernel launches.  Declarations and the contract are in include/gdn.h.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <mutex>
+#include <vector>
+
+#include "../../include/gdn.h"
+#include "gdn_kernels.hpp"
+
+namespace {
+
+using gdn::ScanArgs;
+
+constexpr int kVersion = 10000;  // 1.0.0
+
+enum KernelKind { K_GRAM = 0, K_STATE = 1, K_OUTPUT = 2, K_COPY = 3 };
+const char* const kKernelNames[GDN_NUM_KERNELS] = {"frame_gram", "state_scan", "frame_output",
+                                                   "state_copy"};
+
+// ---------------------------------------------------------------- profiling
+struct Profiler {
+    bool on = false;
+    std::vector<hipEvent_t> pool;   // created lazily, reused across sessions
+    std::vector<int> kind;          // kernel kind of each recorded pair
+    size_t used = 0;                // pairs used in this session
+};
+Profiler g_prof;
+std::mutex g_prof_mu;
+
+struct ProfScope {
+    hipEvent_t end = nullptr;
+    hipStream_t stream;
+    ProfScope(KernelKind k, hipStream_t s) : stream(s) {
+        if (!g_prof.on) return;
+        std::lock_guard<std::mutex> lk(g_prof_mu);
+        if (g_prof.used >= GDN_PROFILE_MAX_LAUNCHES) return;
+        const size_t i = g_prof.used;
+        while (g_prof.pool.size() < 2 * (i + 1)) {
+            hipEvent_t e;
+            if (hipEventCreate(&e) != hipSuccess) return;
+            g_prof.pool.push_back(e);
+        }
+        if (g_prof.kind.size() < i + 1) g_prof.kind.resize(i + 1);
+        g_prof.kind[i] = k;
+        g_prof.used = i + 1;
+        (void)hipEventRecord(g_prof.pool[2 * i], s);
+        end = g_prof.pool[2 * i + 1];
+    }
+    ~ProfScope() {
+        if (end) (void)hipEventRecord(end, stream);
+    }
+};
+
+// ---------------------------------------------------------------- device checks
+struct DevInfo {
+    bool known = false;
+    bool ok = false;
+    int cus = 0;
+};
+std::mutex g_dev_mu;
+DevInfo g_dev[64];
+
+gdn_status check_device(int* cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return GDN_ERR_NO_DEVICE;
+    if (dev >= 64) return GDN_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    DevInfo& di = g_dev[dev];
+    if (!di.known) {
+        hipDeviceProp_t p;
+        if (hipGetDeviceProperties(&p, dev) != hipSuccess) return GDN_ERR_NO_DEVICE;
+        di.ok = strncmp(p.gcnArchName, "gfx950", 6) == 0;
+        di.cus = p.multiProcessorCount;
+        di.known = true;
+    }
+    if (cus) *cus = di.cus;
+    return di.ok ? GDN_OK : GDN_ERR_UNSUPPORTED;
+}
+
+// ---------------------------------------------------------------- planning
+struct Plan {
+    int D = 0;
+    int esz = 0;             // bytes per q/k/v/o element
+    int64_t units = 0;       // B*H
+    int Fc = 0;              // frames per launch chunk
+    size_t item_bytes = 0;   // workspace per (b, h, frame)
+    size_t ws_bytes = 0;
+};
+
+bool dim_ok(int D) { return D == 16 || D == 32 || D == 64 || D == 128; }
+
+gdn_status check_desc(const gdn_desc* d, bool step, Plan* p) {
+    if (!d) return GDN_ERR_INVALID_ARG;
+    if (d->B < 0 || d->H < 0 || d->F < 0 || d->N < 0) return GDN_ERR_INVALID_ARG;
+    if (d->io_dtype != GDN_BF16 && d->io_dtype != GDN_F32) return GDN_ERR_INVALID_ARG;
+    if ((d->flags & ~GDN_FLAG_GATES_ARE_LOGITS) != 0) return GDN_ERR_INVALID_ARG;
+    if (!(d->eps > 0.0f) || !isfinite(d->eps)) return GDN_ERR_INVALID_ARG;
+    if (step && d->F != 1) return GDN_ERR_INVALID_ARG;
+    if (d->Dk < 1 || d->Dv < 1) return GDN_ERR_INVALID_ARG;
+    if (d->Dk != d->Dv || !dim_ok(d->Dk)) return GDN_ERR_UNSUPPORTED;
+    // element counts must fit comfortably in 64-bit byte offsets
+    const double tok = (double)d->B * d->F * d->N * d->H * d->Dk;
+    if (tok > 1e15) return GDN_ERR_INVALID_ARG;
+    p->D = d->Dk;
+    p->esz = d->io_dtype == GDN_BF16 ? 2 : 4;
+    p->units = (int64_t)d->B * d->H;
+    p->Fc = d->F;  // whole clip per launch
+    p->item_bytes = (size_t)12 * p->D * p->D;
+    p->ws_bytes = (p->units > 0 && d->F > 0) ? (size_t)p->units * p->Fc * p->item_bytes : 0;
+    return GDN_OK;
+}
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+Range rng(const void* ptr, size_t bytes) {
+    const uintptr_t b = (uintptr_t)ptr;
+    return Range{b, b + bytes};
+}
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
+bool aligned(const void* p, uintptr_t al) { return ((uintptr_t)p & (al - 1)) == 0; }
+
+template <typename T, int D>
+gdn_status launch_all(const Plan& p, ScanArgs a, hipStream_t stream, int cus) {
+    const int units = (int)p.units;
+    for (int f0 = 0; f0 < a.F; f0 += p.Fc) {
+        a.f0 = f0;
+        a.Fc = a.F - f0 < p.Fc ? a.F - f0 : p.Fc;
+        const int items = units * a.Fc;
+        {
+            ProfScope ps(K_GRAM, stream);
+            hipLaunchKernelGGL((gdn::frame_gram_kernel<T, D>), dim3(items), dim3(256), 0, stream, a);
+        }
+        if (hipGetLastError() != hipSuccess) return GDN_ERR_LAUNCH;
+        {
+            using SC = gdn::StateCfg<T, D>;
+            const int grid = 8 * ((units + 7) / 8) * SC::RT;
+            ProfScope ps(K_STATE, stream);
+            hipLaunchKernelGGL((gdn::state_scan_kernel<T, D>), dim3(grid), dim3(SC::NW * 64), 0, stream,
+                               a);
+        }
+        if (hipGetLastError() != hipSuccess) return GDN_ERR_LAUNCH;
+        // chained chunks carry the state through S_out
+        a.S_in = a.S_out;
+        if (a.N > 0) {
+            // token ranges per frame: enough workgroups to cover every CU a few times
+            const int want = 4 * (cus > 0 ? cus : 256);
+            int tsplit = (want + items - 1) / items;
+            const int maxsplit = (a.N + 63) / 64;
+            if (tsplit > maxsplit) tsplit = maxsplit;
+            if (tsplit < 1) tsplit = 1;
+            int tchunk = (a.N + tsplit - 1) / tsplit;
+            tchunk = (tchunk + 15) / 16 * 16;
+            tsplit = (a.N + tchunk - 1) / tchunk;
+            a.tsplit = tsplit;
+            a.tchunk = tchunk;
+            ProfScope ps(K_OUTPUT, stream);
+            hipLaunchKernelGGL((gdn::frame_output_kernel<T, D>), dim3(items * tsplit), dim3(256), 0,
+                               stream, a);
+        }
+        if (hipGetLastError() != hipSuccess) return GDN_ERR_LAUNCH;
+    }
+    return GDN_OK;
+}
+
+template <typename T>
+gdn_status dispatch_d(const Plan& p, const ScanArgs& a, hipStream_t s, int cus) {
+    switch (p.D) {
+        case 16: return launch_all<T, 16>(p, a, s, cus);
+        case 32: return launch_all<T, 32>(p, a, s, cus);
+        case 64: return launch_all<T, 64>(p, a, s, cus);
+        case 128: return launch_all<T, 128>(p, a, s, cus);
+        default: return GDN_ERR_UNSUPPORTED;
+    }
+}
+
+gdn_status run(const gdn_desc* d, bool step, const void* q, const void* k, const void* v,
+               const float* beta, const float* alpha, const float* S0, void* o, float* S_final,
+               void* workspace, size_t workspace_bytes, void* stream_v) {
+    Plan p;
+    gdn_status st = check_desc(d, step, &p);
+    if (st != GDN_OK) return st;
+
+    const size_t ntok = (size_t)d->B * d->F * d->N * d->H;
+    const size_t tok_bytes = ntok * (size_t)p.D * p.esz;
+    const size_t beta_bytes = ntok * sizeof(float);
+    const size_t alpha_bytes = (size_t)d->B * d->F * d->H * sizeof(float);
+    const size_t state_bytes = (size_t)p.units * p.D * p.D * sizeof(float);
+
+    // required pointers
+    if (ntok > 0 && (!q || !k || !v || !beta || !o)) return GDN_ERR_INVALID_ARG;
+    if (alpha_bytes > 0 && !alpha) return GDN_ERR_INVALID_ARG;
+    // alignment
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+        return GDN_ERR_ALIGNMENT;
+    if (!aligned(beta, 4) || !aligned(alpha, 4)) return GDN_ERR_ALIGNMENT;
+    if (!aligned(S0, 16) || !aligned(S_final, 16)) return GDN_ERR_ALIGNMENT;
+    if (p.ws_bytes > 0) {
+        if (!workspace || workspace_bytes < p.ws_bytes) return GDN_ERR_WORKSPACE;
+        if (!aligned(workspace, 256)) return GDN_ERR_ALIGNMENT;
+    }
+    // aliasing: outputs must not overlap inputs, each other or the workspace
+    const Range rq = rng(q, q ? tok_bytes : 0), rk = rng(k, k ? tok_bytes : 0),
+                rv = rng(v, v ? tok_bytes : 0), rb = rng(beta, beta ? beta_bytes : 0),
+                ra = rng(alpha, alpha ? alpha_bytes : 0), rs0 = rng(S0, S0 ? state_bytes : 0),
+                ro = rng(o, o ? tok_bytes : 0), rsf = rng(S_final, S_final ? state_bytes : 0),
+                rw = rng(workspace, workspace ? p.ws_bytes : 0);
+    const Range ins[] = {rq, rk, rv, rb, ra, rs0};
+    for (const Range& x : ins) {
+        if (overlap(ro, x)) return GDN_ERR_ALIAS;
+        if (overlap(rw, x)) return GDN_ERR_ALIAS;
+    }
+    for (int i = 0; i < 5; ++i)
+        if (overlap(rsf, ins[i])) return GDN_ERR_ALIAS;
+    if (overlap(rsf, rs0) && S_final != S0) return GDN_ERR_ALIAS;
+    if (overlap(ro, rsf) || overlap(ro, rw) || overlap(rsf, rw)) return GDN_ERR_ALIAS;
+
+    // nothing to compute
+    if (p.units == 0) return GDN_OK;
+    if (d->F == 0 && !S_final) return GDN_OK;
+
+    int cus = 0;
+    st = check_device(&cus);
+    if (st != GDN_OK) return st;
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_v);
+
+    if (d->F == 0) {  // S_final <- S0 (or zeros)
+        if (S_final == S0) return GDN_OK;
+        const size_t n = (size_t)p.units * p.D * p.D;
+        ProfScope ps(K_COPY, stream);
+        hipLaunchKernelGGL(gdn::state_copy_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                           stream, S0, S_final, n);
+        return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+    }
+
+    ScanArgs a;
+    memset(&a, 0, sizeof(a));
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.beta = beta;
+    a.alpha = alpha;
+    a.S_in = S0;
+    a.o = o;
+    a.S_out = S_final;
+    a.S_out2 = nullptr;
+    a.ws = static_cast<unsigned char*>(workspace);
+    a.B = d->B;
+    a.H = d->H;
+    a.F = d->F;
+    a.N = d->N;
+    a.logits = (d->flags & GDN_FLAG_GATES_ARE_LOGITS) ? 1 : 0;
+    a.eps = d->eps;
+    a.tsplit = 1;
+    a.tchunk = 16;
+    if (p.Fc < d->F && !S_final) return GDN_ERR_INVALID_ARG;  // chunked carry needs S_final
+    return d->io_dtype == GDN_BF16 ? dispatch_d<uint16_t>(p, a, stream, cus)
+                                   : dispatch_d<float>(p, a, stream, cus);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t gdn_workspace_size(const gdn_desc* d) {
+    Plan p;
+    if (check_desc(d, false, &p) != GDN_OK) return 0;
+    return p.ws_bytes;
+}
+
+gdn_status gdn_frame_scan_fwd(const gdn_desc* d, const void* q, const void* k, const void* v,
+                              const float* beta, const float* alpha, const float* S0, void* o,
+                              float* S_final, void* workspace, size_t workspace_bytes, void* stream) {
+    return run(d, false, q, k, v, beta, alpha, S0, o, S_final, workspace, workspace_bytes, stream);
+}
+
+gdn_status gdn_frame_step(const gdn_desc* d, const void* q, const void* k, const void* v,
+                          const float* beta, const float* alpha, const float* S_in, void* o,
+                          float* S_out, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!S_out) return GDN_ERR_INVALID_ARG;
+    return run(d, true, q, k, v, beta, alpha, S_in, o, S_out, workspace, workspace_bytes, stream);
+}
+
+const char* gdn_status_string(gdn_status s) {
+    switch (s) {
+        case GDN_OK: return "ok";
+        case GDN_ERR_INVALID_ARG: return "invalid argument";
+        case GDN_ERR_UNSUPPORTED: return "unsupported configuration";
+        case GDN_ERR_ALIGNMENT: return "misaligned pointer";
+        case GDN_ERR_ALIAS: return "output aliases another buffer";
+        case GDN_ERR_WORKSPACE: return "workspace missing or too small";
+        case GDN_ERR_LAUNCH: return "kernel launch failed";
+        case GDN_ERR_NO_DEVICE: return "no HIP device";
+    }
+    return "unknown status";
+}
+
+int32_t gdn_version(void) { return kVersion; }
+
+gdn_status gdn_profile_begin(void) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof.used = 0;
+    g_prof.on = true;
+    return GDN_OK;
+}
+
+gdn_status gdn_profile_end(double* total_ms, int64_t* launches) {
+    std::vector<hipEvent_t> ev;
+    std::vector<int> kinds;
+    size_t used;
+    {
+        std::lock_guard<std::mutex> lk(g_prof_mu);
+        g_prof.on = false;
+        used = g_prof.used;
+        ev = g_prof.pool;
+        kinds = g_prof.kind;
+    }
+    for (int k = 0; k < GDN_NUM_KERNELS; ++k) {
+        if (total_ms) total_ms[k] = 0.0;
+        if (launches) launches[k] = 0;
+    }
+    for (size_t i = 0; i < used; ++i) {
+        if (hipEventSynchronize(ev[2 * i + 1]) != hipSuccess) return GDN_ERR_LAUNCH;
+        float ms = 0.0f;
+        if (hipEventElapsedTime(&ms, ev[2 * i], ev[2 * i + 1]) != hipSuccess) return GDN_ERR_LAUNCH;
+        if (total_ms) total_ms[kinds[i]] += ms;
+        if (launches) launches[kinds[i]] += 1;
+    }
+    return GDN_OK;
+}
+
+const char* gdn_kernel_name(int32_t k) {
+    return (k >= 0 && k < GDN_NUM_KERNELS) ? kKernelNames[k] : nullptr;
+}
+
+}  // extern "C"
