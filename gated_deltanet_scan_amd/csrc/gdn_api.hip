@@ -103,13 +103,17 @@ gdn_status check_desc(const gdn_desc* d, bool step, Plan* p) {
     if (step && d->F != 1) return GDN_ERR_INVALID_ARG;
     if (d->Dk < 1 || d->Dv < 1) return GDN_ERR_INVALID_ARG;
     if (d->Dk != d->Dv || !dim_ok(d->Dk)) return GDN_ERR_UNSUPPORTED;
-    // element counts must fit comfortably in 64-bit byte offsets
+    // element counts must fit comfortably in 64-bit byte offsets, and one
+    // frame of one tensor in the 32-bit offsets of a buffer resource
     const double tok = (double)d->B * d->F * d->N * d->H * d->Dk;
     if (tok > 1e15) return GDN_ERR_INVALID_ARG;
+    const double esz = d->io_dtype == GDN_BF16 ? 2.0 : 4.0;
+    if (((double)d->N + 1024.0) * d->H * d->Dk * esz >= 2147483648.0) return GDN_ERR_UNSUPPORTED;
     p->D = d->Dk;
     p->esz = d->io_dtype == GDN_BF16 ? 2 : 4;
     p->units = (int64_t)d->B * d->H;
-    p->Fc = d->F;  // whole clip per launch
+    // frames per launch chunk (state_scan stages the chunk's gates in LDS)
+    p->Fc = d->F < gdn::kMaxChunkFrames ? d->F : gdn::kMaxChunkFrames;
     p->item_bytes = (size_t)12 * p->D * p->D;
     p->ws_bytes = (p->units > 0 && d->F > 0) ? (size_t)p->units * p->Fc * p->item_bytes : 0;
     return GDN_OK;
@@ -134,7 +138,9 @@ gdn_status launch_all(const Plan& p, ScanArgs a, hipStream_t stream, int cus) {
         const int items = units * a.Fc;
         {
             ProfScope ps(K_GRAM, stream);
-            hipLaunchKernelGGL((gdn::frame_gram_kernel<T, D>), dim3(items), dim3(256), 0, stream, a);
+            // persistent: one workgroup per CU, each streaming its share of the items
+            const int grid = items < cus ? items : (cus > 0 ? cus : 256);
+            hipLaunchKernelGGL((gdn::frame_gram_kernel<T, D>), dim3(grid), dim3(512), 0, stream, a);
         }
         if (hipGetLastError() != hipSuccess) return GDN_ERR_LAUNCH;
         {
@@ -258,6 +264,7 @@ gdn_status run(const gdn_desc* d, bool step, const void* q, const void* k, const
     a.eps = d->eps;
     a.tsplit = 1;
     a.tchunk = 16;
+    a.tok_bytes = d->N > 0 ? (uint32_t)(((size_t)(d->N - 1) * d->H * p.D + p.D) * p.esz) : 0u;
     if (p.Fc < d->F && !S_final) return GDN_ERR_INVALID_ARG;  // chunked carry needs S_final
     return d->io_dtype == GDN_BF16 ? dispatch_d<uint16_t>(p, a, stream, cus)
                                    : dispatch_d<float>(p, a, stream, cus);

@@ -37,6 +37,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------- scalar helpers
 __device__ __forceinline__ uint16_t f2bf(float x) {
@@ -45,6 +47,52 @@ __device__ __forceinline__ uint16_t f2bf(float x) {
 }
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 __device__ __forceinline__ float sigmoid_f(float x) { return 1.0f / (1.0f + __expf(-x)); }
+// Sum over aligned groups of L consecutive lanes (L = 1, 2, 4, 8, 16), result
+// in every lane of the group, using DPP lane swaps inside a 16-lane row.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int L>
+__device__ __forceinline__ float group_sum(float x) {
+    static_assert(L <= 16, "group larger than a DPP row");
+    if constexpr (L >= 2) x += dpp_f<0xB1>(x);    // quad_perm [1,0,3,2]
+    if constexpr (L >= 4) x += dpp_f<0x4E>(x);    // quad_perm [2,3,0,1]
+    if constexpr (L >= 8) x += dpp_f<0x141>(x);   // row_half_mirror
+    if constexpr (L >= 16) x += dpp_f<0x140>(x);  // row_mirror
+    return x;
+}
+// Two floats to two bf16 (round to nearest even) in one dword, x in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float x, float y) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x, y}, bf16x2));
+}
+// Frames per state_scan launch (alpha values are staged in LDS).
+constexpr int kMaxChunkFrames = 256;
+
+// ---------------------------------------------------------------- buffer resources
+// Token tensors are read and written through raw buffer resources whose range
+// ends at the last valid row: the hardware returns zeros for loads past it and
+// drops stores past it.  Ragged tails therefore need no branches, and every
+// prefetch is issued unconditionally, which keeps the compiler's wait counts
+// exact (a conditional load forces a full drain at the next use).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;  // raw 32-bit buffer, gfx9-family config word
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, kRsrcWord3);
+}
+__device__ __forceinline__ u32x4 bload16(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ __forceinline__ float bload4f(rsrc_t r, uint32_t off) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ __forceinline__ void bstore8(rsrc_t r, uint32_t off, u32x2 v) {
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
+}
+__device__ __forceinline__ void bstore16(rsrc_t r, uint32_t off, u32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+}
 
 // ---------------------------------------------------------------- I/O type traits
 // Storage type of q/k/v/o: uint16_t holds bfloat16 bits; float is the fp32 mode.
@@ -61,6 +109,7 @@ template <> struct IO<uint16_t> {
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x),
                                                       __builtin_bit_cast(bf16x8, y), acc, 0, 0, 0);
     }
+    __device__ static __forceinline__ frag bload(rsrc_t r, uint32_t off) { return bload16(r, off); }
     __device__ static __forceinline__ float get(const frag& x, int e) {
         const uint32_t w = x[e >> 1];
         return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
@@ -81,6 +130,12 @@ template <> struct IO<float> {
 #pragma unroll
         for (int s = 0; s < 8; ++s)
             acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[s], y[s], acc, 0, 0, 0);
+    }
+    __device__ static __forceinline__ frag bload(rsrc_t r, uint32_t off) {
+        const u32x4 lo = bload16(r, off), hi = bload16(r, off + 16);
+        return f32x8{__uint_as_float(lo[0]), __uint_as_float(lo[1]), __uint_as_float(lo[2]),
+                     __uint_as_float(lo[3]), __uint_as_float(hi[0]), __uint_as_float(hi[1]),
+                     __uint_as_float(hi[2]), __uint_as_float(hi[3])};
     }
     __device__ static __forceinline__ float get(const frag& x, int e) { return x[e]; }
     __device__ static __forceinline__ uint32_t bits(float x) { return __float_as_uint(x); }
@@ -114,6 +169,8 @@ struct ScanArgs {
     int f0, Fc;           // frames [f0, f0 + Fc) of this launch
     int tsplit;           // token ranges per frame in frame_output
     int tchunk;           // tokens per range (multiple of 16)
+    uint32_t tok_bytes;   // bytes from a head's first token row of a frame to the
+                          // end of its last row: (N-1)*H*D*esz + D*esz (0 if N == 0)
     int logits;
     float eps;
 };
@@ -132,18 +189,19 @@ __device__ __forceinline__ int xcd_remap(int id, int per, int total) {
 // ================================================================== frame_gram
 template <typename T, int D> struct GramCfg {
     static constexpr int SZ = IO<T>::bytes;
-    static constexpr int SL = D / 8;                                // 8-value slices per token
-    static constexpr int TS0 = SZ == 2 ? 128 : 64;
-    static constexpr int TS = (TS0 * SL >= 256) ? TS0 : 256 / SL;  // tokens per LDS stage
-    static constexpr int TPT = TS * SL / 256;                       // tokens per thread per stage
-    static constexpr int ROWB = TS * SZ;                            // bytes per LDS row
-    static constexpr int CHUNKS = ROWB / 16;                        // 16-byte chunks per row
-    static constexpr int ARR = D * ROWB;                            // bytes per transposed array
-    static constexpr int LDS = 3 * ARR;
-    static constexpr int RB = D / 16;                               // 16-row blocks per matrix
-    static constexpr int NRW = (2 * RB + 3) / 4;                    // row blocks per wave
-    static constexpr int KST = TS / 32;                             // 32-token steps per stage
-    static constexpr int TPC = 16 / SZ;                             // tokens per 16-byte chunk
+    static constexpr int SL = D / 8;                                 // 8-value slices per token
+    static constexpr int TS0 = SZ == 2 ? 64 : 32;
+    static constexpr int TS = TS0 > 2048 / D ? TS0 : 2048 / D;      // tokens per LDS stage
+    static constexpr int TPT = TS * SL / 256;                        // tokens per producer thread
+    static constexpr int ROWB = TS * SZ;                             // bytes per LDS row
+    static constexpr int CHUNKS = ROWB / 16;                         // 16-byte chunks per row
+    static constexpr int ARR = D * ROWB;                             // bytes per transposed array
+    static constexpr int BUF = 3 * ARR;                              // one stage: K, wK, uV
+    static constexpr int LDS = 2 * BUF;                              // double buffer
+    static constexpr int RB = D / 16;                                // 16-row blocks per matrix
+    static constexpr int NRW = (2 * RB + 3) / 4;                     // row blocks per MFMA wave
+    static constexpr int KST = TS / 32;                              // 32-token steps per stage
+    static constexpr int TPC = 16 / SZ;                              // tokens per 16-byte chunk
     static_assert(TPT >= 1 && TPT * SZ <= 16 && TPC % TPT == 0, "stage shape");
     static_assert(CHUNKS >= 8 && (CHUNKS & (CHUNKS - 1)) == 0, "swizzle needs >= 8 chunks");
 };
@@ -154,32 +212,6 @@ template <typename T, int D> struct GramCfg {
 template <int ROWB>
 __device__ __forceinline__ int lds_chunk(int row, int c) {
     return row * ROWB + ((c ^ ((row ^ (row >> 3)) & 7)) << 4);
-}
-
-// Pack TPT consecutive tokens of one feature (bits already in storage width)
-// into one LDS store of TPT*SZ bytes.
-template <int TPT, int SZ>
-__device__ __forceinline__ void lds_store_tokens(unsigned char* p, const uint32_t (&v)[TPT]) {
-    if constexpr (SZ == 2) {
-        if constexpr (TPT == 8) {
-            *reinterpret_cast<u32x4*>(p) = u32x4{v[0] | (v[1] << 16), v[2] | (v[3] << 16),
-                                                 v[4] | (v[5] << 16), v[6] | (v[7] << 16)};
-        } else if constexpr (TPT == 4) {
-            *reinterpret_cast<u32x2*>(p) = u32x2{v[0] | (v[1] << 16), v[2] | (v[3] << 16)};
-        } else if constexpr (TPT == 2) {
-            *reinterpret_cast<uint32_t*>(p) = v[0] | (v[1] << 16);
-        } else {
-            *reinterpret_cast<uint16_t*>(p) = (uint16_t)v[0];
-        }
-    } else {
-        if constexpr (TPT == 4) {
-            *reinterpret_cast<u32x4*>(p) = u32x4{v[0], v[1], v[2], v[3]};
-        } else if constexpr (TPT == 2) {
-            *reinterpret_cast<u32x2*>(p) = u32x2{v[0], v[1]};
-        } else {
-            *reinterpret_cast<uint32_t*>(p) = v[0];
-        }
-    }
 }
 
 // Fragment (8 contraction values) of LDS row `row`, tokens 8g..8g+7 of 32-token step ks.
@@ -196,124 +228,200 @@ __device__ __forceinline__ typename IO<T>::frag lds_frag(const unsigned char* ba
     }
 }
 
+// 16-bit storage bits of element e of a fragment (bf16) / 32-bit (fp32).
+template <typename T>
+__device__ __forceinline__ uint32_t elem_bits(const typename IO<T>::frag& x, int e) {
+    if constexpr (sizeof(T) == 2) {
+        return (e & 1) ? (x[e >> 1] >> 16) : (x[e >> 1] & 0xffffu);
+    } else {
+        return __float_as_uint(x[e]);
+    }
+}
+
+// Persistent workgroups of 8 waves; workgroup w takes the (b, h, f) items
+// w, w + grid, w + 2*grid, ... in frame-major order (head fastest), so the
+// heads of one frame together read each contiguous token row of [B,F,N,H,D].
+// Waves 4-7 produce: they stream K_f, V_f and beta through registers (four
+// stages of 64 tokens in flight, continuing across items), reduce the key
+// norms across the lanes of each token, scale, and write the stage transposed
+// ([feature][token]) into one half of a double-buffered LDS.  Waves 0-3
+// consume the other half with MFMA:
+//     G += (rho K)^T (beta rho K),    U += V^T (beta rho K)
+// so both products share the scaled B operand and V is only transposed; after
+// an item's last stage they write Gm = -alpha G and U to the workspace.
 template <typename T, int D>
-__global__ __launch_bounds__(256, 1) void frame_gram_kernel(ScanArgs a) {
+__global__ __launch_bounds__(512, 1) void frame_gram_kernel(ScanArgs a) {
     using C = GramCfg<T, D>;
     using io = IO<T>;
     using frag = typename io::frag;
     __shared__ __attribute__((aligned(16))) unsigned char smem[C::LDS];
-    unsigned char* const sKT = smem;                // raw keys          [feature][token]
-    unsigned char* const sWK = smem + C::ARR;       // beta*rho^2 * k    [feature][token]
-    unsigned char* const sUV = smem + 2 * C::ARR;   // beta*rho   * v    [feature][token]
 
-    const int item = blockIdx.x;                    // (b*H + h)*Fc + fl
-    const int fl = item % a.Fc;
-    const int bh = item / a.Fc;
-    const int h = bh % a.H;
-    const int b = bh / a.H;
-    const int f = a.f0 + fl;
     const int N = a.N, H = a.H;
+    const int items = a.B * a.H * a.Fc;
+    const int nmine = (int)blockIdx.x < items ? (items - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
+    const int nst = (N + C::TS - 1) / C::TS;
+    const int total = nmine * nst;                  // stages of this workgroup
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = lane & 15, g = lane >> 4;
+    const bool producer = wave >= 4;
 
-    const size_t rowstride = (size_t)H * D;                     // elements between tokens
-    const size_t tok0 = ((size_t)b * a.F + f) * (size_t)N;      // first token of the frame
-    const T* kb = static_cast<const T*>(a.k) + tok0 * rowstride + (size_t)h * D;
-    const T* vb = static_cast<const T*>(a.v) + tok0 * rowstride + (size_t)h * D;
-    const float* bb = a.beta + tok0 * H + h;
-
-    // loader role: 8-feature slice s of tokens tl*TPT + j
-    const int s = tid % C::SL;
-    const int tl = tid / C::SL;
-
-    frag kr[C::TPT], vr[C::TPT];
-    float br[C::TPT];
-    auto load_stage = [&](int st) {
-#pragma unroll
-        for (int j = 0; j < C::TPT; ++j) {
-            const int n = st * C::TS + tl * C::TPT + j;
-            if (n < N) {
-                kr[j] = io::load(kb + (size_t)n * rowstride + s * 8);
-                vr[j] = io::load(vb + (size_t)n * rowstride + s * 8);
-                br[j] = bb[(size_t)n * H];
-            } else {
-                kr[j] = io::zero();
-                vr[j] = io::zero();
-                br[j] = 0.0f;
-            }
-        }
+    struct Item {
+        int b, h, f, ws;                            // batch, head, frame, workspace item
+    };
+    auto item_of = [&](int k) {
+        const int x = (int)blockIdx.x + k * (int)gridDim.x;
+        Item it;
+        it.h = x % H;
+        const int fl = (x / H) % a.Fc;
+        it.b = x / (H * a.Fc);
+        it.f = a.f0 + fl;
+        it.ws = (it.b * H + it.h) * a.Fc + fl;
+        return it;
     };
 
-    f32x4 acc[C::NRW][C::RB];
-#pragma unroll
-    for (int i = 0; i < C::NRW; ++i)
-#pragma unroll
-        for (int j = 0; j < C::RB; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
-
-    const int nst = (N + C::TS - 1) / C::TS;
+    // ---- producer state (32-bit offsets: the host bounds a frame below 2 GiB)
+    const int ptid = tid & 255;
+    const int s = ptid % C::SL;                     // 8-feature slice
+    const int tl = ptid / C::SL;                    // token group: tokens tl*TPT + j
+    const size_t rowstride = (size_t)H * D;         // elements between tokens
+    const uint32_t row_bytes = (uint32_t)(H * D * C::SZ);
+    const uint32_t kv_off0 = (uint32_t)(tl * C::TPT) * row_bytes + (uint32_t)(s * 8 * C::SZ);
+    const uint32_t b_off0 = (uint32_t)(tl * C::TPT * H * 4);
+    const uint32_t beta_bytes = N > 0 ? (uint32_t)(((N - 1) * H + 1) * 4) : 0u;
     const float inv_n = N > 0 ? 1.0f / (float)N : 0.0f;
-    if (nst > 0) load_stage(0);
+    const float inv_eps = 1.0f / a.eps;
 
-    for (int st = 0; st < nst; ++st) {
-        // ---- key norms (wavefront reduction over the SL lanes of a token) and
-        //      per-token scales; the previous stage's fragment reads finished
-        //      at the barrier that closed the last iteration
-        float wsc[C::TPT], usc[C::TPT];
+    struct Stage {
+        frag k[C::TPT], v[C::TPT];
+        float bt[C::TPT];
+    };
+    // Stage gs of this workgroup's stream; stages past the end read rows past
+    // the last token, which the buffer range check returns as zeros.
+    auto load_stage = [&](int gs, Stage& R) {
+        int kk = gs / (nst > 0 ? nst : 1), st = gs - kk * nst;
+        if (kk >= nmine) {
+            kk = nmine - 1;
+            st = nst;
+        }
+        const Item it = item_of(kk);
+        const size_t tok0 = ((size_t)it.b * a.F + it.f) * (size_t)N;
+        const rsrc_t rk = make_rsrc(static_cast<const T*>(a.k) + tok0 * rowstride + (size_t)it.h * D,
+                                    a.tok_bytes);
+        const rsrc_t rv = make_rsrc(static_cast<const T*>(a.v) + tok0 * rowstride + (size_t)it.h * D,
+                                    a.tok_bytes);
+        const rsrc_t rb = make_rsrc(a.beta + tok0 * H + it.h, beta_bytes);
+        const uint32_t kvo = kv_off0 + (uint32_t)(st * C::TS) * row_bytes;
+        const uint32_t bo = b_off0 + (uint32_t)(st * C::TS * H * 4);
+#pragma unroll
+        for (int j = 0; j < C::TPT; ++j) {
+            R.k[j] = io::bload(rk, kvo + (uint32_t)j * row_bytes);
+            R.v[j] = io::bload(rv, kvo + (uint32_t)j * row_bytes);
+            R.bt[j] = bload4f(rb, bo + (uint32_t)(j * H * 4));
+        }
+    };
+    // Norms, scales and the transposed LDS write of stage gs.
+    auto write_stage = [&](int gs, const Stage& R, unsigned char* buf) {
+        const int st = gs % nst;
+        float rho[C::TPT], xs[C::TPT];
 #pragma unroll
         for (int j = 0; j < C::TPT; ++j) {
             float ss = 0.0f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float x = io::get(kr[j], e);
-                ss = fmaf(x, x, ss);
+                const float kx = io::get(R.k[j], e);
+                ss = fmaf(kx, kx, ss);
             }
-#pragma unroll
-            for (int m = 1; m < C::SL; m <<= 1) ss += __shfl_xor(ss, m, 64);
-            float bt = br[j];
+            ss = group_sum<C::SL>(ss);
+            float bt = R.bt[j];
             if (a.logits) bt = (st * C::TS + tl * C::TPT + j < N) ? sigmoid_f(bt) * inv_n : 0.0f;
-            const float rho = 1.0f / fmaxf(sqrtf(ss), a.eps);
-            wsc[j] = bt * rho * rho;   // G = sum_i w_i k_i k_i^T
-            usc[j] = bt * rho;         // U = sum_i u_i v_i k_i^T
+            rho[j] = fminf(__builtin_amdgcn_rsqf(ss), inv_eps);   // 1 / max(|k|, eps)
+            xs[j] = bt * rho[j];
         }
-        // ---- transposed write: one LDS store per (feature, array) packs this
-        //      thread's TPT consecutive tokens
-        {
-            const int t0 = tl * C::TPT;
-            const int cbase = t0 / C::TPC, within = (t0 % C::TPC) * C::SZ;
+        unsigned char* sKH = buf;                   // rho k         (A of G)
+        unsigned char* sVT = buf + C::ARR;          // v             (A of U)
+        unsigned char* sXB = buf + 2 * C::ARR;      // beta rho k    (B of both)
+        const int t0 = tl * C::TPT;
+        const int cbase = t0 / C::TPC, within = (t0 % C::TPC) * C::SZ;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int off = lds_chunk<C::ROWB>(s * 8 + e, cbase) + within;
-                uint32_t raw[C::TPT], wk[C::TPT], uv[C::TPT];
+        for (int e = 0; e < 8; ++e) {
+            const int off = lds_chunk<C::ROWB>(s * 8 + e, cbase) + within;
+            if constexpr (sizeof(T) == 2) {
+                if constexpr (C::TPT == 1) {
+                    const float kx = io::get(R.k[0], e);
+                    *reinterpret_cast<uint16_t*>(sKH + off) = f2bf(rho[0] * kx);
+                    *reinterpret_cast<uint16_t*>(sXB + off) = f2bf(xs[0] * kx);
+                    *reinterpret_cast<uint16_t*>(sVT + off) = (uint16_t)elem_bits<T>(R.v[0], e);
+                } else {
+                    uint32_t kh[C::TPT / 2], xb[C::TPT / 2], vt[C::TPT / 2];
+#pragma unroll
+                    for (int j = 0; j < C::TPT; j += 2) {
+                        const float k0 = io::get(R.k[j], e), k1 = io::get(R.k[j + 1], e);
+                        kh[j / 2] = pack_bf16x2(rho[j] * k0, rho[j + 1] * k1);
+                        xb[j / 2] = pack_bf16x2(xs[j] * k0, xs[j + 1] * k1);
+                        vt[j / 2] = elem_bits<T>(R.v[j], e) | (elem_bits<T>(R.v[j + 1], e) << 16);
+                    }
+                    if constexpr (C::TPT == 8) {
+                        *reinterpret_cast<u32x4*>(sKH + off) = u32x4{kh[0], kh[1], kh[2], kh[3]};
+                        *reinterpret_cast<u32x4*>(sXB + off) = u32x4{xb[0], xb[1], xb[2], xb[3]};
+                        *reinterpret_cast<u32x4*>(sVT + off) = u32x4{vt[0], vt[1], vt[2], vt[3]};
+                    } else if constexpr (C::TPT == 4) {
+                        *reinterpret_cast<u32x2*>(sKH + off) = u32x2{kh[0], kh[1]};
+                        *reinterpret_cast<u32x2*>(sXB + off) = u32x2{xb[0], xb[1]};
+                        *reinterpret_cast<u32x2*>(sVT + off) = u32x2{vt[0], vt[1]};
+                    } else {
+                        *reinterpret_cast<uint32_t*>(sKH + off) = kh[0];
+                        *reinterpret_cast<uint32_t*>(sXB + off) = xb[0];
+                        *reinterpret_cast<uint32_t*>(sVT + off) = vt[0];
+                    }
+                }
+            } else {
+                float kh[C::TPT], xb[C::TPT], vt[C::TPT];
 #pragma unroll
                 for (int j = 0; j < C::TPT; ++j) {
-                    const float x = io::get(kr[j], e);
-                    if constexpr (sizeof(T) == 2) {
-                        raw[j] = __float_as_uint(x) >> 16;
-                    } else {
-                        raw[j] = __float_as_uint(x);
-                    }
-                    wk[j] = io::bits(wsc[j] * x);
-                    uv[j] = io::bits(usc[j] * io::get(vr[j], e));
+                    const float kx = R.k[j][e];
+                    kh[j] = rho[j] * kx;
+                    xb[j] = xs[j] * kx;
+                    vt[j] = R.v[j][e];
                 }
-                lds_store_tokens<C::TPT, C::SZ>(sKT + off, raw);
-                lds_store_tokens<C::TPT, C::SZ>(sWK + off, wk);
-                lds_store_tokens<C::TPT, C::SZ>(sUV + off, uv);
+                if constexpr (C::TPT == 4) {
+                    *reinterpret_cast<f32x4*>(sKH + off) = f32x4{kh[0], kh[1], kh[2], kh[3]};
+                    *reinterpret_cast<f32x4*>(sXB + off) = f32x4{xb[0], xb[1], xb[2], xb[3]};
+                    *reinterpret_cast<f32x4*>(sVT + off) = f32x4{vt[0], vt[1], vt[2], vt[3]};
+                } else if constexpr (C::TPT == 2) {
+                    *reinterpret_cast<f32x2*>(sKH + off) = f32x2{kh[0], kh[1]};
+                    *reinterpret_cast<f32x2*>(sXB + off) = f32x2{xb[0], xb[1]};
+                    *reinterpret_cast<f32x2*>(sVT + off) = f32x2{vt[0], vt[1]};
+                } else {
+                    *reinterpret_cast<float*>(sKH + off) = kh[0];
+                    *reinterpret_cast<float*>(sXB + off) = xb[0];
+                    *reinterpret_cast<float*>(sVT + off) = vt[0];
+                }
             }
         }
-        __syncthreads();
-        if (st + 1 < nst) load_stage(st + 1);     // in flight during the MFMAs
+    };
 
-        // ---- G += (wK)^T K,  U += (uV)^T K  over the stage's tokens
+    // ---- consumer state
+    f32x4 acc[C::NRW][C::RB];
+    auto zero_acc = [&]() {
 #pragma unroll
+        for (int i = 0; i < C::NRW; ++i)
+#pragma unroll
+            for (int j = 0; j < C::RB; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
+    };
+    auto mfma_stage = [&](const unsigned char* buf) {
+        const unsigned char* sKH = buf;
+        const unsigned char* sVT = buf + C::ARR;
+        const unsigned char* sXB = buf + 2 * C::ARR;
+#pragma unroll 1
         for (int ks = 0; ks < C::KST; ++ks) {
             frag bk[C::RB];
 #pragma unroll
-            for (int j = 0; j < C::RB; ++j) bk[j] = lds_frag<T, C::ROWB>(sKT, j * 16 + r, ks, g);
+            for (int j = 0; j < C::RB; ++j) bk[j] = lds_frag<T, C::ROWB>(sXB, j * 16 + r, ks, g);
 #pragma unroll
             for (int i = 0; i < C::NRW; ++i) {
-                const int gb = wave + 4 * i;      // row block over [G rows ; U rows]
+                const int gb = wave + 4 * i;        // row block over [G rows ; U rows]
                 if (gb < 2 * C::RB) {
-                    const unsigned char* src = gb < C::RB ? sWK : sUV;
+                    const unsigned char* src = gb < C::RB ? sKH : sVT;
                     const int rowb = gb < C::RB ? gb : gb - C::RB;
                     const frag ak = lds_frag<T, C::ROWB>(src, rowb * 16 + r, ks, g);
 #pragma unroll
@@ -321,72 +429,133 @@ __global__ __launch_bounds__(256, 1) void frame_gram_kernel(ScanArgs a) {
                 }
             }
         }
-        __syncthreads();
-    }
-
-    // ---- epilogue: Gm^T = -alpha G^T (hi/lo planes or fp32) and U^T (fp32)
-    float al = a.alpha[((size_t)b * a.F + f) * H + h];
-    if (a.logits) al = sigmoid_f(al);
-    unsigned char* wsi = a.ws + (size_t)item * WS<D>::item_bytes;
+    };
+    // Gm^T = -alpha G^T (hi/lo planes or fp32) and U^T (fp32) of item k
+    auto epilogue = [&](int k) {
+        const Item it = item_of(k);
+        float al = a.alpha[((size_t)it.b * a.F + it.f) * H + it.h];
+        if (a.logits) al = sigmoid_f(al);
+        unsigned char* wsi = a.ws + (size_t)it.ws * WS<D>::item_bytes;
 #pragma unroll
-    for (int i = 0; i < C::NRW; ++i) {
-        const int gb = wave + 4 * i;
-        if (gb >= 2 * C::RB) continue;
+        for (int i = 0; i < C::NRW; ++i) {
+            const int gb = wave + 4 * i;
+            if (gb >= 2 * C::RB) continue;
 #pragma unroll
-        for (int j = 0; j < C::RB; ++j) {
-            const f32x4 x = acc[i][j];
-            const int col = j * 16 + r;                    // e
-            if (gb < C::RB) {
-                const int row0 = gb * 16 + 4 * g;           // c
-                const size_t idx = (size_t)col * D + row0;  // Gm^T[e][c..c+3]
-                const f32x4 m = x * (-al);
-                if constexpr (sizeof(T) == 2) {
-                    uint16_t* hi = reinterpret_cast<uint16_t*>(wsi + WS<D>::gm_off);
-                    uint16_t* lo = hi + (size_t)D * D;
-                    uint32_t hb[4], lb[4];
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        hb[t] = f2bf(m[t]);
-                        lb[t] = f2bf(m[t] - bf2f((uint16_t)hb[t]));
+            for (int j = 0; j < C::RB; ++j) {
+                const f32x4 x = acc[i][j];
+                const int col = j * 16 + r;                    // e
+                if (gb < C::RB) {
+                    const int row0 = gb * 16 + 4 * g;           // c
+                    const size_t idx = (size_t)col * D + row0;  // Gm^T[e][c..c+3]
+                    const f32x4 m = x * (-al);
+                    if constexpr (sizeof(T) == 2) {
+                        uint16_t* hi = reinterpret_cast<uint16_t*>(wsi + WS<D>::gm_off);
+                        uint16_t* lo = hi + (size_t)D * D;
+                        const uint32_t h01 = pack_bf16x2(m[0], m[1]), h23 = pack_bf16x2(m[2], m[3]);
+                        const uint32_t l01 = pack_bf16x2(m[0] - bf2f(h01 & 0xffffu), m[1] - bf2f(h01 >> 16));
+                        const uint32_t l23 = pack_bf16x2(m[2] - bf2f(h23 & 0xffffu), m[3] - bf2f(h23 >> 16));
+                        *reinterpret_cast<u32x2*>(hi + idx) = u32x2{h01, h23};
+                        *reinterpret_cast<u32x2*>(lo + idx) = u32x2{l01, l23};
+                    } else {
+                        float* gm = reinterpret_cast<float*>(wsi + WS<D>::gm_off);
+                        *reinterpret_cast<f32x4*>(gm + idx) = m;
                     }
-                    *reinterpret_cast<u32x2*>(hi + idx) = u32x2{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)};
-                    *reinterpret_cast<u32x2*>(lo + idx) = u32x2{lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16)};
                 } else {
-                    float* gm = reinterpret_cast<float*>(wsi + WS<D>::gm_off);
-                    *reinterpret_cast<f32x4*>(gm + idx) = m;
+                    const int row0 = (gb - C::RB) * 16 + 4 * g;  // a
+                    float* ut = reinterpret_cast<float*>(wsi + WS<D>::ut_off);
+                    *reinterpret_cast<f32x4*>(ut + (size_t)col * D + row0) = x;
                 }
-            } else {
-                const int row0 = (gb - C::RB) * 16 + 4 * g;  // a
-                float* ut = reinterpret_cast<float*>(wsi + WS<D>::ut_off);
-                *reinterpret_cast<f32x4*>(ut + (size_t)col * D + row0) = x;
             }
         }
+    };
+
+    if (nst == 0) {                                  // no tokens: G = U = 0
+        if (!producer) {
+            zero_acc();
+            for (int k = 0; k < nmine; ++k) epilogue(k);
+        }
+        return;
+    }
+
+    // ---- pipeline: period p produces stage p into LDS buffer p&1 while the
+    //      consumers multiply stage p-1 from buffer (p-1)&1.  The producers keep
+    //      four register stages in flight (ring slot p&3).  The two roles run
+    //      separate loops with the same number of barriers, so their registers
+    //      (load stages vs accumulators) are never live together, and every
+    //      load is unconditional so wait counts stay exact.
+    unsigned char* const buf0 = smem;
+    unsigned char* const buf1 = smem + C::BUF;
+    const int nquad = (total + 1 + 3) / 4;          // periods 0..total, in groups of 4
+    if (producer) {
+        Stage R0, R1, R2, R3;
+        load_stage(0, R0);
+        load_stage(1, R1);
+        load_stage(2, R2);
+        load_stage(3, R3);
+        for (int q = 0; q < nquad; ++q) {
+            const int p = 4 * q;
+            if (p < total) write_stage(p, R0, buf0);
+            load_stage(p + 4, R0);
+            __syncthreads();
+            if (p + 1 < total) write_stage(p + 1, R1, buf1);
+            load_stage(p + 5, R1);
+            __syncthreads();
+            if (p + 2 < total) write_stage(p + 2, R2, buf0);
+            load_stage(p + 6, R2);
+            __syncthreads();
+            if (p + 3 < total) write_stage(p + 3, R3, buf1);
+            load_stage(p + 7, R3);
+            __syncthreads();
+        }
+        return;
+    }
+    zero_acc();
+    for (int p = 0; p < 4 * nquad; ++p) {
+        if (p >= 1 && p <= total) {
+            mfma_stage((p & 1) ? buf0 : buf1);      // stage p-1 sits in buffer (p-1)&1
+            if ((p - 1) % nst == nst - 1) {
+                epilogue((p - 1) / nst);
+                zero_acc();
+            }
+        }
+        __syncthreads();
     }
 }
 
 // ================================================================== state_scan
 template <typename T, int D> struct StateCfg {
-    static constexpr int CT = D >= 32 ? 2 : 1;       // 16-column tiles per wave
-    static constexpr int NW = D / (16 * CT);         // waves per workgroup
-    static constexpr int KS = (D + 31) / 32;         // 32-wide contraction steps
-    static constexpr int RT = D / 16;                // row tiles per (b, h)
-    static constexpr int PADB = 16;                  // LDS row padding (bytes)
+    static constexpr int CT = D >= 32 ? 2 : 1;          // 16-column tiles per wave
+    static constexpr int NW = D / (16 * CT);            // waves per workgroup
+    static constexpr int KS = (D + 31) / 32;            // 32-wide contraction steps
+    static constexpr int RT = D / 16;                   // row tiles per (b, h)
+    static constexpr int PADB = 16;                     // LDS row padding (bytes)
     static constexpr int ROWB = D * IO<T>::bytes + PADB;
     static constexpr int NPL = sizeof(T) == 2 ? 2 : 1;  // planes (hi, lo) of S in LDS
+    // frames of operands in flight: the ring must fit the 6-bit vector-memory
+    // counter (63 outstanding loads and stores per wave) or every frame drains it
+    static constexpr int LOADS = CT * KS * (IO<T>::bytes == 2 ? 2 : 2) + CT;
+    static constexpr int PD = (56 / LOADS) < 4 ? (56 / LOADS) : 4;
+    static_assert(PD >= 2, "ring too shallow");
 };
 
 // One workgroup owns rows [16*rt, 16*rt+16) of one (b, h) state; wave w owns
 // columns [32w, 32w+32) (16 wide for D = 16).  Per frame:
 //   acc = alpha*S + U_f ;  acc += S_hi Gm_hi + S_lo Gm_hi + S_hi Gm_lo  (bf16)
 //   (fp32 mode: acc += S Gm with fp32 MFMA)
-// S is kept in fp32 registers; its bf16 hi/lo split lives in LDS as the A
-// operand and is copied to the workspace for frame_output.
+// S stays in fp32 registers; its bf16 hi/lo split is double-buffered in LDS
+// as the A operand (one barrier per frame), and the previous frame's planes
+// are copied to the workspace for frame_output while this frame's MFMAs run.
+// Each output tile keeps two accumulators (even / odd contraction steps) to
+// halve the dependent MFMA chain.  The operands of the next PD frames are in
+// flight in a register ring.
 template <typename T, int D>
-__global__ __launch_bounds__(D >= 32 ? 2 * D : 64) void state_scan_kernel(ScanArgs a) {  // NW*64
+__global__ __launch_bounds__(D >= 32 ? 2 * D : 64, 1) void state_scan_kernel(ScanArgs a) {  // NW*64
     using C = StateCfg<T, D>;
     using io = IO<T>;
     using frag = typename io::frag;
-    __shared__ __attribute__((aligned(16))) unsigned char sS[C::NPL][16 * C::ROWB];
+    constexpr int PLANE = 16 * C::ROWB;
+    __shared__ __attribute__((aligned(16))) unsigned char sS[2][C::NPL][PLANE];
+    __shared__ float sAlpha[kMaxChunkFrames];
 
     const int units = a.B * a.H;
     const int id = xcd_remap(blockIdx.x, C::RT, units * C::RT);
@@ -395,8 +564,14 @@ __global__ __launch_bounds__(D >= 32 ? 2 * D : 64) void state_scan_kernel(ScanAr
     const int bh = id / C::RT;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = lane & 15, g = lane >> 4;
-    const int a0 = rt * 16;                          // first state row of this tile
+    const int a0 = rt * 16;                             // first state row of this tile
     const int h = bh % a.H, b = bh / a.H;
+    const int Fc = a.Fc;
+
+    for (int i = tid; i < Fc; i += C::NW * 64) {
+        const float x = a.alpha[((size_t)b * a.F + a.f0 + i) * a.H + h];
+        sAlpha[i] = a.logits ? sigmoid_f(x) : x;
+    }
 
     // ---- initial state: registers (accumulator layout) and LDS (operand layout)
     f32x4 S[C::CT];
@@ -407,7 +582,7 @@ __global__ __launch_bounds__(D >= 32 ? 2 * D : 64) void state_scan_kernel(ScanAr
 #pragma unroll
         for (int t = 0; t < 4; ++t) S[ct][t] = sin ? sin[(size_t)(a0 + 4 * g + t) * D + col] : 0.0f;
     }
-    auto put_lds = [&]() {
+    auto put_lds = [&](int buf) {
 #pragma unroll
         for (int ct = 0; ct < C::CT; ++ct) {
             const int col = (wave * C::CT + ct) * 16 + r;
@@ -416,98 +591,127 @@ __global__ __launch_bounds__(D >= 32 ? 2 * D : 64) void state_scan_kernel(ScanAr
                 const int off = (4 * g + t) * C::ROWB + col * io::bytes;
                 if constexpr (sizeof(T) == 2) {
                     const uint16_t hi = f2bf(S[ct][t]);
-                    *reinterpret_cast<uint16_t*>(&sS[0][off]) = hi;
-                    *reinterpret_cast<uint16_t*>(&sS[1][off]) = f2bf(S[ct][t] - bf2f(hi));
+                    *reinterpret_cast<uint16_t*>(&sS[buf][0][off]) = hi;
+                    *reinterpret_cast<uint16_t*>(&sS[buf][1][off]) = f2bf(S[ct][t] - bf2f(hi));
                 } else {
-                    *reinterpret_cast<float*>(&sS[0][off]) = S[ct][t];
+                    *reinterpret_cast<float*>(&sS[buf][0][off]) = S[ct][t];
                 }
             }
         }
     };
-    put_lds();
-    __syncthreads();
+    put_lds(0);
 
-    // ---- per-frame operands, prefetched one frame ahead
     struct Ops {
         frag bh_[C::CT][C::KS];   // Gm hi (fp32 mode: Gm)
-        frag bl_[C::CT][C::KS];   // Gm lo (unused in fp32 mode)
+        frag bl_[C::CT][C::KS];   // Gm lo (bf16 mode only)
         f32x4 u[C::CT];           // U rows of this tile, accumulator layout
     };
-    const size_t item0 = (size_t)bh * a.Fc;
+    const size_t item0 = (size_t)bh * Fc;
+    // Loads of frame fl (always a valid frame: callers clamp).  For D = 16 the
+    // upper half of the contraction lanes reads in-bounds data zeroed at use.
     auto load_ops = [&](int fl, Ops& o) {
         const unsigned char* wsi = a.ws + (item0 + fl) * WS<D>::item_bytes;
+        const T* gm = reinterpret_cast<const T*>(wsi + WS<D>::gm_off);
+        const float* ut = reinterpret_cast<const float*>(wsi + WS<D>::ut_off);
 #pragma unroll
         for (int ct = 0; ct < C::CT; ++ct) {
             const int col = (wave * C::CT + ct) * 16 + r;   // e
 #pragma unroll
             for (int ks = 0; ks < C::KS; ++ks) {
-                const int c0 = ks * 32 + 8 * g;
-                if (c0 < D) {
-                    const T* gm = reinterpret_cast<const T*>(wsi + WS<D>::gm_off);
-                    o.bh_[ct][ks] = io::load(gm + (size_t)col * D + c0);
-                    if constexpr (sizeof(T) == 2)
-                        o.bl_[ct][ks] = io::load(gm + (size_t)D * D + (size_t)col * D + c0);
-                } else {
-                    o.bh_[ct][ks] = io::zero();
-                    o.bl_[ct][ks] = io::zero();
-                }
+                const int c0 = (ks * 32 + 8 * g) % D;
+                o.bh_[ct][ks] = io::load(gm + (size_t)col * D + c0);
+                if constexpr (sizeof(T) == 2)
+                    o.bl_[ct][ks] = io::load(gm + (size_t)D * D + (size_t)col * D + c0);
             }
-            const float* ut = reinterpret_cast<const float*>(wsi + WS<D>::ut_off);
             o.u[ct] = *reinterpret_cast<const f32x4*>(ut + (size_t)col * D + a0 + 4 * g);
         }
     };
+    const bool kvalid = 8 * g < D || D >= 32;          // D = 16: lanes g >= 2 carry zeros
 
-    Ops cur, nxt;
-    if (a.Fc > 0) load_ops(0, cur);
-    for (int fl = 0; fl < a.Fc; ++fl) {
-        if (fl + 1 < a.Fc) load_ops(fl + 1, nxt);
-        const int f = a.f0 + fl;
-        float al = a.alpha[((size_t)b * a.F + f) * a.H + h];
-        if (a.logits) al = sigmoid_f(al);
-
-        f32x4 acc[C::CT];
+    // Workspace S planes of this unit's frames through a buffer resource: the
+    // copy issued for frame -1 (before the first frame) falls outside it and
+    // is dropped, so the copy needs no branch.
+    const rsrc_t rsp = make_rsrc(a.ws + item0 * WS<D>::item_bytes, (uint32_t)(Fc * WS<D>::item_bytes));
+    constexpr int rowbytes = D * io::bytes;
+    constexpr int chunks = 16 * rowbytes / 16;          // per plane
+    auto copy_planes = [&](int fl, int buf) {           // S_fl, held in sS[buf], to frame fl
+        // frame -1 maps to 2 GiB: past the resource (at most 256 frames of
+        // 192 KiB) with no 32-bit overflow once the plane offset is added
+        const uint32_t base = fl >= 0 ? (uint32_t)fl * (uint32_t)WS<D>::item_bytes + (uint32_t)WS<D>::sp_off
+                                      : 0x80000000u;
 #pragma unroll
-        for (int ct = 0; ct < C::CT; ++ct) acc[ct] = S[ct] * al + cur.u[ct];
+        for (int x0 = 0; x0 < C::NPL * chunks; x0 += C::NW * 64) {
+            const int x = x0 + tid;
+            if (C::NPL * chunks % (C::NW * 64) == 0 || x < C::NPL * chunks) {
+                const int pl = x / chunks, cc = x % chunks;
+                const int row = cc / (rowbytes / 16), col16 = cc % (rowbytes / 16);
+                const u32x4 val = *reinterpret_cast<const u32x4*>(&sS[buf][pl][row * C::ROWB + col16 * 16]);
+                bstore16(rsp, base + (uint32_t)(pl * D * D * io::bytes + (a0 + row) * rowbytes + col16 * 16),
+                         val);
+            }
+        }
+    };
+
+    auto step = [&](int fl, const Ops& o) {
+        const int cur = fl & 1;                         // buffer holding S_{fl-1}
+        const float al = sAlpha[fl];
+        f32x4 acc[C::CT], acc2[C::CT];
+#pragma unroll
+        for (int ct = 0; ct < C::CT; ++ct) {
+            acc[ct] = S[ct] * al + o.u[ct];
+            acc2[ct] = f32x4{0, 0, 0, 0};
+        }
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
-            const int c0 = ks * 32 + 8 * g;
-            frag ahi = io::zero(), alo = io::zero();
-            if (c0 < D) {
-                if constexpr (sizeof(T) == 2) {
-                    ahi = *reinterpret_cast<const u32x4*>(&sS[0][r * C::ROWB + c0 * 2]);
-                    alo = *reinterpret_cast<const u32x4*>(&sS[1][r * C::ROWB + c0 * 2]);
-                } else {
-                    ahi = io::load(reinterpret_cast<const float*>(&sS[0][r * C::ROWB + c0 * 4]));
-                }
+            const int c0 = (ks * 32 + 8 * g) % D;
+            frag ahi, alo;
+            if constexpr (sizeof(T) == 2) {
+                ahi = *reinterpret_cast<const u32x4*>(&sS[cur][0][r * C::ROWB + c0 * 2]);
+                alo = *reinterpret_cast<const u32x4*>(&sS[cur][1][r * C::ROWB + c0 * 2]);
+            } else {
+                ahi = io::load(reinterpret_cast<const float*>(&sS[cur][0][r * C::ROWB + c0 * 4]));
+                alo = io::zero();
+            }
+            if (!kvalid) {
+                ahi = io::zero();
+                alo = io::zero();
             }
 #pragma unroll
             for (int ct = 0; ct < C::CT; ++ct) {
-                io::mma(acc[ct], ahi, cur.bh_[ct][ks]);
+                f32x4& dst = (ks & 1) ? acc2[ct] : acc[ct];
+                io::mma(dst, ahi, o.bh_[ct][ks]);
                 if constexpr (sizeof(T) == 2) {
-                    io::mma(acc[ct], alo, cur.bh_[ct][ks]);
-                    io::mma(acc[ct], ahi, cur.bl_[ct][ks]);
+                    io::mma(dst, alo, o.bh_[ct][ks]);
+                    io::mma(dst, ahi, o.bl_[ct][ks]);
                 }
             }
         }
-        __syncthreads();                 // every wave has read S_{f-1} from LDS
+        copy_planes(fl - 1, cur);                       // S_{fl-1}: overlaps the MFMAs
 #pragma unroll
-        for (int ct = 0; ct < C::CT; ++ct) S[ct] = acc[ct];
-        put_lds();
-        __syncthreads();                 // S_f visible in LDS
+        for (int ct = 0; ct < C::CT; ++ct) S[ct] = acc[ct] + acc2[ct];
+        put_lds(cur ^ 1);
+        __syncthreads();                                // S_fl visible; S_{fl-1} reads done
+    };
 
-        // S_f (operand planes) to the workspace for frame_output: 16 rows x D
-        unsigned char* sp = a.ws + (item0 + fl) * WS<D>::item_bytes + WS<D>::sp_off;
-        constexpr int rowbytes = D * io::bytes;
-        constexpr int chunks = 16 * rowbytes / 16;   // per plane
-        for (int x = tid; x < C::NPL * chunks; x += C::NW * 64) {
-            const int pl = x / chunks, cc = x % chunks;
-            const int row = cc / (rowbytes / 16), col16 = cc % (rowbytes / 16);
-            const u32x4 val = *reinterpret_cast<const u32x4*>(&sS[pl][row * C::ROWB + col16 * 16]);
-            *reinterpret_cast<u32x4*>(sp + (size_t)pl * D * D * io::bytes +
-                                      (size_t)(a0 + row) * rowbytes + col16 * 16) = val;
+    Ops ring[C::PD];
+#pragma unroll
+    for (int j = 0; j < C::PD; ++j) load_ops(j < Fc ? j : Fc - 1, ring[j]);
+    __syncthreads();                                    // alpha and S_in staged
+    const int nfull = Fc / C::PD;
+    for (int gi = 0; gi < nfull; ++gi) {
+#pragma unroll
+        for (int j = 0; j < C::PD; ++j) {
+            const int fl = gi * C::PD + j;
+            step(fl, ring[j]);
+            const int nx = fl + C::PD;
+            load_ops(nx < Fc ? nx : Fc - 1, ring[j]);
         }
-        cur = nxt;
     }
+    const int rem = Fc - nfull * C::PD;
+#pragma unroll
+    for (int j = 0; j < C::PD; ++j)
+        if (j < rem) step(nfull * C::PD + j, ring[j]);
+    copy_planes(Fc - 1, Fc & 1);                        // the last frame's S planes
 
     // ---- final state (fp32, row-major [a][e])
 #pragma unroll
@@ -524,27 +728,41 @@ __global__ __launch_bounds__(D >= 32 ? 2 * D : 64) void state_scan_kernel(ScanAr
 
 // ================================================================== frame_output
 template <typename T, int D> struct OutCfg {
+    static constexpr int SZ = IO<T>::bytes;
     static constexpr int RT = D / 16;               // 16-row tiles of S (output features)
     static constexpr int NWR = RT < 4 ? RT : 4;     // waves splitting the rows
     static constexpr int RPW = RT / NWR;            // row tiles per wave
     static constexpr int TG = 4 / NWR;              // waves splitting the tokens
     static constexpr int KS = (D + 31) / 32;
+    static constexpr int ROWB = D * SZ + 16;        // padded LDS row (one token)
+    static constexpr int LPR = D * SZ / 16;         // 16-byte loads per token row
+    static constexpr int RPP = 256 / LPR;           // token rows per load pass
+    static constexpr int BT = RPP > 64 ? RPP : 64;  // tokens per LDS block
+    static constexpr int NLD = BT / RPP;            // loads per thread per block
+    static constexpr int PD = SZ == 2 ? 4 : 2;      // blocks of Q in flight
+    static constexpr int LDS = 2 * BT * ROWB;
+    static_assert(BT % RPP == 0 && RPP >= 1, "block shape");
 };
 
 // o_i = S_f q_i computed as O^T = S Q^T: A = S (rows a, contraction e) held in
-// registers for the whole token loop, B = Q^T whose fragments are 8 contiguous
-// features of one token, loaded straight from global memory.
+// registers for the whole token range, B = Q^T.  Q is staged once per
+// workgroup: 64-token blocks stream from HBM PD blocks ahead into registers,
+// then into a double-buffered LDS tile from which every wave reads its B
+// fragments (a token row of Q is 8 contiguous features per lane).
 template <typename T, int D>
-__global__ __launch_bounds__(256) void frame_output_kernel(ScanArgs a) {
+__global__ __launch_bounds__(256, 2) void frame_output_kernel(ScanArgs a) {
     using C = OutCfg<T, D>;
     using io = IO<T>;
     using frag = typename io::frag;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[C::LDS];
 
-    const int item = blockIdx.x / a.tsplit;       // (b*H + h)*Fc + fl
-    const int part = blockIdx.x % a.tsplit;
-    const int fl = item % a.Fc;
-    const int bh = item / a.Fc;
-    const int h = bh % a.H, b = bh / a.H;
+    // frame-major order, head fastest: x = ((b*Fc + fl)*tsplit + part)*H + h
+    const int x = blockIdx.x;
+    const int h = x % a.H;
+    const int part = (x / a.H) % a.tsplit;
+    const int fl = (x / (a.H * a.tsplit)) % a.Fc;
+    const int b = x / (a.H * a.tsplit * a.Fc);
+    const int item = (b * a.H + h) * a.Fc + fl;   // workspace item
     const int f = a.f0 + fl;
     const int N = a.N, H = a.H;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -554,6 +772,34 @@ __global__ __launch_bounds__(256) void frame_output_kernel(ScanArgs a) {
     const int nbeg = part * a.tchunk;
     const int nend = min(N, nbeg + a.tchunk);
     if (nbeg >= nend) return;
+    const bool kvalid = 8 * g < D || D >= 32;      // D = 16: lanes g >= 2 carry zeros
+
+    // token range [nbeg, nend) of this head through buffer resources: rows past
+    // nend read as zeros and their stores are dropped
+    const size_t rowstride = (size_t)H * D;
+    const size_t tok0 = ((size_t)b * a.F + f) * (size_t)N + nbeg;
+    const uint32_t rbytes = (uint32_t)(((size_t)(nend - nbeg - 1) * rowstride + D) * C::SZ);
+    const rsrc_t rq = make_rsrc(static_cast<const T*>(a.q) + tok0 * rowstride + (size_t)h * D, rbytes);
+    const rsrc_t ro = make_rsrc(static_cast<T*>(a.o) + tok0 * rowstride + (size_t)h * D, rbytes);
+    const uint32_t row_bytes = (uint32_t)(H * D * C::SZ);
+    const int nloc = nend - nbeg;
+    const int nblk = (nloc + C::BT - 1) / C::BT;
+
+    // loader role: row lr of each pass, 16-byte column lc
+    const int lc = tid % C::LPR, lr = tid / C::LPR;
+    struct QStage {
+        u32x4 v[C::NLD];
+    };
+    auto load_blk = [&](int blk, QStage& R) {
+        const uint32_t base = (uint32_t)(blk * C::BT + lr) * row_bytes + (uint32_t)(lc * 16);
+#pragma unroll
+        for (int i = 0; i < C::NLD; ++i) R.v[i] = bload16(rq, base + (uint32_t)(i * C::RPP) * row_bytes);
+    };
+    auto put_blk = [&](const QStage& R, unsigned char* buf) {
+#pragma unroll
+        for (int i = 0; i < C::NLD; ++i)
+            *reinterpret_cast<u32x4*>(buf + (lr + i * C::RPP) * C::ROWB + lc * 16) = R.v[i];
+    };
 
     // ---- S_f rows of this wave as A fragments
     const unsigned char* sp = a.ws + (size_t)item * WS<D>::item_bytes + WS<D>::sp_off;
@@ -565,64 +811,86 @@ __global__ __launch_bounds__(256) void frame_output_kernel(ScanArgs a) {
         const int row = (wr * C::RPW + i) * 16 + r;
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
-            const int c0 = ks * 32 + 8 * g;
-            if (c0 < D) {
-                ah[i][ks] = io::load(s_hi + (size_t)row * D + c0);
-                if constexpr (sizeof(T) == 2) alw[i][ks] = io::load(s_lo + (size_t)row * D + c0);
-            } else {
-                ah[i][ks] = io::zero();
-                alw[i][ks] = io::zero();
-            }
+            const int c0 = (ks * 32 + 8 * g) % D;
+            ah[i][ks] = kvalid ? io::load(s_hi + (size_t)row * D + c0) : io::zero();
+            if constexpr (sizeof(T) == 2)
+                alw[i][ks] = kvalid ? io::load(s_lo + (size_t)row * D + c0) : io::zero();
         }
     }
 
-    const size_t rowstride = (size_t)H * D;
-    const size_t tok0 = ((size_t)b * a.F + f) * (size_t)N;
-    const T* qb = static_cast<const T*>(a.q) + tok0 * rowstride + (size_t)h * D;
-    T* ob = static_cast<T*>(a.o) + tok0 * rowstride + (size_t)h * D;
-
-    auto load_q = [&](int t0, frag (&bq)[C::KS]) {
-        const int n = t0 + r;
-#pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
-            const int c0 = ks * 32 + 8 * g;
-            bq[ks] = (n < nend && c0 < D) ? io::load(qb + (size_t)n * rowstride + c0) : io::zero();
-        }
-    };
-
-    const int step = 16 * C::TG;
-    int t0 = nbeg + 16 * wt;
-    frag cq[C::KS], nq[C::KS];
-    if (t0 < nend) load_q(t0, cq);
-    for (; t0 < nend; t0 += step) {
-        if (t0 + step < nend) load_q(t0 + step, nq);
-        f32x4 acc[C::RPW];
-#pragma unroll
-        for (int i = 0; i < C::RPW; ++i) {
-            acc[i] = f32x4{0, 0, 0, 0};
+    auto compute_blk = [&](int blk, const unsigned char* buf) {
+#pragma unroll 1
+        for (int sb = wt; sb < C::BT / 16; sb += C::TG) {       // 16-token sub-blocks
+            frag bq[C::KS];
 #pragma unroll
             for (int ks = 0; ks < C::KS; ++ks) {
-                io::mma(acc[i], ah[i][ks], cq[ks]);
-                if constexpr (sizeof(T) == 2) io::mma(acc[i], alw[i][ks], cq[ks]);
+                const int c0 = (ks * 32 + 8 * g) % D;
+                const unsigned char* src = buf + (sb * 16 + r) * C::ROWB + c0 * C::SZ;
+                if constexpr (sizeof(T) == 2) {
+                    bq[ks] = *reinterpret_cast<const u32x4*>(src);
+                } else {
+                    const f32x4 lo = *reinterpret_cast<const f32x4*>(src);
+                    const f32x4 hi = *reinterpret_cast<const f32x4*>(src + 16);
+                    bq[ks] = f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                }
+                if (!kvalid) bq[ks] = io::zero();
             }
-        }
-        const int n = t0 + r;
-        if (n < nend) {
+            f32x4 acc[C::RPW];
 #pragma unroll
             for (int i = 0; i < C::RPW; ++i) {
-                const int col0 = (wr * C::RPW + i) * 16 + 4 * g;   // output features a..a+3
-                T* dst = ob + (size_t)n * rowstride + col0;
+                acc[i] = f32x4{0, 0, 0, 0};
+#pragma unroll
+                for (int ks = 0; ks < C::KS; ++ks) {
+                    io::mma(acc[i], ah[i][ks], bq[ks]);
+                    if constexpr (sizeof(T) == 2) io::mma(acc[i], alw[i][ks], bq[ks]);
+                }
+            }
+            const uint32_t n = (uint32_t)(blk * C::BT + sb * 16 + r);   // local token
+#pragma unroll
+            for (int i = 0; i < C::RPW; ++i) {
+                const uint32_t col0 = (uint32_t)((wr * C::RPW + i) * 16 + 4 * g);   // a..a+3
+                const uint32_t off = n * row_bytes + col0 * C::SZ;
                 if constexpr (sizeof(T) == 2) {
-                    const uint32_t x0 = f2bf(acc[i][0]), x1 = f2bf(acc[i][1]);
-                    const uint32_t x2 = f2bf(acc[i][2]), x3 = f2bf(acc[i][3]);
-                    *reinterpret_cast<u32x2*>(dst) = u32x2{x0 | (x1 << 16), x2 | (x3 << 16)};
+                    bstore8(ro, off, u32x2{pack_bf16x2(acc[i][0], acc[i][1]),
+                                           pack_bf16x2(acc[i][2], acc[i][3])});
                 } else {
-                    *reinterpret_cast<f32x4*>(dst) = acc[i];
+                    bstore16(ro, off, u32x4{__float_as_uint(acc[i][0]), __float_as_uint(acc[i][1]),
+                                            __float_as_uint(acc[i][2]), __float_as_uint(acc[i][3])});
                 }
             }
         }
+    };
+
+    // ---- pipeline over 64-token blocks: ring slot blk % PD, LDS buffer blk & 1.
+    // One barrier per block: a wave at the barrier of block blk has finished
+    // computing block blk-1, whose buffer block blk+1 overwrites.
+    // Full groups of PD blocks run without conditions (exact wait counts); the
+    // remainder consumes the blocks already in the ring.
+    static_assert(C::PD % 2 == 0, "ring slot parity must match the LDS buffer parity");
+    QStage ring[C::PD];
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) cq[ks] = nq[ks];
+    for (int j = 0; j < C::PD; ++j) load_blk(j, ring[j]);
+    const int nfull = nblk / C::PD;
+    for (int gi = 0; gi < nfull; ++gi) {
+#pragma unroll
+        for (int j = 0; j < C::PD; ++j) {
+            const int blk = gi * C::PD + j;
+            unsigned char* buf = smem + (j & 1) * (C::BT * C::ROWB);
+            put_blk(ring[j], buf);
+            __syncthreads();
+            load_blk(blk + C::PD, ring[j]);       // past the range: zeros, no traffic
+            compute_blk(blk, buf);
+        }
+    }
+    const int rem = nblk - nfull * C::PD;
+#pragma unroll
+    for (int j = 0; j < C::PD; ++j) {
+        if (j < rem) {
+            unsigned char* buf = smem + (j & 1) * (C::BT * C::ROWB);
+            put_blk(ring[j], buf);
+            __syncthreads();
+            compute_blk(nfull * C::PD + j, buf);
+        }
     }
 }
 
