@@ -114,7 +114,7 @@ gdn_status check_desc(const gdn_desc* d, bool step, Plan* p) {
     p->units = (int64_t)d->B * d->H;
     // frames per launch chunk (state_scan stages the chunk's gates in LDS)
     p->Fc = d->F < gdn::kMaxChunkFrames ? d->F : gdn::kMaxChunkFrames;
-    p->item_bytes = (size_t)12 * p->D * p->D;
+    p->item_bytes = gdn::ws_item_bytes(p->esz, p->D);
     p->ws_bytes = (p->units > 0 && d->F > 0) ? (size_t)p->units * p->Fc * p->item_bytes : 0;
     return GDN_OK;
 }

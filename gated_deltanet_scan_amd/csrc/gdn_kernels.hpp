@@ -141,18 +141,41 @@ template <> struct IO<float> {
     __device__ static __forceinline__ uint32_t bits(float x) { return __float_as_uint(x); }
 };
 
-// Workspace: per (b, h, local frame) item, a block of 12*D*D bytes:
-//   [0, 4D^2)     Gm^T  (bf16 mode: hi plane then lo plane; fp32 mode: fp32)
-//   [4D^2, 8D^2)  U^T   fp32
-//   [8D^2, 12D^2) S_f   (bf16 mode: hi plane then lo plane; fp32 mode: fp32), [a][e]
-// with Gm^T[e][c] = -alpha G[c][e] and U^T[e][a] = U[a][e]: the transposes make
-// state_scan's operand and accumulator loads contiguous 16-byte runs.
-template <int D> struct WS {
-    static constexpr size_t item_bytes = (size_t)12 * D * D;
+// Workspace: per (b, h, local frame) item, three D x D matrices stored
+// fragment-major.  An MFMA fragment (64 lanes x 8 contraction values) is kept
+// as 64 consecutive 16-byte lane slots (bf16: one 1 KiB block; fp32: two
+// 1 KiB blocks with values 0-3 and 4-7 of every lane), so that every 64-lane
+// load or store of it touches one contiguous KiB.
+//   Gm^T   operand of state_scan: rows e, contraction c; Gm^T[e][c] = -alpha G[c][e]
+//          (bf16 mode: hi plane then lo plane; fp32 mode: one fp32 plane)
+//   U^T    accumulator tiles of state_scan: block (e-tile, a-tile) holds, in
+//          lane 16g+r, U[16a_t + 4g + t][16e_t + r] for t = 0..3 (fp32)
+//   S_f    operand of frame_output: rows a, contraction e (planes as Gm)
+template <typename T, int D> struct WS {
+    static constexpr int KS = (D + 31) / 32;                  // contraction fragments per tile
+    static constexpr int RT = D / 16;                         // 16-row tiles
+    static constexpr int NPL = sizeof(T) == 2 ? 2 : 1;        // planes per operand (hi, lo)
+    static constexpr size_t FRAG = sizeof(T) == 2 ? 1024 : 2048;
+    static constexpr size_t OPND = (size_t)RT * KS * FRAG;    // one operand plane
     static constexpr size_t gm_off = 0;
-    static constexpr size_t ut_off = (size_t)4 * D * D;
-    static constexpr size_t sp_off = (size_t)8 * D * D;
+    static constexpr size_t ut_off = NPL * OPND;
+    static constexpr size_t sp_off = ut_off + (size_t)RT * RT * 1024;
+    static constexpr size_t item_bytes = sp_off + NPL * OPND;
+    // byte offset of lane `lane`'s slot in operand fragment (tile, kt), half h (fp32)
+    __device__ static __forceinline__ uint32_t frag_off(int tile, int kt, int h, int lane) {
+        return (uint32_t)((tile * KS + kt) * FRAG) + (uint32_t)(h * 1024 + lane * 16);
+    }
 };
+
+// Host-side copy of the per-item workspace size (must match WS<T, D>).
+constexpr size_t ws_item_bytes(int esz, int D) {
+    const size_t KS = (size_t)(D + 31) / 32, RT = (size_t)D / 16, NPL = esz == 2 ? 2 : 1;
+    const size_t opnd = RT * KS * (esz == 2 ? 1024 : 2048);
+    return 2 * NPL * opnd + RT * RT * 1024;
+}
+static_assert(ws_item_bytes(2, 16) == WS<uint16_t, 16>::item_bytes && ws_item_bytes(2, 128) == WS<uint16_t, 128>::item_bytes &&
+                  ws_item_bytes(4, 16) == WS<float, 16>::item_bytes && ws_item_bytes(4, 64) == WS<float, 64>::item_bytes,
+              "host and device workspace layouts disagree");
 
 struct ScanArgs {
     const void* q;
@@ -430,12 +453,14 @@ __global__ __launch_bounds__(512, 1) void frame_gram_kernel(ScanArgs a) {
             }
         }
     };
-    // Gm^T = -alpha G^T (hi/lo planes or fp32) and U^T (fp32) of item k
+    // Gm^T = -alpha G^T (hi/lo planes or fp32) and U^T (fp32) of item k, in
+    // the fragment-major layout state_scan loads
     auto epilogue = [&](int k) {
+        using W = WS<T, D>;
         const Item it = item_of(k);
         float al = a.alpha[((size_t)it.b * a.F + it.f) * H + it.h];
         if (a.logits) al = sigmoid_f(al);
-        unsigned char* wsi = a.ws + (size_t)it.ws * WS<D>::item_bytes;
+        unsigned char* wsi = a.ws + (size_t)it.ws * W::item_bytes;
 #pragma unroll
         for (int i = 0; i < C::NRW; ++i) {
             const int gb = wave + 4 * i;
@@ -443,27 +468,27 @@ __global__ __launch_bounds__(512, 1) void frame_gram_kernel(ScanArgs a) {
 #pragma unroll
             for (int j = 0; j < C::RB; ++j) {
                 const f32x4 x = acc[i][j];
-                const int col = j * 16 + r;                    // e
                 if (gb < C::RB) {
-                    const int row0 = gb * 16 + 4 * g;           // c
-                    const size_t idx = (size_t)col * D + row0;  // Gm^T[e][c..c+3]
+                    // lane (r, g) holds G[16gb + 4g + t][16j + r] = Gm^T[e][c] with e = 16j + r:
+                    // fragment (e-tile j, kt = gb/2), lane slot 16*g' + r with
+                    // g' = 2*(gb%2) + g/2, values 4*(g%2) + t
                     const f32x4 m = x * (-al);
+                    const int slot = 16 * (2 * (gb & 1) + (g >> 1)) + r;
                     if constexpr (sizeof(T) == 2) {
-                        uint16_t* hi = reinterpret_cast<uint16_t*>(wsi + WS<D>::gm_off);
-                        uint16_t* lo = hi + (size_t)D * D;
+                        const uint32_t off = W::gm_off + W::frag_off(j, gb >> 1, 0, slot) + (g & 1) * 8;
                         const uint32_t h01 = pack_bf16x2(m[0], m[1]), h23 = pack_bf16x2(m[2], m[3]);
                         const uint32_t l01 = pack_bf16x2(m[0] - bf2f(h01 & 0xffffu), m[1] - bf2f(h01 >> 16));
                         const uint32_t l23 = pack_bf16x2(m[2] - bf2f(h23 & 0xffffu), m[3] - bf2f(h23 >> 16));
-                        *reinterpret_cast<u32x2*>(hi + idx) = u32x2{h01, h23};
-                        *reinterpret_cast<u32x2*>(lo + idx) = u32x2{l01, l23};
+                        *reinterpret_cast<u32x2*>(wsi + off) = u32x2{h01, h23};
+                        *reinterpret_cast<u32x2*>(wsi + off + W::OPND) = u32x2{l01, l23};
                     } else {
-                        float* gm = reinterpret_cast<float*>(wsi + WS<D>::gm_off);
-                        *reinterpret_cast<f32x4*>(gm + idx) = m;
+                        const uint32_t off = W::gm_off + W::frag_off(j, gb >> 1, g & 1, slot);
+                        *reinterpret_cast<f32x4*>(wsi + off) = m;
                     }
                 } else {
-                    const int row0 = (gb - C::RB) * 16 + 4 * g;  // a
-                    float* ut = reinterpret_cast<float*>(wsi + WS<D>::ut_off);
-                    *reinterpret_cast<f32x4*>(ut + (size_t)col * D + row0) = x;
+                    // lane (r, g) holds U[16ga + 4g + t][16j + r]: block (j, ga), slot 16g + r
+                    const int ga = gb - C::RB;
+                    *reinterpret_cast<f32x4*>(wsi + W::ut_off + (size_t)(j * W::RT + ga) * 1024 + lane * 16) = x;
                 }
             }
         }
@@ -607,23 +632,27 @@ __global__ __launch_bounds__(D >= 32 ? 2 * D : 64, 1) void state_scan_kernel(Sca
         f32x4 u[C::CT];           // U rows of this tile, accumulator layout
     };
     const size_t item0 = (size_t)bh * Fc;
-    // Loads of frame fl (always a valid frame: callers clamp).  For D = 16 the
-    // upper half of the contraction lanes reads in-bounds data zeroed at use.
+    using W = WS<T, D>;
+    // Loads of frame fl (always a valid frame: callers clamp); every load is
+    // one contiguous KiB of a fragment-major workspace matrix.
     auto load_ops = [&](int fl, Ops& o) {
-        const unsigned char* wsi = a.ws + (item0 + fl) * WS<D>::item_bytes;
-        const T* gm = reinterpret_cast<const T*>(wsi + WS<D>::gm_off);
-        const float* ut = reinterpret_cast<const float*>(wsi + WS<D>::ut_off);
+        const unsigned char* wsi = a.ws + (item0 + fl) * W::item_bytes;
 #pragma unroll
         for (int ct = 0; ct < C::CT; ++ct) {
-            const int col = (wave * C::CT + ct) * 16 + r;   // e
+            const int et = wave * C::CT + ct;                // e-tile
 #pragma unroll
             for (int ks = 0; ks < C::KS; ++ks) {
-                const int c0 = (ks * 32 + 8 * g) % D;
-                o.bh_[ct][ks] = io::load(gm + (size_t)col * D + c0);
-                if constexpr (sizeof(T) == 2)
-                    o.bl_[ct][ks] = io::load(gm + (size_t)D * D + (size_t)col * D + c0);
+                if constexpr (sizeof(T) == 2) {
+                    const unsigned char* gp = wsi + W::gm_off + W::frag_off(et, ks, 0, lane);
+                    o.bh_[ct][ks] = *reinterpret_cast<const u32x4*>(gp);
+                    o.bl_[ct][ks] = *reinterpret_cast<const u32x4*>(gp + W::OPND);
+                } else {
+                    const f32x4 lo = *reinterpret_cast<const f32x4*>(wsi + W::gm_off + W::frag_off(et, ks, 0, lane));
+                    const f32x4 hi = *reinterpret_cast<const f32x4*>(wsi + W::gm_off + W::frag_off(et, ks, 1, lane));
+                    o.bh_[ct][ks] = f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                }
             }
-            o.u[ct] = *reinterpret_cast<const f32x4*>(ut + (size_t)col * D + a0 + 4 * g);
+            o.u[ct] = *reinterpret_cast<const f32x4*>(wsi + W::ut_off + (size_t)(et * W::RT + rt) * 1024 + lane * 16);
         }
     };
     const bool kvalid = 8 * g < D || D >= 32;          // D = 16: lanes g >= 2 carry zeros
@@ -631,23 +660,23 @@ __global__ __launch_bounds__(D >= 32 ? 2 * D : 64, 1) void state_scan_kernel(Sca
     // Workspace S planes of this unit's frames through a buffer resource: the
     // copy issued for frame -1 (before the first frame) falls outside it and
     // is dropped, so the copy needs no branch.
-    const rsrc_t rsp = make_rsrc(a.ws + item0 * WS<D>::item_bytes, (uint32_t)(Fc * WS<D>::item_bytes));
-    constexpr int rowbytes = D * io::bytes;
-    constexpr int chunks = 16 * rowbytes / 16;          // per plane
+    const rsrc_t rsp = make_rsrc(a.ws + item0 * W::item_bytes, (uint32_t)(Fc * W::item_bytes));
+    constexpr int NH = sizeof(T) == 2 ? 1 : 2;          // 16-byte halves per lane slot
+    constexpr int SLOTS = C::NPL * C::KS * NH * 64;     // 16-byte slots this tile writes
     auto copy_planes = [&](int fl, int buf) {           // S_fl, held in sS[buf], to frame fl
         // frame -1 maps to 2 GiB: past the resource (at most 256 frames of
         // 192 KiB) with no 32-bit overflow once the plane offset is added
-        const uint32_t base = fl >= 0 ? (uint32_t)fl * (uint32_t)WS<D>::item_bytes + (uint32_t)WS<D>::sp_off
+        const uint32_t base = fl >= 0 ? (uint32_t)fl * (uint32_t)W::item_bytes + (uint32_t)W::sp_off
                                       : 0x80000000u;
 #pragma unroll
-        for (int x0 = 0; x0 < C::NPL * chunks; x0 += C::NW * 64) {
+        for (int x0 = 0; x0 < SLOTS; x0 += C::NW * 64) {
             const int x = x0 + tid;
-            if (C::NPL * chunks % (C::NW * 64) == 0 || x < C::NPL * chunks) {
-                const int pl = x / chunks, cc = x % chunks;
-                const int row = cc / (rowbytes / 16), col16 = cc % (rowbytes / 16);
-                const u32x4 val = *reinterpret_cast<const u32x4*>(&sS[buf][pl][row * C::ROWB + col16 * 16]);
-                bstore16(rsp, base + (uint32_t)(pl * D * D * io::bytes + (a0 + row) * rowbytes + col16 * 16),
-                         val);
+            if (SLOTS % (C::NW * 64) == 0 || x < SLOTS) {
+                const int l = x & 63, hh = (x >> 6) % NH, kt = (x / (64 * NH)) % C::KS;
+                const int pl = x / (64 * NH * C::KS);
+                const int c0 = (kt * 32 + 8 * (l >> 4) + 4 * hh) % D;   // D = 16: upper lanes repeat
+                const u32x4 val = *reinterpret_cast<const u32x4*>(&sS[buf][pl][(l & 15) * C::ROWB + c0 * io::bytes]);
+                bstore16(rsp, base + (uint32_t)(pl * W::OPND) + W::frag_off(rt, kt, hh, l), val);
             }
         }
     };
@@ -679,10 +708,17 @@ __global__ __launch_bounds__(D >= 32 ? 2 * D : 64, 1) void state_scan_kernel(Sca
 #pragma unroll
             for (int ct = 0; ct < C::CT; ++ct) {
                 f32x4& dst = (ks & 1) ? acc2[ct] : acc[ct];
-                io::mma(dst, ahi, o.bh_[ct][ks]);
+                frag bhi = o.bh_[ct][ks], blo = o.bl_[ct][ks];
+                if constexpr (D < 32) {            // unwritten upper lanes of the fragment
+                    if (!kvalid) {
+                        bhi = io::zero();
+                        blo = io::zero();
+                    }
+                }
+                io::mma(dst, ahi, bhi);
                 if constexpr (sizeof(T) == 2) {
-                    io::mma(dst, alo, o.bh_[ct][ks]);
-                    io::mma(dst, ahi, o.bl_[ct][ks]);
+                    io::mma(dst, alo, bhi);
+                    io::mma(dst, ahi, blo);
                 }
             }
         }
@@ -801,20 +837,27 @@ __global__ __launch_bounds__(256, 2) void frame_output_kernel(ScanArgs a) {
             *reinterpret_cast<u32x4*>(buf + (lr + i * C::RPP) * C::ROWB + lc * 16) = R.v[i];
     };
 
-    // ---- S_f rows of this wave as A fragments
-    const unsigned char* sp = a.ws + (size_t)item * WS<D>::item_bytes + WS<D>::sp_off;
-    const T* s_hi = reinterpret_cast<const T*>(sp);
-    const T* s_lo = s_hi + (size_t)D * D;         // bf16 mode only
+    // ---- S_f rows of this wave as A fragments (fragment-major workspace)
+    using W = WS<T, D>;
+    const unsigned char* sp = a.ws + (size_t)item * W::item_bytes + W::sp_off;
     frag ah[C::RPW][C::KS], alw[C::RPW][C::KS];
 #pragma unroll
     for (int i = 0; i < C::RPW; ++i) {
-        const int row = (wr * C::RPW + i) * 16 + r;
+        const int rt = wr * C::RPW + i;
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
-            const int c0 = (ks * 32 + 8 * g) % D;
-            ah[i][ks] = kvalid ? io::load(s_hi + (size_t)row * D + c0) : io::zero();
-            if constexpr (sizeof(T) == 2)
-                alw[i][ks] = kvalid ? io::load(s_lo + (size_t)row * D + c0) : io::zero();
+            if constexpr (sizeof(T) == 2) {
+                ah[i][ks] = *reinterpret_cast<const u32x4*>(sp + W::frag_off(rt, ks, 0, lane));
+                alw[i][ks] = *reinterpret_cast<const u32x4*>(sp + W::OPND + W::frag_off(rt, ks, 0, lane));
+            } else {
+                const f32x4 lo = *reinterpret_cast<const f32x4*>(sp + W::frag_off(rt, ks, 0, lane));
+                const f32x4 hi = *reinterpret_cast<const f32x4*>(sp + W::frag_off(rt, ks, 1, lane));
+                ah[i][ks] = f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            }
+            if (!kvalid) {
+                ah[i][ks] = io::zero();
+                alw[i][ks] = io::zero();
+            }
         }
     }
 
