@@ -56,6 +56,41 @@ struct ProfScope {
     }
 };
 
+// ---------------------------------------------------------------- side stream
+// One non-blocking stream per device (default priority) runs the state
+// recurrence while the caller's stream runs the output pass; events order them.
+struct Side {
+    hipStream_t stream = nullptr;
+    bool failed = false;
+    std::vector<hipEvent_t> ev;
+    size_t next = 0;
+};
+std::mutex g_side_mu;
+Side g_side[64];
+
+hipStream_t side_stream(int dev) {
+    Side& sd = g_side[dev];
+    if (!sd.stream && !sd.failed) {
+        if (hipStreamCreateWithFlags(&sd.stream, hipStreamNonBlocking) != hipSuccess) {
+            sd.stream = nullptr;
+            sd.failed = true;
+        }
+    }
+    return sd.stream;
+}
+hipEvent_t side_event(int dev) {
+    Side& sd = g_side[dev];
+    if (sd.ev.size() < 64) {
+        hipEvent_t e;
+        if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return nullptr;
+        sd.ev.push_back(e);
+        return e;
+    }
+    hipEvent_t e = sd.ev[sd.next];
+    sd.next = (sd.next + 1) % sd.ev.size();
+    return e;
+}
+
 // ---------------------------------------------------------------- device checks
 struct DevInfo {
     bool known = false;
@@ -89,8 +124,14 @@ struct Plan {
     int64_t units = 0;       // B*H
     int Fc = 0;              // frames per launch chunk
     size_t item_bytes = 0;   // workspace per (b, h, frame)
+    size_t carry_off = 0;    // fp32 [B][H][Dv][Dk] state carried between launches
     size_t ws_bytes = 0;
 };
+
+// Frames per state_scan / frame_output launch when the recurrence is
+// pipelined against the output pass on a second stream.
+constexpr int kPipeFrames = 32;
+constexpr bool kPipeline = false;   // overlap measured slower: both passes are L1-fill bound
 
 bool dim_ok(int D) { return D == 16 || D == 32 || D == 64 || D == 128; }
 
@@ -115,7 +156,10 @@ gdn_status check_desc(const gdn_desc* d, bool step, Plan* p) {
     // frames per launch chunk (state_scan stages the chunk's gates in LDS)
     p->Fc = d->F < gdn::kMaxChunkFrames ? d->F : gdn::kMaxChunkFrames;
     p->item_bytes = gdn::ws_item_bytes(p->esz, p->D);
-    p->ws_bytes = (p->units > 0 && d->F > 0) ? (size_t)p->units * p->Fc * p->item_bytes : 0;
+    p->carry_off = ((size_t)p->units * p->Fc * p->item_bytes + 255) / 256 * 256;
+    p->ws_bytes = (p->units > 0 && d->F > 0)
+                      ? p->carry_off + (size_t)p->units * p->D * p->D * sizeof(float)
+                      : 0;
     return GDN_OK;
 }
 
@@ -130,11 +174,52 @@ bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.
 bool aligned(const void* p, uintptr_t al) { return ((uintptr_t)p & (al - 1)) == 0; }
 
 template <typename T, int D>
-gdn_status launch_all(const Plan& p, ScanArgs a, hipStream_t stream, int cus) {
+gdn_status launch_state(ScanArgs a, hipStream_t stream) {
+    using SC = gdn::StateCfg<T, D>;
+    const int units = a.B * a.H;
+    const int grid = 8 * ((units + 7) / 8) * SC::RG;
+    ProfScope ps(K_STATE, stream);
+    hipLaunchKernelGGL((gdn::state_scan_kernel<T, D>), dim3(grid), dim3(SC::NW * 64), 0, stream, a);
+    return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
+template <typename T, int D>
+gdn_status launch_output(ScanArgs a, hipStream_t stream, int cus) {
+    if (a.N <= 0 || a.Fc <= 0) return GDN_OK;
+    const int items = a.B * a.H * a.Fc;
+    // token ranges per frame: enough workgroups to cover every CU a few times
+    const int want = 4 * (cus > 0 ? cus : 256);
+    int tsplit = (want + items - 1) / items;
+    const int maxsplit = (a.N + 63) / 64;
+    if (tsplit > maxsplit) tsplit = maxsplit;
+    if (tsplit < 1) tsplit = 1;
+    int tchunk = (a.N + tsplit - 1) / tsplit;
+    tchunk = (tchunk + 15) / 16 * 16;
+    tsplit = (a.N + tchunk - 1) / tchunk;
+    a.tsplit = tsplit;
+    a.tchunk = tchunk;
+    ProfScope ps(K_OUTPUT, stream);
+    hipLaunchKernelGGL((gdn::frame_output_kernel<T, D>), dim3(items * tsplit), dim3(256), 0, stream, a);
+    return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
+// Launch order.  frame_gram covers a chunk of up to kMaxChunkFrames frames on
+// the caller's stream.  The recurrence then runs in sub-chunks of kPipeFrames
+// frames on the side stream; each sub-chunk's output pass waits (on the
+// caller's stream) for that sub-chunk only, so outputs of early frames overlap
+// the recurrence of later ones.  The state is carried in `carry` (S_final, or
+// the workspace's carry region).  Everything the call enqueues is ordered
+// before the caller's stream continues: the last output pass waits for the
+// last recurrence launch.
+template <typename T, int D>
+gdn_status launch_all(const Plan& p, ScanArgs a, hipStream_t stream, int cus, float* carry, int dev) {
     const int units = (int)p.units;
+    gdn_status st = GDN_OK;
     for (int f0 = 0; f0 < a.F; f0 += p.Fc) {
         a.f0 = f0;
         a.Fc = a.F - f0 < p.Fc ? a.F - f0 : p.Fc;
+        a.wsFc = a.Fc;
+        a.fsub0 = 0;
         const int items = units * a.Fc;
         {
             ProfScope ps(K_GRAM, stream);
@@ -143,44 +228,48 @@ gdn_status launch_all(const Plan& p, ScanArgs a, hipStream_t stream, int cus) {
             hipLaunchKernelGGL((gdn::frame_gram_kernel<T, D>), dim3(grid), dim3(512), 0, stream, a);
         }
         if (hipGetLastError() != hipSuccess) return GDN_ERR_LAUNCH;
-        {
-            using SC = gdn::StateCfg<T, D>;
-            const int grid = 8 * ((units + 7) / 8) * SC::RT;
-            ProfScope ps(K_STATE, stream);
-            hipLaunchKernelGGL((gdn::state_scan_kernel<T, D>), dim3(grid), dim3(SC::NW * 64), 0, stream,
-                               a);
+
+        hipStream_t side = nullptr;
+        if (kPipeline && a.N > 0 && a.Fc > kPipeFrames) {
+            std::lock_guard<std::mutex> lk(g_side_mu);
+            side = side_stream(dev);
         }
-        if (hipGetLastError() != hipSuccess) return GDN_ERR_LAUNCH;
-        // chained chunks carry the state through S_out
-        a.S_in = a.S_out;
-        if (a.N > 0) {
-            // token ranges per frame: enough workgroups to cover every CU a few times
-            const int want = 4 * (cus > 0 ? cus : 256);
-            int tsplit = (want + items - 1) / items;
-            const int maxsplit = (a.N + 63) / 64;
-            if (tsplit > maxsplit) tsplit = maxsplit;
-            if (tsplit < 1) tsplit = 1;
-            int tchunk = (a.N + tsplit - 1) / tsplit;
-            tchunk = (tchunk + 15) / 16 * 16;
-            tsplit = (a.N + tchunk - 1) / tchunk;
-            a.tsplit = tsplit;
-            a.tchunk = tchunk;
-            ProfScope ps(K_OUTPUT, stream);
-            hipLaunchKernelGGL((gdn::frame_output_kernel<T, D>), dim3(items * tsplit), dim3(256), 0,
-                               stream, a);
+        if (!side) {                                   // one stream: recurrence, then outputs
+            ScanArgs s = a;
+            s.S_out = carry;
+            if ((st = launch_state<T, D>(s, stream)) != GDN_OK) return st;
+            a.S_in = carry;
+            if ((st = launch_output<T, D>(a, stream, cus)) != GDN_OK) return st;
+            continue;
         }
-        if (hipGetLastError() != hipSuccess) return GDN_ERR_LAUNCH;
+        std::lock_guard<std::mutex> lk(g_side_mu);
+        hipEvent_t eg = side_event(dev);
+        if (!eg || hipEventRecord(eg, stream) != hipSuccess || hipStreamWaitEvent(side, eg, 0) != hipSuccess)
+            return GDN_ERR_LAUNCH;
+        for (int s0 = 0; s0 < a.Fc; s0 += kPipeFrames) {
+            ScanArgs s = a;
+            s.fsub0 = s0;
+            s.Fc = a.Fc - s0 < kPipeFrames ? a.Fc - s0 : kPipeFrames;
+            s.S_out = carry;
+            if ((st = launch_state<T, D>(s, side)) != GDN_OK) return st;
+            a.S_in = carry;
+            hipEvent_t es = side_event(dev);
+            if (!es || hipEventRecord(es, side) != hipSuccess || hipStreamWaitEvent(stream, es, 0) != hipSuccess)
+                return GDN_ERR_LAUNCH;
+            s.S_in = carry;
+            if ((st = launch_output<T, D>(s, stream, cus)) != GDN_OK) return st;
+        }
     }
     return GDN_OK;
 }
 
 template <typename T>
-gdn_status dispatch_d(const Plan& p, const ScanArgs& a, hipStream_t s, int cus) {
+gdn_status dispatch_d(const Plan& p, const ScanArgs& a, hipStream_t s, int cus, float* carry, int dev) {
     switch (p.D) {
-        case 16: return launch_all<T, 16>(p, a, s, cus);
-        case 32: return launch_all<T, 32>(p, a, s, cus);
-        case 64: return launch_all<T, 64>(p, a, s, cus);
-        case 128: return launch_all<T, 128>(p, a, s, cus);
+        case 16: return launch_all<T, 16>(p, a, s, cus, carry, dev);
+        case 32: return launch_all<T, 32>(p, a, s, cus, carry, dev);
+        case 64: return launch_all<T, 64>(p, a, s, cus, carry, dev);
+        case 128: return launch_all<T, 128>(p, a, s, cus, carry, dev);
         default: return GDN_ERR_UNSUPPORTED;
     }
 }
@@ -264,10 +353,16 @@ gdn_status run(const gdn_desc* d, bool step, const void* q, const void* k, const
     a.eps = d->eps;
     a.tsplit = 1;
     a.tchunk = 16;
+    a.wsFc = p.Fc;
+    a.fsub0 = 0;
     a.tok_bytes = d->N > 0 ? (uint32_t)(((size_t)(d->N - 1) * d->H * p.D + p.D) * p.esz) : 0u;
-    if (p.Fc < d->F && !S_final) return GDN_ERR_INVALID_ARG;  // chunked carry needs S_final
-    return d->io_dtype == GDN_BF16 ? dispatch_d<uint16_t>(p, a, stream, cus)
-                                   : dispatch_d<float>(p, a, stream, cus);
+    // the state between launches lives in S_final, or in the workspace's carry region
+    float* carry = S_final ? S_final
+                           : reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + p.carry_off);
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    return d->io_dtype == GDN_BF16 ? dispatch_d<uint16_t>(p, a, stream, cus, carry, dev)
+                                   : dispatch_d<float>(p, a, stream, cus, carry, dev);
 }
 
 }  // namespace

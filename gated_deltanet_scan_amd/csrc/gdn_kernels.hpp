@@ -189,7 +189,9 @@ struct ScanArgs {
     float* S_out2;        // optional second copy of that state (NULL: none)
     unsigned char* ws;
     int B, H, F, N;
-    int f0, Fc;           // frames [f0, f0 + Fc) of this launch
+    int f0, Fc;           // frames [f0 + fsub0, f0 + fsub0 + Fc) of this launch
+    int wsFc, fsub0;      // frames per (b, h) held in the workspace, and the first
+                          // of them this launch covers (frame_gram: 0)
     int tsplit;           // token ranges per frame in frame_output
     int tchunk;           // tokens per range (multiple of 16)
     uint32_t tok_bytes;   // bytes from a head's first token row of a frame to the
@@ -298,7 +300,7 @@ __global__ __launch_bounds__(512, 1) void frame_gram_kernel(ScanArgs a) {
         const int fl = (x / H) % a.Fc;
         it.b = x / (H * a.Fc);
         it.f = a.f0 + fl;
-        it.ws = (it.b * H + it.h) * a.Fc + fl;
+        it.ws = (it.b * H + it.h) * a.wsFc + fl;
         return it;
     };
 
@@ -549,77 +551,80 @@ __global__ __launch_bounds__(512, 1) void frame_gram_kernel(ScanArgs a) {
 
 // ================================================================== state_scan
 template <typename T, int D> struct StateCfg {
-    static constexpr int CT = D >= 32 ? 2 : 1;          // 16-column tiles per wave
-    static constexpr int NW = D / (16 * CT);            // waves per workgroup
-    static constexpr int KS = (D + 31) / 32;            // 32-wide contraction steps
     static constexpr int RT = D / 16;                   // row tiles per (b, h)
+    static constexpr int RTW = 1;                       // row tiles per workgroup (2 measured slower)
+    static constexpr int RG = RT / RTW;                 // workgroups per (b, h)
+    static constexpr int NW = D / 16;                   // waves: one 16-column tile each
+    static constexpr int KS = (D + 31) / 32;            // 32-wide contraction steps
     static constexpr int PADB = 16;                     // LDS row padding (bytes)
     static constexpr int ROWB = D * IO<T>::bytes + PADB;
     static constexpr int NPL = sizeof(T) == 2 ? 2 : 1;  // planes (hi, lo) of S in LDS
     // frames of operands in flight: the ring must fit the 6-bit vector-memory
     // counter (63 outstanding loads and stores per wave) or every frame drains it
-    static constexpr int LOADS = CT * KS * (IO<T>::bytes == 2 ? 2 : 2) + CT;
-    static constexpr int PD = (56 / LOADS) < 4 ? (56 / LOADS) : 4;
+    static constexpr int LOADS = KS * 2 + RTW;
+    static constexpr int PD = (48 / LOADS) < 4 ? (48 / LOADS) : 4;
     static_assert(PD >= 2, "ring too shallow");
 };
 
-// One workgroup owns rows [16*rt, 16*rt+16) of one (b, h) state; wave w owns
-// columns [32w, 32w+32) (16 wide for D = 16).  Per frame:
+// One workgroup owns RTW consecutive 16-row tiles of one (b, h) state (rows
+// [16*RTW*rg, 16*RTW*(rg+1))); wave w owns columns [16w, 16w+16) of them.
+// Rows of S evolve independently, so workgroups never communicate.  Per frame:
 //   acc = alpha*S + U_f ;  acc += S_hi Gm_hi + S_lo Gm_hi + S_hi Gm_lo  (bf16)
 //   (fp32 mode: acc += S Gm with fp32 MFMA)
 // S stays in fp32 registers; its bf16 hi/lo split is double-buffered in LDS
 // as the A operand (one barrier per frame), and the previous frame's planes
 // are copied to the workspace for frame_output while this frame's MFMAs run.
-// Each output tile keeps two accumulators (even / odd contraction steps) to
-// halve the dependent MFMA chain.  The operands of the next PD frames are in
-// flight in a register ring.
+// Every workgroup of a head reads all of Gm_f (64 KiB as hi/lo planes) each
+// frame; the per-CU rate of those L2 reads, not the MFMAs, bounds this kernel
+// (about 1.5 us per frame at D = 128), so more rows per workgroup do not help.
+// The operands of the next PD frames are in flight in a register ring.
 template <typename T, int D>
-__global__ __launch_bounds__(D >= 32 ? 2 * D : 64, 1) void state_scan_kernel(ScanArgs a) {  // NW*64
+__global__ __launch_bounds__(4 * D, 1) void state_scan_kernel(ScanArgs a) {  // NW*64 threads
     using C = StateCfg<T, D>;
     using io = IO<T>;
     using frag = typename io::frag;
-    constexpr int PLANE = 16 * C::ROWB;
+    constexpr int ROWS = 16 * C::RTW;
+    constexpr int PLANE = ROWS * C::ROWB;
     __shared__ __attribute__((aligned(16))) unsigned char sS[2][C::NPL][PLANE];
     __shared__ float sAlpha[kMaxChunkFrames];
 
     const int units = a.B * a.H;
-    const int id = xcd_remap(blockIdx.x, C::RT, units * C::RT);
+    const int id = xcd_remap(blockIdx.x, C::RG, units * C::RG);
     if (id < 0) return;
-    const int rt = id % C::RT;
-    const int bh = id / C::RT;
+    const int rg = id % C::RG;
+    const int bh = id / C::RG;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = lane & 15, g = lane >> 4;
-    const int a0 = rt * 16;                             // first state row of this tile
+    const int a0 = rg * ROWS;                           // first state row of this workgroup
     const int h = bh % a.H, b = bh / a.H;
     const int Fc = a.Fc;
+    const int col = wave * 16 + r;                      // this lane's state column e
 
     for (int i = tid; i < Fc; i += C::NW * 64) {
-        const float x = a.alpha[((size_t)b * a.F + a.f0 + i) * a.H + h];
+        const float x = a.alpha[((size_t)b * a.F + a.f0 + a.fsub0 + i) * a.H + h];
         sAlpha[i] = a.logits ? sigmoid_f(x) : x;
     }
 
     // ---- initial state: registers (accumulator layout) and LDS (operand layout)
-    f32x4 S[C::CT];
+    f32x4 S[C::RTW];
     const float* sin = a.S_in ? a.S_in + (size_t)bh * D * D : nullptr;
 #pragma unroll
-    for (int ct = 0; ct < C::CT; ++ct) {
-        const int col = (wave * C::CT + ct) * 16 + r;
+    for (int i = 0; i < C::RTW; ++i)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) S[ct][t] = sin ? sin[(size_t)(a0 + 4 * g + t) * D + col] : 0.0f;
-    }
+        for (int t = 0; t < 4; ++t)
+            S[i][t] = sin ? sin[(size_t)(a0 + 16 * i + 4 * g + t) * D + col] : 0.0f;
     auto put_lds = [&](int buf) {
 #pragma unroll
-        for (int ct = 0; ct < C::CT; ++ct) {
-            const int col = (wave * C::CT + ct) * 16 + r;
+        for (int i = 0; i < C::RTW; ++i) {
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                const int off = (4 * g + t) * C::ROWB + col * io::bytes;
+                const int off = (16 * i + 4 * g + t) * C::ROWB + col * io::bytes;
                 if constexpr (sizeof(T) == 2) {
-                    const uint16_t hi = f2bf(S[ct][t]);
+                    const uint16_t hi = f2bf(S[i][t]);
                     *reinterpret_cast<uint16_t*>(&sS[buf][0][off]) = hi;
-                    *reinterpret_cast<uint16_t*>(&sS[buf][1][off]) = f2bf(S[ct][t] - bf2f(hi));
+                    *reinterpret_cast<uint16_t*>(&sS[buf][1][off]) = f2bf(S[i][t] - bf2f(hi));
                 } else {
-                    *reinterpret_cast<float*>(&sS[buf][0][off]) = S[ct][t];
+                    *reinterpret_cast<float*>(&sS[buf][0][off]) = S[i][t];
                 }
             }
         }
@@ -627,33 +632,32 @@ __global__ __launch_bounds__(D >= 32 ? 2 * D : 64, 1) void state_scan_kernel(Sca
     put_lds(0);
 
     struct Ops {
-        frag bh_[C::CT][C::KS];   // Gm hi (fp32 mode: Gm)
-        frag bl_[C::CT][C::KS];   // Gm lo (bf16 mode only)
-        f32x4 u[C::CT];           // U rows of this tile, accumulator layout
+        frag bh_[C::KS];          // Gm hi (fp32 mode: Gm) for this wave's 16 columns
+        frag bl_[C::KS];          // Gm lo (bf16 mode only)
+        f32x4 u[C::RTW];          // U rows of each row tile, accumulator layout
     };
-    const size_t item0 = (size_t)bh * Fc;
+    const size_t item0 = (size_t)bh * a.wsFc + a.fsub0;
     using W = WS<T, D>;
     // Loads of frame fl (always a valid frame: callers clamp); every load is
     // one contiguous KiB of a fragment-major workspace matrix.
     auto load_ops = [&](int fl, Ops& o) {
         const unsigned char* wsi = a.ws + (item0 + fl) * W::item_bytes;
 #pragma unroll
-        for (int ct = 0; ct < C::CT; ++ct) {
-            const int et = wave * C::CT + ct;                // e-tile
-#pragma unroll
-            for (int ks = 0; ks < C::KS; ++ks) {
-                if constexpr (sizeof(T) == 2) {
-                    const unsigned char* gp = wsi + W::gm_off + W::frag_off(et, ks, 0, lane);
-                    o.bh_[ct][ks] = *reinterpret_cast<const u32x4*>(gp);
-                    o.bl_[ct][ks] = *reinterpret_cast<const u32x4*>(gp + W::OPND);
-                } else {
-                    const f32x4 lo = *reinterpret_cast<const f32x4*>(wsi + W::gm_off + W::frag_off(et, ks, 0, lane));
-                    const f32x4 hi = *reinterpret_cast<const f32x4*>(wsi + W::gm_off + W::frag_off(et, ks, 1, lane));
-                    o.bh_[ct][ks] = f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                }
+        for (int ks = 0; ks < C::KS; ++ks) {
+            if constexpr (sizeof(T) == 2) {
+                const unsigned char* gp = wsi + W::gm_off + W::frag_off(wave, ks, 0, lane);
+                o.bh_[ks] = *reinterpret_cast<const u32x4*>(gp);
+                o.bl_[ks] = *reinterpret_cast<const u32x4*>(gp + W::OPND);
+            } else {
+                const f32x4 lo = *reinterpret_cast<const f32x4*>(wsi + W::gm_off + W::frag_off(wave, ks, 0, lane));
+                const f32x4 hi = *reinterpret_cast<const f32x4*>(wsi + W::gm_off + W::frag_off(wave, ks, 1, lane));
+                o.bh_[ks] = f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
             }
-            o.u[ct] = *reinterpret_cast<const f32x4*>(wsi + W::ut_off + (size_t)(et * W::RT + rt) * 1024 + lane * 16);
         }
+#pragma unroll
+        for (int i = 0; i < C::RTW; ++i)
+            o.u[i] = *reinterpret_cast<const f32x4*>(wsi + W::ut_off +
+                                                     (size_t)(wave * W::RT + rg * C::RTW + i) * 1024 + lane * 16);
     };
     const bool kvalid = 8 * g < D || D >= 32;          // D = 16: lanes g >= 2 carry zeros
 
@@ -662,7 +666,7 @@ __global__ __launch_bounds__(D >= 32 ? 2 * D : 64, 1) void state_scan_kernel(Sca
     // is dropped, so the copy needs no branch.
     const rsrc_t rsp = make_rsrc(a.ws + item0 * W::item_bytes, (uint32_t)(Fc * W::item_bytes));
     constexpr int NH = sizeof(T) == 2 ? 1 : 2;          // 16-byte halves per lane slot
-    constexpr int SLOTS = C::NPL * C::KS * NH * 64;     // 16-byte slots this tile writes
+    constexpr int SLOTS = C::NPL * C::RTW * C::KS * NH * 64;   // 16-byte slots per frame
     auto copy_planes = [&](int fl, int buf) {           // S_fl, held in sS[buf], to frame fl
         // frame -1 maps to 2 GiB: past the resource (at most 256 frames of
         // 192 KiB) with no 32-bit overflow once the plane offset is added
@@ -673,48 +677,53 @@ __global__ __launch_bounds__(D >= 32 ? 2 * D : 64, 1) void state_scan_kernel(Sca
             const int x = x0 + tid;
             if (SLOTS % (C::NW * 64) == 0 || x < SLOTS) {
                 const int l = x & 63, hh = (x >> 6) % NH, kt = (x / (64 * NH)) % C::KS;
-                const int pl = x / (64 * NH * C::KS);
+                const int i = (x / (64 * NH * C::KS)) % C::RTW, pl = x / (64 * NH * C::KS * C::RTW);
                 const int c0 = (kt * 32 + 8 * (l >> 4) + 4 * hh) % D;   // D = 16: upper lanes repeat
-                const u32x4 val = *reinterpret_cast<const u32x4*>(&sS[buf][pl][(l & 15) * C::ROWB + c0 * io::bytes]);
-                bstore16(rsp, base + (uint32_t)(pl * W::OPND) + W::frag_off(rt, kt, hh, l), val);
+                const u32x4 val =
+                    *reinterpret_cast<const u32x4*>(&sS[buf][pl][(16 * i + (l & 15)) * C::ROWB + c0 * io::bytes]);
+                bstore16(rsp, base + (uint32_t)(pl * W::OPND) + W::frag_off(rg * C::RTW + i, kt, hh, l), val);
             }
         }
     };
 
-    auto step = [&](int fl, const Ops& o) {
+    // One frame.  The ring slot `o` is reloaded with frame `nx` as soon as this
+    // frame's MFMAs have been issued, so the loads stream through L1 while the
+    // wave writes the new state to LDS and waits at the barrier.
+    auto step = [&](int fl, Ops& o, int nx, bool reload) {
         const int cur = fl & 1;                         // buffer holding S_{fl-1}
         const float al = sAlpha[fl];
-        f32x4 acc[C::CT], acc2[C::CT];
+        f32x4 acc[C::RTW], acc2[C::RTW];
 #pragma unroll
-        for (int ct = 0; ct < C::CT; ++ct) {
-            acc[ct] = S[ct] * al + o.u[ct];
-            acc2[ct] = f32x4{0, 0, 0, 0};
+        for (int i = 0; i < C::RTW; ++i) {
+            acc[i] = S[i] * al + o.u[i];
+            acc2[i] = f32x4{0, 0, 0, 0};
         }
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
             const int c0 = (ks * 32 + 8 * g) % D;
-            frag ahi, alo;
-            if constexpr (sizeof(T) == 2) {
-                ahi = *reinterpret_cast<const u32x4*>(&sS[cur][0][r * C::ROWB + c0 * 2]);
-                alo = *reinterpret_cast<const u32x4*>(&sS[cur][1][r * C::ROWB + c0 * 2]);
-            } else {
-                ahi = io::load(reinterpret_cast<const float*>(&sS[cur][0][r * C::ROWB + c0 * 4]));
-                alo = io::zero();
-            }
-            if (!kvalid) {
-                ahi = io::zero();
-                alo = io::zero();
+            frag bhi = o.bh_[ks], blo = o.bl_[ks];
+            if constexpr (D < 32) {                    // unwritten upper lanes of the fragment
+                if (!kvalid) {
+                    bhi = io::zero();
+                    blo = io::zero();
+                }
             }
 #pragma unroll
-            for (int ct = 0; ct < C::CT; ++ct) {
-                f32x4& dst = (ks & 1) ? acc2[ct] : acc[ct];
-                frag bhi = o.bh_[ct][ks], blo = o.bl_[ct][ks];
-                if constexpr (D < 32) {            // unwritten upper lanes of the fragment
-                    if (!kvalid) {
-                        bhi = io::zero();
-                        blo = io::zero();
-                    }
+            for (int i = 0; i < C::RTW; ++i) {
+                frag ahi, alo;
+                const int ro = (16 * i + r) * C::ROWB;
+                if constexpr (sizeof(T) == 2) {
+                    ahi = *reinterpret_cast<const u32x4*>(&sS[cur][0][ro + c0 * 2]);
+                    alo = *reinterpret_cast<const u32x4*>(&sS[cur][1][ro + c0 * 2]);
+                } else {
+                    ahi = io::load(reinterpret_cast<const float*>(&sS[cur][0][ro + c0 * 4]));
+                    alo = io::zero();
                 }
+                if (!kvalid) {
+                    ahi = io::zero();
+                    alo = io::zero();
+                }
+                f32x4& dst = (ks & 1) ? acc2[i] : acc[i];
                 io::mma(dst, ahi, bhi);
                 if constexpr (sizeof(T) == 2) {
                     io::mma(dst, alo, bhi);
@@ -722,9 +731,10 @@ __global__ __launch_bounds__(D >= 32 ? 2 * D : 64, 1) void state_scan_kernel(Sca
                 }
             }
         }
+        if (reload) load_ops(nx, o);
         copy_planes(fl - 1, cur);                       // S_{fl-1}: overlaps the MFMAs
 #pragma unroll
-        for (int ct = 0; ct < C::CT; ++ct) S[ct] = acc[ct] + acc2[ct];
+        for (int i = 0; i < C::RTW; ++i) S[i] = acc[i] + acc2[i];
         put_lds(cur ^ 1);
         __syncthreads();                                // S_fl visible; S_{fl-1} reads done
     };
@@ -738,26 +748,24 @@ __global__ __launch_bounds__(D >= 32 ? 2 * D : 64, 1) void state_scan_kernel(Sca
 #pragma unroll
         for (int j = 0; j < C::PD; ++j) {
             const int fl = gi * C::PD + j;
-            step(fl, ring[j]);
             const int nx = fl + C::PD;
-            load_ops(nx < Fc ? nx : Fc - 1, ring[j]);
+            step(fl, ring[j], nx < Fc ? nx : Fc - 1, true);
         }
     }
     const int rem = Fc - nfull * C::PD;
 #pragma unroll
     for (int j = 0; j < C::PD; ++j)
-        if (j < rem) step(nfull * C::PD + j, ring[j]);
+        if (j < rem) step(nfull * C::PD + j, ring[j], 0, false);
     copy_planes(Fc - 1, Fc & 1);                        // the last frame's S planes
 
     // ---- final state (fp32, row-major [a][e])
 #pragma unroll
-    for (int ct = 0; ct < C::CT; ++ct) {
-        const int col = (wave * C::CT + ct) * 16 + r;
+    for (int i = 0; i < C::RTW; ++i) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const size_t idx = (size_t)bh * D * D + (size_t)(a0 + 4 * g + t) * D + col;
-            if (a.S_out) a.S_out[idx] = S[ct][t];
-            if (a.S_out2) a.S_out2[idx] = S[ct][t];
+            const size_t idx = (size_t)bh * D * D + (size_t)(a0 + 16 * i + 4 * g + t) * D + col;
+            if (a.S_out) a.S_out[idx] = S[i][t];
+            if (a.S_out2) a.S_out2[idx] = S[i][t];
         }
     }
 }
@@ -798,8 +806,8 @@ __global__ __launch_bounds__(256, 2) void frame_output_kernel(ScanArgs a) {
     const int part = (x / a.H) % a.tsplit;
     const int fl = (x / (a.H * a.tsplit)) % a.Fc;
     const int b = x / (a.H * a.tsplit * a.Fc);
-    const int item = (b * a.H + h) * a.Fc + fl;   // workspace item
-    const int f = a.f0 + fl;
+    const int item = (b * a.H + h) * a.wsFc + a.fsub0 + fl;   // workspace item
+    const int f = a.f0 + a.fsub0 + fl;
     const int N = a.N, H = a.H;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = lane & 15, g = lane >> 4;
