@@ -147,10 +147,11 @@ template <> struct IO<float> {
 // 1 KiB blocks with values 0-3 and 4-7 of every lane), so that every 64-lane
 // load or store of it touches one contiguous KiB.
 //   Gm^T   operand of state_scan: rows e, contraction c; Gm^T[e][c] = -alpha G[c][e]
-//          (bf16 mode: hi plane then lo plane; fp32 mode: one fp32 plane)
+//          (one plane: bf16, rounded to nearest even, or fp32)
 //   U^T    accumulator tiles of state_scan: block (e-tile, a-tile) holds, in
 //          lane 16g+r, U[16a_t + 4g + t][16e_t + r] for t = 0..3 (fp32)
-//   S_f    operand of frame_output: rows a, contraction e (planes as Gm)
+//   S_f    operand of frame_output: rows a, contraction e (bf16 mode: the hi
+//          plane, then the lo plane S - hi; fp32 mode: one fp32 plane)
 template <typename T, int D> struct WS {
     static constexpr int KS = (D + 31) / 32;                  // contraction fragments per tile
     static constexpr int RT = D / 16;                         // 16-row tiles
@@ -158,7 +159,7 @@ template <typename T, int D> struct WS {
     static constexpr size_t FRAG = sizeof(T) == 2 ? 1024 : 2048;
     static constexpr size_t OPND = (size_t)RT * KS * FRAG;    // one operand plane
     static constexpr size_t gm_off = 0;
-    static constexpr size_t ut_off = NPL * OPND;
+    static constexpr size_t ut_off = OPND;
     static constexpr size_t sp_off = ut_off + (size_t)RT * RT * 1024;
     static constexpr size_t item_bytes = sp_off + NPL * OPND;
     // byte offset of lane `lane`'s slot in operand fragment (tile, kt), half h (fp32)
@@ -171,7 +172,7 @@ template <typename T, int D> struct WS {
 constexpr size_t ws_item_bytes(int esz, int D) {
     const size_t KS = (size_t)(D + 31) / 32, RT = (size_t)D / 16, NPL = esz == 2 ? 2 : 1;
     const size_t opnd = RT * KS * (esz == 2 ? 1024 : 2048);
-    return 2 * NPL * opnd + RT * RT * 1024;
+    return (1 + NPL) * opnd + RT * RT * 1024;
 }
 static_assert(ws_item_bytes(2, 16) == WS<uint16_t, 16>::item_bytes && ws_item_bytes(2, 128) == WS<uint16_t, 128>::item_bytes &&
                   ws_item_bytes(4, 16) == WS<float, 16>::item_bytes && ws_item_bytes(4, 64) == WS<float, 64>::item_bytes,
@@ -455,7 +456,7 @@ __global__ __launch_bounds__(512, 1) void frame_gram_kernel(ScanArgs a) {
             }
         }
     };
-    // Gm^T = -alpha G^T (hi/lo planes or fp32) and U^T (fp32) of item k, in
+    // Gm^T = -alpha G^T (bf16 or fp32) and U^T (fp32) of item k, in
     // the fragment-major layout state_scan loads
     auto epilogue = [&](int k) {
         using W = WS<T, D>;
@@ -478,11 +479,7 @@ __global__ __launch_bounds__(512, 1) void frame_gram_kernel(ScanArgs a) {
                     const int slot = 16 * (2 * (gb & 1) + (g >> 1)) + r;
                     if constexpr (sizeof(T) == 2) {
                         const uint32_t off = W::gm_off + W::frag_off(j, gb >> 1, 0, slot) + (g & 1) * 8;
-                        const uint32_t h01 = pack_bf16x2(m[0], m[1]), h23 = pack_bf16x2(m[2], m[3]);
-                        const uint32_t l01 = pack_bf16x2(m[0] - bf2f(h01 & 0xffffu), m[1] - bf2f(h01 >> 16));
-                        const uint32_t l23 = pack_bf16x2(m[2] - bf2f(h23 & 0xffffu), m[3] - bf2f(h23 >> 16));
-                        *reinterpret_cast<u32x2*>(wsi + off) = u32x2{h01, h23};
-                        *reinterpret_cast<u32x2*>(wsi + off + W::OPND) = u32x2{l01, l23};
+                        *reinterpret_cast<u32x2*>(wsi + off) = u32x2{pack_bf16x2(m[0], m[1]), pack_bf16x2(m[2], m[3])};
                     } else {
                         const uint32_t off = W::gm_off + W::frag_off(j, gb >> 1, g & 1, slot);
                         *reinterpret_cast<f32x4*>(wsi + off) = m;
@@ -561,7 +558,7 @@ template <typename T, int D> struct StateCfg {
     static constexpr int NPL = sizeof(T) == 2 ? 2 : 1;  // planes (hi, lo) of S in LDS
     // frames of operands in flight: the ring must fit the 6-bit vector-memory
     // counter (63 outstanding loads and stores per wave) or every frame drains it
-    static constexpr int LOADS = KS * 2 + RTW;
+    static constexpr int LOADS = KS + RTW;
     static constexpr int PD = (48 / LOADS) < 4 ? (48 / LOADS) : 4;
     static_assert(PD >= 2, "ring too shallow");
 };
@@ -569,12 +566,15 @@ template <typename T, int D> struct StateCfg {
 // One workgroup owns RTW consecutive 16-row tiles of one (b, h) state (rows
 // [16*RTW*rg, 16*RTW*(rg+1))); wave w owns columns [16w, 16w+16) of them.
 // Rows of S evolve independently, so workgroups never communicate.  Per frame:
-//   acc = alpha*S + U_f ;  acc += S_hi Gm_hi + S_lo Gm_hi + S_hi Gm_lo  (bf16)
+//   acc = alpha*S + U_f ;  acc += S_hi Gm + S_lo Gm  (bf16 Gm, S = S_hi + S_lo)
 //   (fp32 mode: acc += S Gm with fp32 MFMA)
+// Gm is rounded to bf16 once; that relative error (2^-9 of S Gm) is of the
+// same size as the error G already carries from its bf16 operands, and far
+// below the error of U, so a second (lo) plane of Gm would buy nothing.
 // S stays in fp32 registers; its bf16 hi/lo split is double-buffered in LDS
 // as the A operand (one barrier per frame), and the previous frame's planes
 // are copied to the workspace for frame_output while this frame's MFMAs run.
-// Every workgroup of a head reads all of Gm_f (64 KiB as hi/lo planes) each
+// Every workgroup of a head reads all of Gm_f (32 KiB in bf16) each
 // frame; the per-CU rate of those L2 reads, not the MFMAs, bounds this kernel
 // (about 1.5 us per frame at D = 128), so more rows per workgroup do not help.
 // The operands of the next PD frames are in flight in a register ring.
@@ -632,8 +632,7 @@ __global__ __launch_bounds__(4 * D, 1) void state_scan_kernel(ScanArgs a) {  // 
     put_lds(0);
 
     struct Ops {
-        frag bh_[C::KS];          // Gm hi (fp32 mode: Gm) for this wave's 16 columns
-        frag bl_[C::KS];          // Gm lo (bf16 mode only)
+        frag bh_[C::KS];          // Gm for this wave's 16 columns
         f32x4 u[C::RTW];          // U rows of each row tile, accumulator layout
     };
     const size_t item0 = (size_t)bh * a.wsFc + a.fsub0;
@@ -645,9 +644,7 @@ __global__ __launch_bounds__(4 * D, 1) void state_scan_kernel(ScanArgs a) {  // 
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
             if constexpr (sizeof(T) == 2) {
-                const unsigned char* gp = wsi + W::gm_off + W::frag_off(wave, ks, 0, lane);
-                o.bh_[ks] = *reinterpret_cast<const u32x4*>(gp);
-                o.bl_[ks] = *reinterpret_cast<const u32x4*>(gp + W::OPND);
+                o.bh_[ks] = *reinterpret_cast<const u32x4*>(wsi + W::gm_off + W::frag_off(wave, ks, 0, lane));
             } else {
                 const f32x4 lo = *reinterpret_cast<const f32x4*>(wsi + W::gm_off + W::frag_off(wave, ks, 0, lane));
                 const f32x4 hi = *reinterpret_cast<const f32x4*>(wsi + W::gm_off + W::frag_off(wave, ks, 1, lane));
@@ -701,12 +698,9 @@ __global__ __launch_bounds__(4 * D, 1) void state_scan_kernel(ScanArgs a) {  // 
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
             const int c0 = (ks * 32 + 8 * g) % D;
-            frag bhi = o.bh_[ks], blo = o.bl_[ks];
+            frag bhi = o.bh_[ks];
             if constexpr (D < 32) {                    // unwritten upper lanes of the fragment
-                if (!kvalid) {
-                    bhi = io::zero();
-                    blo = io::zero();
-                }
+                if (!kvalid) bhi = io::zero();
             }
 #pragma unroll
             for (int i = 0; i < C::RTW; ++i) {
@@ -725,10 +719,7 @@ __global__ __launch_bounds__(4 * D, 1) void state_scan_kernel(ScanArgs a) {  // 
                 }
                 f32x4& dst = (ks & 1) ? acc2[i] : acc[i];
                 io::mma(dst, ahi, bhi);
-                if constexpr (sizeof(T) == 2) {
-                    io::mma(dst, alo, bhi);
-                    io::mma(dst, ahi, blo);
-                }
+                if constexpr (sizeof(T) == 2) io::mma(dst, alo, bhi);
             }
         }
         if (reload) load_ops(nx, o);

@@ -56,11 +56,14 @@ def desc(B=1, H=2, F=3, N=5, D=16, io=_lib.GDN_BF16, flags=0, eps=1e-6, Dv=None)
 
 
 def test_workspace_size(lib):
-    # per (b, h, frame): G, U and the state planes (12*D*D bytes for D >= 32),
-    # rounded to 256 bytes, then one fp32 carry state per (b, h)
-    d = desc(B=2, H=3, F=5, N=7, D=64)
-    per_frames = 2 * 3 * 5 * 12 * 64 * 64
-    assert lib.gdn_workspace_size(ctypes.byref(d)) == (per_frames + 255) // 256 * 256 + 2 * 3 * 64 * 64 * 4
+    # per (b, h, frame): Gm, U and the state planes for frame_output (bf16:
+    # 2 + 4 + 2*2 bytes per matrix entry; fp32: 4 + 4 + 4), rounded to 256
+    # bytes, then one fp32 carry state per (b, h)
+    for io, per_entry in ((_lib.GDN_BF16, 10), (_lib.GDN_F32, 12)):
+        d = desc(B=2, H=3, F=5, N=7, D=64, io=io)
+        per_frames = 2 * 3 * 5 * per_entry * 64 * 64
+        assert lib.gdn_workspace_size(ctypes.byref(d)) == \
+            (per_frames + 255) // 256 * 256 + 2 * 3 * 64 * 64 * 4
     assert lib.gdn_workspace_size(ctypes.byref(desc(D=48))) == 0
     assert lib.gdn_workspace_size(None) == 0
     assert lib.gdn_workspace_size(ctypes.byref(desc(F=0))) == 0
