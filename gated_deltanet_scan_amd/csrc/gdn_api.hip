@@ -225,7 +225,7 @@ gdn_status launch_all(const Plan& p, ScanArgs a, hipStream_t stream, int cus, fl
             ProfScope ps(K_GRAM, stream);
             // persistent: one workgroup per CU, each streaming its share of the items
             const int grid = items < cus ? items : (cus > 0 ? cus : 256);
-            hipLaunchKernelGGL((gdn::frame_gram_kernel<T, D>), dim3(grid), dim3(512), 0, stream, a);
+            hipLaunchKernelGGL((gdn::frame_gram_kernel<T, D>), dim3(grid), dim3(1024), 0, stream, a);
         }
         if (hipGetLastError() != hipSuccess) return GDN_ERR_LAUNCH;
 

@@ -84,6 +84,12 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
 __device__ __forceinline__ u32x4 bload16(rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
+// Streams read exactly once (K, V, Q): the non-temporal policy bit keeps them
+// from displacing reused lines; measured about 12% faster for this pattern.
+constexpr int kNonTemporal = 2;
+__device__ __forceinline__ u32x4 bload16_nt(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNonTemporal);
+}
 __device__ __forceinline__ float bload4f(rsrc_t r, uint32_t off) {
     return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
@@ -215,29 +221,37 @@ __device__ __forceinline__ int xcd_remap(int id, int per, int total) {
 // ================================================================== frame_gram
 template <typename T, int D> struct GramCfg {
     static constexpr int SZ = IO<T>::bytes;
-    static constexpr int SL = D / 8;                                 // 8-value slices per token
-    static constexpr int TS0 = SZ == 2 ? 64 : 32;
-    static constexpr int TS = TS0 > 2048 / D ? TS0 : 2048 / D;      // tokens per LDS stage
-    static constexpr int TPT = TS * SL / 256;                        // tokens per producer thread
-    static constexpr int ROWB = TS * SZ;                             // bytes per LDS row
-    static constexpr int CHUNKS = ROWB / 16;                         // 16-byte chunks per row
-    static constexpr int ARR = D * ROWB;                             // bytes per transposed array
-    static constexpr int BUF = 3 * ARR;                              // one stage: K, wK, uV
-    static constexpr int LDS = 2 * BUF;                              // double buffer
-    static constexpr int RB = D / 16;                                // 16-row blocks per matrix
-    static constexpr int NRW = (2 * RB + 3) / 4;                     // row blocks per MFMA wave
-    static constexpr int KST = TS / 32;                              // 32-token steps per stage
-    static constexpr int TPC = 16 / SZ;                              // tokens per 16-byte chunk
-    static_assert(TPT >= 1 && TPT * SZ <= 16 && TPC % TPT == 0, "stage shape");
-    static_assert(CHUNKS >= 8 && (CHUNKS & (CHUNKS - 1)) == 0, "swizzle needs >= 8 chunks");
+    static constexpr int FPT = 16 / SZ;                 // features per producer thread: one
+                                                        // 16-byte load per token
+    static constexpr int SL = D / FPT;                  // producer lanes sharing one token
+    static constexpr int NP = 512;                      // producer threads (waves 8-15)
+    static constexpr int TPT = 2;                       // tokens per producer thread: one
+                                                        // 2-token transposed LDS write per feature
+    static constexpr int TS = NP * TPT / SL;            // tokens per stage
+    static constexpr int ROWB = TS * SZ;                // bytes per LDS row (one feature)
+    static constexpr int CHUNKS = ROWB / 16;            // 16-byte chunks per row
+    static constexpr int ARR = D * ROWB;                // one transposed array: 16 KiB
+    static constexpr int BUF = 3 * ARR;                 // one stage: rho K, V, beta rho K
+    static constexpr int LDS = 2 * BUF;                 // double buffer
+    static constexpr int RB = D / 16;                   // 16-row blocks per matrix
+    static constexpr int TR = RB >= 2 ? RB / 2 : 1;     // row blocks per consumer tile
+    static constexpr int TC = RB >= 2 ? RB / 2 : 1;     // column blocks per consumer tile
+    static constexpr int NCT = RB / TC;                 // column tiles
+    static constexpr int NT = (2 * RB / TR) * NCT;      // tiles = busy consumer waves
+    static constexpr int KST = TS / 32;                 // 32-token steps per stage
+    static_assert(ARR == 16384 && NT <= 8 && TS % 32 == 0, "stage shape");
+    static_assert(CHUNKS >= 8 && CHUNKS % 8 == 0, "the swizzle permutes groups of 8 chunks");
+    static_assert(SL >= 2 && SL <= 32, "token lanes");
 };
 
-// Byte offset of 16-byte chunk c of LDS row `row`.  The XOR swizzle spreads
-// both the transposing writes (rows 8 apart) and the fragment reads (16
-// consecutive rows) over the banks.
+// Byte offset of 16-byte chunk c of LDS row `row`.  The XOR swizzle was
+// chosen by measuring candidates on gfx950: with it the fragment reads (16
+// consecutive rows, four chunks) run conflict-free at one KiB per 5 clocks,
+// and the transposing 8-byte writes at the 8 clocks per wave that every
+// candidate needed; (row ^ row >> 3) made the reads 2-way.
 template <int ROWB>
 __device__ __forceinline__ int lds_chunk(int row, int c) {
-    return row * ROWB + ((c ^ ((row ^ (row >> 3)) & 7)) << 4);
+    return row * ROWB + ((c ^ ((row ^ (row >> 4)) & 7)) << 4);
 }
 
 // Fragment (8 contraction values) of LDS row `row`, tokens 8g..8g+7 of 32-token step ks.
@@ -254,32 +268,59 @@ __device__ __forceinline__ typename IO<T>::frag lds_frag(const unsigned char* ba
     }
 }
 
-// 16-bit storage bits of element e of a fragment (bf16) / 32-bit (fp32).
-template <typename T>
-__device__ __forceinline__ uint32_t elem_bits(const typename IO<T>::frag& x, int e) {
-    if constexpr (sizeof(T) == 2) {
+// The 16 bytes of consecutive features of one token a producer thread loads.
+template <typename T> struct Quad;
+template <> struct Quad<uint16_t> {
+    using type = u32x4;
+    __device__ static __forceinline__ type load(rsrc_t r, uint32_t off) { return bload16_nt(r, off); }
+    __device__ static __forceinline__ float get(const type& x, int e) {
+        const uint32_t w = x[e >> 1];
+        return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+    }
+    __device__ static __forceinline__ uint32_t bits(const type& x, int e) {
         return (e & 1) ? (x[e >> 1] >> 16) : (x[e >> 1] & 0xffffu);
+    }
+};
+template <> struct Quad<float> {
+    using type = u32x4;
+    __device__ static __forceinline__ type load(rsrc_t r, uint32_t off) { return bload16_nt(r, off); }
+    __device__ static __forceinline__ float get(const type& x, int e) { return __uint_as_float(x[e]); }
+    __device__ static __forceinline__ uint32_t bits(const type& x, int e) { return x[e]; }
+};
+
+// Sum over aligned groups of L lanes (L <= 32); the step across the two rows
+// of a 32-lane group (fp32 at D = 128) uses ds_swizzle (lane ^ 16).
+template <int L>
+__device__ __forceinline__ float lane_group_sum(float x) {
+    if constexpr (L <= 16) {
+        return group_sum<L>(x);
     } else {
-        return __float_as_uint(x[e]);
+        static_assert(L == 32, "group of 32 lanes at most");
+        x = group_sum<16>(x);
+        return x + __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
     }
 }
 
-// Persistent workgroups of 8 waves; workgroup w takes the (b, h, f) items
+// Persistent workgroups of 16 waves; workgroup w takes the (b, h, f) items
 // w, w + grid, w + 2*grid, ... in frame-major order (head fastest), so the
 // heads of one frame together read each contiguous token row of [B,F,N,H,D].
-// Waves 4-7 produce: they stream K_f, V_f and beta through registers (four
-// stages of 64 tokens in flight, continuing across items), reduce the key
-// norms across the lanes of each token, scale, and write the stage transposed
-// ([feature][token]) into one half of a double-buffered LDS.  Waves 0-3
-// consume the other half with MFMA:
+// Waves 8-15 produce: each thread streams 16 bytes of features of two tokens
+// of K_f and V_f (and their betas) through registers, four stages ahead, reduces the
+// key norms over the lanes of each token, scales, and writes the stage
+// transposed ([feature][token]) into one half of a double-buffered LDS.
+// Waves 0-7 consume the other half with MFMA, one 64x64 tile of the stacked
+// [G ; U] each:
 //     G += (rho K)^T (beta rho K),    U += V^T (beta rho K)
 // so both products share the scaled B operand and V is only transposed; after
-// an item's last stage they write Gm = -alpha G and U to the workspace.
+// an item's last stage they write Gm = -alpha G and U to the workspace.  Two
+// waves of each role per SIMD let one issue while the other waits: a single
+// wave issues VALU work far below the SIMD's rate.
 template <typename T, int D>
-__global__ __launch_bounds__(512, 1) void frame_gram_kernel(ScanArgs a) {
+__global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
     using C = GramCfg<T, D>;
     using io = IO<T>;
     using frag = typename io::frag;
+    using Q = Quad<T>;
     __shared__ __attribute__((aligned(16))) unsigned char smem[C::LDS];
 
     const int N = a.N, H = a.H;
@@ -287,9 +328,10 @@ __global__ __launch_bounds__(512, 1) void frame_gram_kernel(ScanArgs a) {
     const int nmine = (int)blockIdx.x < items ? (items - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
     const int nst = (N + C::TS - 1) / C::TS;
     const int total = nmine * nst;                  // stages of this workgroup
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches and offsets
     const int r = lane & 15, g = lane >> 4;
-    const bool producer = wave >= 4;
+    const bool producer = wave >= 8;
 
     struct Item {
         int b, h, f, ws;                            // batch, head, frame, workspace item
@@ -306,20 +348,33 @@ __global__ __launch_bounds__(512, 1) void frame_gram_kernel(ScanArgs a) {
     };
 
     // ---- producer state (32-bit offsets: the host bounds a frame below 2 GiB)
-    const int ptid = tid & 255;
-    const int s = ptid % C::SL;                     // 8-feature slice
-    const int tl = ptid / C::SL;                    // token group: tokens tl*TPT + j
+    const int ptid = tid & (C::NP - 1);
+    const int s = ptid % C::SL;                     // features s*FPT .. s*FPT+3
+    const int tl = ptid / C::SL;                    // tokens tl*TPT .. tl*TPT+TPT-1
     const size_t rowstride = (size_t)H * D;         // elements between tokens
     const uint32_t row_bytes = (uint32_t)(H * D * C::SZ);
-    const uint32_t kv_off0 = (uint32_t)(tl * C::TPT) * row_bytes + (uint32_t)(s * 8 * C::SZ);
-    const uint32_t b_off0 = (uint32_t)(tl * C::TPT * H * 4);
+    const uint32_t kv_off0 = (uint32_t)(tl * C::TPT) * row_bytes + (uint32_t)(s * C::FPT * C::SZ);
+    // betas: each producer wave covers TPW consecutive tokens of a stage; lane l
+    // loads the beta of its (l % TPW)-th token and the lanes of each token pick
+    // theirs up with ds_bpermute, one load instead of one per lane and token
+    constexpr int TPW = 64 / C::SL * C::TPT;
+    static_assert(TPW <= 64, "a wave's tokens must fit its lanes");
+    const uint32_t b_off0 = (uint32_t)(((ptid >> 6) * TPW + lane % TPW) * H * 4);
+    const int b_src0 = 4 * (((ptid & 63) / C::SL) * C::TPT);        // ds_bpermute byte address
     const uint32_t beta_bytes = N > 0 ? (uint32_t)(((N - 1) * H + 1) * 4) : 0u;
     const float inv_n = N > 0 ? 1.0f / (float)N : 0.0f;
     const float inv_eps = 1.0f / a.eps;
+    // this thread's LDS write offsets (feature e, its TPT tokens), fixed for every stage
+    int woff[C::FPT];
+#pragma unroll
+    for (int e = 0; e < C::FPT; ++e) {
+        const int t0b = tl * C::TPT * C::SZ;        // byte position of the first token in a row
+        woff[e] = lds_chunk<C::ROWB>(s * C::FPT + e, t0b >> 4) + (t0b & 15);
+    }
 
     struct Stage {
-        frag k[C::TPT], v[C::TPT];
-        float bt[C::TPT];
+        typename Q::type k[C::TPT], v[C::TPT];
+        float bt;                                   // beta of this lane's token (see b_off0)
     };
     // Stage gs of this workgroup's stream; stages past the end read rows past
     // the last token, which the buffer range check returns as zeros.
@@ -340,10 +395,10 @@ __global__ __launch_bounds__(512, 1) void frame_gram_kernel(ScanArgs a) {
         const uint32_t bo = b_off0 + (uint32_t)(st * C::TS * H * 4);
 #pragma unroll
         for (int j = 0; j < C::TPT; ++j) {
-            R.k[j] = io::bload(rk, kvo + (uint32_t)j * row_bytes);
-            R.v[j] = io::bload(rv, kvo + (uint32_t)j * row_bytes);
-            R.bt[j] = bload4f(rb, bo + (uint32_t)(j * H * 4));
+            R.k[j] = Q::load(rk, kvo + (uint32_t)j * row_bytes);
+            R.v[j] = Q::load(rv, kvo + (uint32_t)j * row_bytes);
         }
+        R.bt = bload4f(rb, bo);
     };
     // Norms, scales and the transposed LDS write of stage gs.
     auto write_stage = [&](int gs, const Stage& R, unsigned char* buf) {
@@ -353,12 +408,12 @@ __global__ __launch_bounds__(512, 1) void frame_gram_kernel(ScanArgs a) {
         for (int j = 0; j < C::TPT; ++j) {
             float ss = 0.0f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float kx = io::get(R.k[j], e);
+            for (int e = 0; e < C::FPT; ++e) {
+                const float kx = Q::get(R.k[j], e);
                 ss = fmaf(kx, kx, ss);
             }
-            ss = group_sum<C::SL>(ss);
-            float bt = R.bt[j];
+            ss = lane_group_sum<C::SL>(ss);
+            float bt = __int_as_float(__builtin_amdgcn_ds_bpermute(b_src0 + 4 * j, __float_as_int(R.bt)));
             if (a.logits) bt = (st * C::TS + tl * C::TPT + j < N) ? sigmoid_f(bt) * inv_n : 0.0f;
             rho[j] = fminf(__builtin_amdgcn_rsqf(ss), inv_eps);   // 1 / max(|k|, eps)
             xs[j] = bt * rho[j];
@@ -366,73 +421,30 @@ __global__ __launch_bounds__(512, 1) void frame_gram_kernel(ScanArgs a) {
         unsigned char* sKH = buf;                   // rho k         (A of G)
         unsigned char* sVT = buf + C::ARR;          // v             (A of U)
         unsigned char* sXB = buf + 2 * C::ARR;      // beta rho k    (B of both)
-        const int t0 = tl * C::TPT;
-        const int cbase = t0 / C::TPC, within = (t0 % C::TPC) * C::SZ;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int off = lds_chunk<C::ROWB>(s * 8 + e, cbase) + within;
-            if constexpr (sizeof(T) == 2) {
-                if constexpr (C::TPT == 1) {
-                    const float kx = io::get(R.k[0], e);
-                    *reinterpret_cast<uint16_t*>(sKH + off) = f2bf(rho[0] * kx);
-                    *reinterpret_cast<uint16_t*>(sXB + off) = f2bf(xs[0] * kx);
-                    *reinterpret_cast<uint16_t*>(sVT + off) = (uint16_t)elem_bits<T>(R.v[0], e);
-                } else {
-                    uint32_t kh[C::TPT / 2], xb[C::TPT / 2], vt[C::TPT / 2];
-#pragma unroll
-                    for (int j = 0; j < C::TPT; j += 2) {
-                        const float k0 = io::get(R.k[j], e), k1 = io::get(R.k[j + 1], e);
-                        kh[j / 2] = pack_bf16x2(rho[j] * k0, rho[j + 1] * k1);
-                        xb[j / 2] = pack_bf16x2(xs[j] * k0, xs[j + 1] * k1);
-                        vt[j / 2] = elem_bits<T>(R.v[j], e) | (elem_bits<T>(R.v[j + 1], e) << 16);
-                    }
-                    if constexpr (C::TPT == 8) {
-                        *reinterpret_cast<u32x4*>(sKH + off) = u32x4{kh[0], kh[1], kh[2], kh[3]};
-                        *reinterpret_cast<u32x4*>(sXB + off) = u32x4{xb[0], xb[1], xb[2], xb[3]};
-                        *reinterpret_cast<u32x4*>(sVT + off) = u32x4{vt[0], vt[1], vt[2], vt[3]};
-                    } else if constexpr (C::TPT == 4) {
-                        *reinterpret_cast<u32x2*>(sKH + off) = u32x2{kh[0], kh[1]};
-                        *reinterpret_cast<u32x2*>(sXB + off) = u32x2{xb[0], xb[1]};
-                        *reinterpret_cast<u32x2*>(sVT + off) = u32x2{vt[0], vt[1]};
-                    } else {
-                        *reinterpret_cast<uint32_t*>(sKH + off) = kh[0];
-                        *reinterpret_cast<uint32_t*>(sXB + off) = xb[0];
-                        *reinterpret_cast<uint32_t*>(sVT + off) = vt[0];
-                    }
-                }
+        for (int e = 0; e < C::FPT; ++e) {
+            const float k0 = Q::get(R.k[0], e), k1 = Q::get(R.k[1], e);
+            if constexpr (sizeof(T) == 2) {         // the two tokens' bf16 values in one dword
+                *reinterpret_cast<uint32_t*>(sKH + woff[e]) = pack_bf16x2(rho[0] * k0, rho[1] * k1);
+                *reinterpret_cast<uint32_t*>(sXB + woff[e]) = pack_bf16x2(xs[0] * k0, xs[1] * k1);
+                *reinterpret_cast<uint32_t*>(sVT + woff[e]) = Q::bits(R.v[0], e) | (Q::bits(R.v[1], e) << 16);
             } else {
-                float kh[C::TPT], xb[C::TPT], vt[C::TPT];
-#pragma unroll
-                for (int j = 0; j < C::TPT; ++j) {
-                    const float kx = R.k[j][e];
-                    kh[j] = rho[j] * kx;
-                    xb[j] = xs[j] * kx;
-                    vt[j] = R.v[j][e];
-                }
-                if constexpr (C::TPT == 4) {
-                    *reinterpret_cast<f32x4*>(sKH + off) = f32x4{kh[0], kh[1], kh[2], kh[3]};
-                    *reinterpret_cast<f32x4*>(sXB + off) = f32x4{xb[0], xb[1], xb[2], xb[3]};
-                    *reinterpret_cast<f32x4*>(sVT + off) = f32x4{vt[0], vt[1], vt[2], vt[3]};
-                } else if constexpr (C::TPT == 2) {
-                    *reinterpret_cast<f32x2*>(sKH + off) = f32x2{kh[0], kh[1]};
-                    *reinterpret_cast<f32x2*>(sXB + off) = f32x2{xb[0], xb[1]};
-                    *reinterpret_cast<f32x2*>(sVT + off) = f32x2{vt[0], vt[1]};
-                } else {
-                    *reinterpret_cast<float*>(sKH + off) = kh[0];
-                    *reinterpret_cast<float*>(sXB + off) = xb[0];
-                    *reinterpret_cast<float*>(sVT + off) = vt[0];
-                }
+                *reinterpret_cast<f32x2*>(sKH + woff[e]) = f32x2{rho[0] * k0, rho[1] * k1};
+                *reinterpret_cast<f32x2*>(sXB + woff[e]) = f32x2{xs[0] * k0, xs[1] * k1};
+                *reinterpret_cast<f32x2*>(sVT + woff[e]) = f32x2{Q::get(R.v[0], e), Q::get(R.v[1], e)};
             }
         }
     };
 
-    // ---- consumer state
-    f32x4 acc[C::NRW][C::RB];
+    // ---- consumer state: wave `wave` owns row blocks rt*TR.. and column blocks ct*TC..
+    const bool cbusy = wave < C::NT;
+    const int rt = wave / C::NCT, ct = wave % C::NCT;
+    f32x4 acc[C::TR][C::TC];
     auto zero_acc = [&]() {
 #pragma unroll
-        for (int i = 0; i < C::NRW; ++i)
+        for (int i = 0; i < C::TR; ++i)
 #pragma unroll
-            for (int j = 0; j < C::RB; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
+            for (int j = 0; j < C::TC; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
     };
     auto mfma_stage = [&](const unsigned char* buf) {
         const unsigned char* sKH = buf;
@@ -440,61 +452,64 @@ __global__ __launch_bounds__(512, 1) void frame_gram_kernel(ScanArgs a) {
         const unsigned char* sXB = buf + 2 * C::ARR;
 #pragma unroll 1
         for (int ks = 0; ks < C::KST; ++ks) {
-            frag bk[C::RB];
+            frag A[C::TR], Bf[C::TC];
 #pragma unroll
-            for (int j = 0; j < C::RB; ++j) bk[j] = lds_frag<T, C::ROWB>(sXB, j * 16 + r, ks, g);
-#pragma unroll
-            for (int i = 0; i < C::NRW; ++i) {
-                const int gb = wave + 4 * i;        // row block over [G rows ; U rows]
-                if (gb < 2 * C::RB) {
-                    const unsigned char* src = gb < C::RB ? sKH : sVT;
-                    const int rowb = gb < C::RB ? gb : gb - C::RB;
-                    const frag ak = lds_frag<T, C::ROWB>(src, rowb * 16 + r, ks, g);
-#pragma unroll
-                    for (int j = 0; j < C::RB; ++j) io::mma(acc[i][j], ak, bk[j]);
-                }
+            for (int i = 0; i < C::TR; ++i) {
+                const int gb = rt * C::TR + i;      // row block over [G rows ; U rows]
+                A[i] = lds_frag<T, C::ROWB>(gb < C::RB ? sKH : sVT, (gb % C::RB) * 16 + r, ks, g);
             }
+#pragma unroll
+            for (int j = 0; j < C::TC; ++j) Bf[j] = lds_frag<T, C::ROWB>(sXB, (ct * C::TC + j) * 16 + r, ks, g);
+#pragma unroll
+            for (int i = 0; i < C::TR; ++i)
+#pragma unroll
+                for (int j = 0; j < C::TC; ++j) io::mma(acc[i][j], A[i], Bf[j]);
         }
     };
-    // Gm^T = -alpha G^T (bf16 or fp32) and U^T (fp32) of item k, in
-    // the fragment-major layout state_scan loads
+    // Gm^T = -alpha G^T (bf16 or fp32) and U^T (fp32) of item k, in the
+    // fragment-major layout state_scan loads.  Stores go through a buffer
+    // resource: each block's offset splits into a compile-time part (scalar
+    // soffset) and one per-lane part, so no per-block addresses stay live.
+    using W = WS<T, D>;
+    // per-lane parts: Gm slot 16*(2*(gb%2) + g/2) + r holding values 4*(g%2)..
+    const uint32_t gm_lane = sizeof(T) == 2 ? (uint32_t)(256 * (g >> 1) + 16 * r + 8 * (g & 1))
+                                            : (uint32_t)(1024 * (g & 1) + 256 * (g >> 1) + 16 * r);
+    const uint32_t u_lane = (uint32_t)(lane * 16);
     auto epilogue = [&](int k) {
-        using W = WS<T, D>;
         const Item it = item_of(k);
         float al = a.alpha[((size_t)it.b * a.F + it.f) * H + it.h];
         if (a.logits) al = sigmoid_f(al);
-        unsigned char* wsi = a.ws + (size_t)it.ws * W::item_bytes;
+        const rsrc_t rw = make_rsrc(a.ws + (size_t)it.ws * W::item_bytes, (uint32_t)W::item_bytes);
 #pragma unroll
-        for (int i = 0; i < C::NRW; ++i) {
-            const int gb = wave + 4 * i;
-            if (gb >= 2 * C::RB) continue;
+        for (int i = 0; i < C::TR; ++i) {
+            const int gb = rt * C::TR + i;
 #pragma unroll
-            for (int j = 0; j < C::RB; ++j) {
+            for (int j = 0; j < C::TC; ++j) {
+                const int jb = ct * C::TC + j;
                 const f32x4 x = acc[i][j];
                 if (gb < C::RB) {
-                    // lane (r, g) holds G[16gb + 4g + t][16j + r] = Gm^T[e][c] with e = 16j + r:
-                    // fragment (e-tile j, kt = gb/2), lane slot 16*g' + r with
-                    // g' = 2*(gb%2) + g/2, values 4*(g%2) + t
+                    // lane (r, g) holds G[16gb + 4g + t][16jb + r] = Gm^T[e][c] with e = 16jb + r:
+                    // fragment (e-tile jb, kt = gb/2), lane slot 16*(2*(gb%2) + g/2) + r,
+                    // values 4*(g%2) + t
                     const f32x4 m = x * (-al);
-                    const int slot = 16 * (2 * (gb & 1) + (g >> 1)) + r;
-                    if constexpr (sizeof(T) == 2) {
-                        const uint32_t off = W::gm_off + W::frag_off(j, gb >> 1, 0, slot) + (g & 1) * 8;
-                        *reinterpret_cast<u32x2*>(wsi + off) = u32x2{pack_bf16x2(m[0], m[1]), pack_bf16x2(m[2], m[3])};
-                    } else {
-                        const uint32_t off = W::gm_off + W::frag_off(j, gb >> 1, g & 1, slot);
-                        *reinterpret_cast<f32x4*>(wsi + off) = m;
-                    }
+                    const uint32_t blk = (uint32_t)(W::gm_off + (size_t)(jb * W::KS + (gb >> 1)) * W::FRAG +
+                                                    512 * (gb & 1));
+                    if constexpr (sizeof(T) == 2)
+                        __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf16x2(m[0], m[1]), pack_bf16x2(m[2], m[3])},
+                                                              rw, gm_lane, blk, 0);
+                    else
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, m), rw, gm_lane, blk, 0);
                 } else {
-                    // lane (r, g) holds U[16ga + 4g + t][16j + r]: block (j, ga), slot 16g + r
-                    const int ga = gb - C::RB;
-                    *reinterpret_cast<f32x4*>(wsi + W::ut_off + (size_t)(j * W::RT + ga) * 1024 + lane * 16) = x;
+                    // lane (r, g) holds U[16ga + 4g + t][16jb + r]: block (jb, ga), slot 16g + r
+                    const uint32_t blk = (uint32_t)(W::ut_off + (size_t)(jb * W::RT + (gb - C::RB)) * 1024);
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), rw, u_lane, blk, 0);
                 }
             }
         }
     };
 
     if (nst == 0) {                                  // no tokens: G = U = 0
-        if (!producer) {
+        if (!producer && cbusy) {
             zero_acc();
             for (int k = 0; k < nmine; ++k) epilogue(k);
         }
@@ -535,7 +550,7 @@ __global__ __launch_bounds__(512, 1) void frame_gram_kernel(ScanArgs a) {
     }
     zero_acc();
     for (int p = 0; p < 4 * nquad; ++p) {
-        if (p >= 1 && p <= total) {
+        if (cbusy && p >= 1 && p <= total) {
             mfma_stage((p & 1) ? buf0 : buf1);      // stage p-1 sits in buffer (p-1)&1
             if ((p - 1) % nst == nst - 1) {
                 epilogue((p - 1) / nst);
@@ -828,7 +843,7 @@ __global__ __launch_bounds__(256, 2) void frame_output_kernel(ScanArgs a) {
     auto load_blk = [&](int blk, QStage& R) {
         const uint32_t base = (uint32_t)(blk * C::BT + lr) * row_bytes + (uint32_t)(lc * 16);
 #pragma unroll
-        for (int i = 0; i < C::NLD; ++i) R.v[i] = bload16(rq, base + (uint32_t)(i * C::RPP) * row_bytes);
+        for (int i = 0; i < C::NLD; ++i) R.v[i] = bload16_nt(rq, base + (uint32_t)(i * C::RPP) * row_bytes);
     };
     auto put_blk = [&](const QStage& R, unsigned char* buf) {
 #pragma unroll
