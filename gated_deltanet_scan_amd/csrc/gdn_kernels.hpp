@@ -354,13 +354,9 @@ __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
     const size_t rowstride = (size_t)H * D;         // elements between tokens
     const uint32_t row_bytes = (uint32_t)(H * D * C::SZ);
     const uint32_t kv_off0 = (uint32_t)(tl * C::TPT) * row_bytes + (uint32_t)(s * C::FPT * C::SZ);
-    // betas: each producer wave covers TPW consecutive tokens of a stage; lane l
-    // loads the beta of its (l % TPW)-th token and the lanes of each token pick
-    // theirs up with ds_bpermute, one load instead of one per lane and token
-    constexpr int TPW = 64 / C::SL * C::TPT;
-    static_assert(TPW <= 64, "a wave's tokens must fit its lanes");
-    const uint32_t b_off0 = (uint32_t)(((ptid >> 6) * TPW + lane % TPW) * H * 4);
-    const int b_src0 = 4 * (((ptid & 63) / C::SL) * C::TPT);        // ds_bpermute byte address
+    // betas of this thread's tokens (the lanes of a token load the same value:
+    // an exchange through ds_bpermute instead waited on LDS latency)
+    const uint32_t b_off0 = (uint32_t)(tl * C::TPT * H * 4);
     const uint32_t beta_bytes = N > 0 ? (uint32_t)(((N - 1) * H + 1) * 4) : 0u;
     const float inv_n = N > 0 ? 1.0f / (float)N : 0.0f;
     const float inv_eps = 1.0f / a.eps;
@@ -374,35 +370,43 @@ __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
 
     struct Stage {
         typename Q::type k[C::TPT], v[C::TPT];
-        float bt;                                   // beta of this lane's token (see b_off0)
+        float bt[C::TPT];
     };
-    // Stage gs of this workgroup's stream; stages past the end read rows past
-    // the last token, which the buffer range check returns as zeros.
-    auto load_stage = [&](int gs, Stage& R) {
-        int kk = gs / (nst > 0 ? nst : 1), st = gs - kk * nst;
-        if (kk >= nmine) {
-            kk = nmine - 1;
-            st = nst;
-        }
+    // The producers' load stream walks this workgroup's stages in order, one
+    // per call; the item's buffer resources are rebuilt only when an item
+    // ends, so the per-stage cost is the loads and one offset add.  Stages past
+    // the end stay on the last item past its last token: the buffer range
+    // check returns zeros for them.
+    struct Loader {
+        rsrc_t rk, rv, rb;
+        uint32_t kvo, bo;                           // offsets of the next stage
+        int kk, st;                                 // its item and stage within the item
+    };
+    auto loader_item = [&](Loader& L, int kk) {
         const Item it = item_of(kk);
         const size_t tok0 = ((size_t)it.b * a.F + it.f) * (size_t)N;
-        const rsrc_t rk = make_rsrc(static_cast<const T*>(a.k) + tok0 * rowstride + (size_t)it.h * D,
-                                    a.tok_bytes);
-        const rsrc_t rv = make_rsrc(static_cast<const T*>(a.v) + tok0 * rowstride + (size_t)it.h * D,
-                                    a.tok_bytes);
-        const rsrc_t rb = make_rsrc(a.beta + tok0 * H + it.h, beta_bytes);
-        const uint32_t kvo = kv_off0 + (uint32_t)(st * C::TS) * row_bytes;
-        const uint32_t bo = b_off0 + (uint32_t)(st * C::TS * H * 4);
+        L.rk = make_rsrc(static_cast<const T*>(a.k) + tok0 * rowstride + (size_t)it.h * D, a.tok_bytes);
+        L.rv = make_rsrc(static_cast<const T*>(a.v) + tok0 * rowstride + (size_t)it.h * D, a.tok_bytes);
+        L.rb = make_rsrc(a.beta + tok0 * H + it.h, beta_bytes);
+        L.kvo = kv_off0;
+        L.bo = b_off0;
+        L.kk = kk;
+        L.st = 0;
+    };
+    auto load_stage = [&](Loader& L, Stage& R) {
 #pragma unroll
         for (int j = 0; j < C::TPT; ++j) {
-            R.k[j] = Q::load(rk, kvo + (uint32_t)j * row_bytes);
-            R.v[j] = Q::load(rv, kvo + (uint32_t)j * row_bytes);
+            R.k[j] = Q::load(L.rk, L.kvo + (uint32_t)j * row_bytes);
+            R.v[j] = Q::load(L.rv, L.kvo + (uint32_t)j * row_bytes);
         }
-        R.bt = bload4f(rb, bo);
+#pragma unroll
+        for (int j = 0; j < C::TPT; ++j) R.bt[j] = bload4f(L.rb, L.bo + (uint32_t)(j * H * 4));
+        L.kvo += (uint32_t)C::TS * row_bytes;
+        L.bo += (uint32_t)(C::TS * H * 4);
+        if (++L.st == nst && L.kk + 1 < nmine) loader_item(L, L.kk + 1);
     };
     // Norms, scales and the transposed LDS write of stage gs.
     auto write_stage = [&](int gs, const Stage& R, unsigned char* buf) {
-        const int st = gs % nst;
         float rho[C::TPT], xs[C::TPT];
 #pragma unroll
         for (int j = 0; j < C::TPT; ++j) {
@@ -413,8 +417,8 @@ __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
                 ss = fmaf(kx, kx, ss);
             }
             ss = lane_group_sum<C::SL>(ss);
-            float bt = __int_as_float(__builtin_amdgcn_ds_bpermute(b_src0 + 4 * j, __float_as_int(R.bt)));
-            if (a.logits) bt = (st * C::TS + tl * C::TPT + j < N) ? sigmoid_f(bt) * inv_n : 0.0f;
+            float bt = R.bt[j];
+            if (a.logits) bt = ((gs % nst) * C::TS + tl * C::TPT + j < N) ? sigmoid_f(bt) * inv_n : 0.0f;
             rho[j] = fminf(__builtin_amdgcn_rsqf(ss), inv_eps);   // 1 / max(|k|, eps)
             xs[j] = bt * rho[j];
         }
@@ -526,24 +530,32 @@ __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
     unsigned char* const buf1 = smem + C::BUF;
     const int nquad = (total + 1 + 3) / 4;          // periods 0..total, in groups of 4
     if (producer) {
+        // The fences keep the prologue's loads in stage order: were stage 0
+        // issued last, its wait at the loop head would drain the whole ring.
         Stage R0, R1, R2, R3;
-        load_stage(0, R0);
-        load_stage(1, R1);
-        load_stage(2, R2);
-        load_stage(3, R3);
+        Loader L;
+        loader_item(L, 0);
+        load_stage(L, R0);
+        __builtin_amdgcn_sched_barrier(0);
+        load_stage(L, R1);
+        __builtin_amdgcn_sched_barrier(0);
+        load_stage(L, R2);
+        __builtin_amdgcn_sched_barrier(0);
+        load_stage(L, R3);
+        __builtin_amdgcn_sched_barrier(0);
         for (int q = 0; q < nquad; ++q) {
             const int p = 4 * q;
             if (p < total) write_stage(p, R0, buf0);
-            load_stage(p + 4, R0);
+            load_stage(L, R0);
             __syncthreads();
             if (p + 1 < total) write_stage(p + 1, R1, buf1);
-            load_stage(p + 5, R1);
+            load_stage(L, R1);
             __syncthreads();
             if (p + 2 < total) write_stage(p + 2, R2, buf0);
-            load_stage(p + 6, R2);
+            load_stage(L, R2);
             __syncthreads();
             if (p + 3 < total) write_stage(p + 3, R3, buf1);
-            load_stage(p + 7, R3);
+            load_stage(L, R3);
             __syncthreads();
         }
         return;
