@@ -87,6 +87,11 @@ __device__ __forceinline__ u32x4 bload16(rsrc_t r, uint32_t off) {
 // Streams read exactly once (K, V, Q): the non-temporal policy bit keeps them
 // from displacing reused lines; measured about 12% faster for this pattern.
 constexpr int kNonTemporal = 2;
+// Stores of the recurrence's per-frame state planes: non-temporal with device
+// scope (nt | sc1).  With the default policy their write-back backed up the
+// shared vector-memory counter and stalled the next frames' operand loads
+// once about half the frames were written (state_scan 124 -> 91 us).
+constexpr int kStreamStore = 2 | 16;
 __device__ __forceinline__ u32x4 bload16_nt(rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNonTemporal);
 }
@@ -154,8 +159,9 @@ template <> struct IO<float> {
 // load or store of it touches one contiguous KiB.
 //   Gm^T   operand of state_scan: rows e, contraction c; Gm^T[e][c] = -alpha G[c][e]
 //          (one plane: bf16, rounded to nearest even, or fp32)
-//   U^T    accumulator tiles of state_scan: block (e-tile, a-tile) holds, in
-//          lane 16g+r, U[16a_t + 4g + t][16e_t + r] for t = 0..3 (fp32)
+//   U      tiles in the state's register layout in state_scan: block (e-tile,
+//          a-tile) holds, in lane 16g+r, U[16a_t + r][16e_t + 4g + t] for
+//          t = 0..3 (fp32)
 //   S_f    operand of frame_output: rows a, contraction e (bf16 mode: the hi
 //          plane, then the lo plane S - hi; fp32 mode: one fp32 plane)
 template <typename T, int D> struct WS {
@@ -450,20 +456,29 @@ __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
 #pragma unroll
             for (int j = 0; j < C::TC; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
     };
+    // G tiles: operand A from rho K (rows c), B from beta rho K (columns e).
+    // U tiles are formed transposed, U^T = (beta rho K)^T V: A from beta rho K
+    // (rows e), B from V (columns a), which leaves each lane four consecutive
+    // columns of one row of U, the register layout of the state in state_scan.
+    // Tiles are square in blocks (TR == TC), so a U tile's row blocks are its
+    // e blocks and its column blocks its a blocks; the choice only moves the
+    // (wave-uniform) LDS bases and rows.
+    static_assert(C::TR == C::TC, "square tiles");
+    const bool utile = rt * C::TR >= C::RB;         // this wave's tile lies in the U rows
+    const int a_arr = utile ? 2 : (rt * C::TR < C::RB ? 0 : 1);      // LDS array of operand A
+    const int b_arr = utile ? 1 : 2;                                   // LDS array of operand B
+    const int a_row0 = utile ? ct * C::TC : (rt * C::TR) % C::RB;      // first block of A
+    const int b_row0 = utile ? rt * C::TR - C::RB : ct * C::TC;        // first block of B
     auto mfma_stage = [&](const unsigned char* buf) {
-        const unsigned char* sKH = buf;
-        const unsigned char* sVT = buf + C::ARR;
-        const unsigned char* sXB = buf + 2 * C::ARR;
+        const unsigned char* sA = buf + a_arr * C::ARR;
+        const unsigned char* sB = buf + b_arr * C::ARR;
 #pragma unroll 1
         for (int ks = 0; ks < C::KST; ++ks) {
             frag A[C::TR], Bf[C::TC];
 #pragma unroll
-            for (int i = 0; i < C::TR; ++i) {
-                const int gb = rt * C::TR + i;      // row block over [G rows ; U rows]
-                A[i] = lds_frag<T, C::ROWB>(gb < C::RB ? sKH : sVT, (gb % C::RB) * 16 + r, ks, g);
-            }
+            for (int i = 0; i < C::TR; ++i) A[i] = lds_frag<T, C::ROWB>(sA, (a_row0 + i) * 16 + r, ks, g);
 #pragma unroll
-            for (int j = 0; j < C::TC; ++j) Bf[j] = lds_frag<T, C::ROWB>(sXB, (ct * C::TC + j) * 16 + r, ks, g);
+            for (int j = 0; j < C::TC; ++j) Bf[j] = lds_frag<T, C::ROWB>(sB, (b_row0 + j) * 16 + r, ks, g);
 #pragma unroll
             for (int i = 0; i < C::TR; ++i)
 #pragma unroll
@@ -504,8 +519,10 @@ __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
                     else
                         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, m), rw, gm_lane, blk, 0);
                 } else {
-                    // lane (r, g) holds U[16ga + 4g + t][16jb + r]: block (jb, ga), slot 16g + r
-                    const uint32_t blk = (uint32_t)(W::ut_off + (size_t)(jb * W::RT + (gb - C::RB)) * 1024);
+                    // U tile (transposed): acc[i][j] is block (e block a_row0 + i, a block
+                    // b_row0 + j); lane (r, g) holds U[16ga + r][16eb + 4g + t], slot 16g + r
+                    const int eb = a_row0 + i, ga = b_row0 + j;
+                    const uint32_t blk = (uint32_t)(W::ut_off + (size_t)(eb * W::RT + ga) * 1024);
                     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), rw, u_lane, blk, 0);
                 }
             }
@@ -593,11 +610,18 @@ template <typename T, int D> struct StateCfg {
 // One workgroup owns RTW consecutive 16-row tiles of one (b, h) state (rows
 // [16*RTW*rg, 16*RTW*(rg+1))); wave w owns columns [16w, 16w+16) of them.
 // Rows of S evolve independently, so workgroups never communicate.  Per frame:
-//   acc = alpha*S + U_f ;  acc += S_hi Gm + S_lo Gm  (bf16 Gm, S = S_hi + S_lo)
-//   (fp32 mode: acc += S Gm with fp32 MFMA)
-// Gm is rounded to bf16 once; that relative error (2^-9 of S Gm) is of the
-// same size as the error G already carries from its bf16 operands, and far
-// below the error of U, so a second (lo) plane of Gm would buy nothing.
+//   S_f = alpha*S + U_f + S_hi Gm      (bf16 MFMA, fp32 accumulate)
+//   (fp32 mode: S Gm with fp32 MFMA)
+// The product is formed transposed, (S Gm)^T = Gm^T S^T, with the Gm fragment
+// as operand A and the S rows as operand B, so each lane holds four
+// consecutive columns of one row of S: the state's LDS, workspace and global
+// accesses are then 8 and 16 bytes wide instead of 2 and 4.
+// Gm and S enter the product rounded to bf16 once: that relative error
+// (2^-9 of S Gm, itself small next to alpha S) is of the size G already
+// carries from its bf16 operands and far below the error of U, so neither a
+// lo plane of Gm nor of S in this product buys accuracy (the lo plane of S is
+// still formed, for frame_output).  Each 32-wide contraction step accumulates
+// into its own register set, so the MFMAs of a frame do not wait on each other.
 // S stays in fp32 registers; its bf16 hi/lo split is double-buffered in LDS
 // as the A operand (one barrier per frame), and the previous frame's planes
 // are copied to the workspace for frame_output while this frame's MFMAs run.
@@ -625,34 +649,33 @@ __global__ __launch_bounds__(4 * D, 1) void state_scan_kernel(ScanArgs a) {  // 
     const int a0 = rg * ROWS;                           // first state row of this workgroup
     const int h = bh % a.H, b = bh / a.H;
     const int Fc = a.Fc;
-    const int col = wave * 16 + r;                      // this lane's state column e
+    const int col0 = wave * 16 + 4 * g;                 // this lane's state columns col0..col0+3
 
     for (int i = tid; i < Fc; i += C::NW * 64) {
         const float x = a.alpha[((size_t)b * a.F + a.f0 + a.fsub0 + i) * a.H + h];
         sAlpha[i] = a.logits ? sigmoid_f(x) : x;
     }
 
-    // ---- initial state: registers (accumulator layout) and LDS (operand layout)
+    // ---- initial state: registers (lane (r, g) of tile i: row a0 + 16i + r,
+    //      columns col0..col0+3) and LDS (row-major planes, operand layout)
     f32x4 S[C::RTW];
     const float* sin = a.S_in ? a.S_in + (size_t)bh * D * D : nullptr;
 #pragma unroll
     for (int i = 0; i < C::RTW; ++i)
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-            S[i][t] = sin ? sin[(size_t)(a0 + 16 * i + 4 * g + t) * D + col] : 0.0f;
+        S[i] = sin ? *reinterpret_cast<const f32x4*>(sin + (size_t)(a0 + 16 * i + r) * D + col0)
+                   : f32x4{0, 0, 0, 0};
     auto put_lds = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < C::RTW; ++i) {
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int off = (16 * i + 4 * g + t) * C::ROWB + col * io::bytes;
-                if constexpr (sizeof(T) == 2) {
-                    const uint16_t hi = f2bf(S[i][t]);
-                    *reinterpret_cast<uint16_t*>(&sS[buf][0][off]) = hi;
-                    *reinterpret_cast<uint16_t*>(&sS[buf][1][off]) = f2bf(S[i][t] - bf2f(hi));
-                } else {
-                    *reinterpret_cast<float*>(&sS[buf][0][off]) = S[i][t];
-                }
+            const int off = (16 * i + r) * C::ROWB + col0 * io::bytes;
+            if constexpr (sizeof(T) == 2) {
+                const uint32_t h01 = pack_bf16x2(S[i][0], S[i][1]), h23 = pack_bf16x2(S[i][2], S[i][3]);
+                const uint32_t l01 = pack_bf16x2(S[i][0] - bf2f(h01 & 0xffffu), S[i][1] - bf2f(h01 >> 16));
+                const uint32_t l23 = pack_bf16x2(S[i][2] - bf2f(h23 & 0xffffu), S[i][3] - bf2f(h23 >> 16));
+                *reinterpret_cast<u32x2*>(&sS[buf][0][off]) = u32x2{h01, h23};
+                *reinterpret_cast<u32x2*>(&sS[buf][1][off]) = u32x2{l01, l23};
+            } else {
+                *reinterpret_cast<f32x4*>(&sS[buf][0][off]) = S[i];
             }
         }
     };
@@ -660,7 +683,7 @@ __global__ __launch_bounds__(4 * D, 1) void state_scan_kernel(ScanArgs a) {  // 
 
     struct Ops {
         frag bh_[C::KS];          // Gm for this wave's 16 columns
-        f32x4 u[C::RTW];          // U rows of each row tile, accumulator layout
+        f32x4 u[C::RTW];          // U of each row tile in the state's register layout
     };
     const size_t item0 = (size_t)bh * a.wsFc + a.fsub0;
     using W = WS<T, D>;
@@ -705,7 +728,8 @@ __global__ __launch_bounds__(4 * D, 1) void state_scan_kernel(ScanArgs a) {  // 
                 const int c0 = (kt * 32 + 8 * (l >> 4) + 4 * hh) % D;   // D = 16: upper lanes repeat
                 const u32x4 val =
                     *reinterpret_cast<const u32x4*>(&sS[buf][pl][(16 * i + (l & 15)) * C::ROWB + c0 * io::bytes]);
-                bstore16(rsp, base + (uint32_t)(pl * W::OPND) + W::frag_off(rg * C::RTW + i, kt, hh, l), val);
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    val, rsp, base + (uint32_t)(pl * W::OPND) + W::frag_off(rg * C::RTW + i, kt, hh, l), 0, kStreamStore);
             }
         }
     };
@@ -716,11 +740,12 @@ __global__ __launch_bounds__(4 * D, 1) void state_scan_kernel(ScanArgs a) {  // 
     auto step = [&](int fl, Ops& o, int nx, bool reload) {
         const int cur = fl & 1;                         // buffer holding S_{fl-1}
         const float al = sAlpha[fl];
-        f32x4 acc[C::RTW], acc2[C::RTW];
+        f32x4 acc[C::KS][C::RTW];                       // one chain per contraction step
 #pragma unroll
         for (int i = 0; i < C::RTW; ++i) {
-            acc[i] = S[i] * al + o.u[i];
-            acc2[i] = f32x4{0, 0, 0, 0};
+            acc[0][i] = S[i] * al + o.u[i];
+#pragma unroll
+            for (int ks = 1; ks < C::KS; ++ks) acc[ks][i] = f32x4{0, 0, 0, 0};
         }
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
@@ -731,28 +756,25 @@ __global__ __launch_bounds__(4 * D, 1) void state_scan_kernel(ScanArgs a) {  // 
             }
 #pragma unroll
             for (int i = 0; i < C::RTW; ++i) {
-                frag ahi, alo;
                 const int ro = (16 * i + r) * C::ROWB;
-                if constexpr (sizeof(T) == 2) {
+                frag ahi;
+                if constexpr (sizeof(T) == 2)
                     ahi = *reinterpret_cast<const u32x4*>(&sS[cur][0][ro + c0 * 2]);
-                    alo = *reinterpret_cast<const u32x4*>(&sS[cur][1][ro + c0 * 2]);
-                } else {
+                else
                     ahi = io::load(reinterpret_cast<const float*>(&sS[cur][0][ro + c0 * 4]));
-                    alo = io::zero();
-                }
-                if (!kvalid) {
-                    ahi = io::zero();
-                    alo = io::zero();
-                }
-                f32x4& dst = (ks & 1) ? acc2[i] : acc[i];
-                io::mma(dst, ahi, bhi);
-                if constexpr (sizeof(T) == 2) io::mma(dst, alo, bhi);
+                if (!kvalid) ahi = io::zero();
+                io::mma(acc[ks][i], bhi, ahi);             // (S Gm)^T += Gm^T S^T
             }
         }
         if (reload) load_ops(nx, o);
         copy_planes(fl - 1, cur);                       // S_{fl-1}: overlaps the MFMAs
 #pragma unroll
-        for (int i = 0; i < C::RTW; ++i) S[i] = acc[i] + acc2[i];
+        for (int i = 0; i < C::RTW; ++i) {
+            f32x4 t = acc[0][i];
+#pragma unroll
+            for (int ks = 1; ks < C::KS; ++ks) t += acc[ks][i];
+            S[i] = t;
+        }
         put_lds(cur ^ 1);
         __syncthreads();                                // S_fl visible; S_{fl-1} reads done
     };
@@ -779,12 +801,9 @@ __global__ __launch_bounds__(4 * D, 1) void state_scan_kernel(ScanArgs a) {  // 
     // ---- final state (fp32, row-major [a][e])
 #pragma unroll
     for (int i = 0; i < C::RTW; ++i) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const size_t idx = (size_t)bh * D * D + (size_t)(a0 + 16 * i + 4 * g + t) * D + col;
-            if (a.S_out) a.S_out[idx] = S[i][t];
-            if (a.S_out2) a.S_out2[idx] = S[i][t];
-        }
+        const size_t idx = (size_t)bh * D * D + (size_t)(a0 + 16 * i + r) * D + col0;
+        if (a.S_out) *reinterpret_cast<f32x4*>(a.S_out + idx) = S[i];
+        if (a.S_out2) *reinterpret_cast<f32x4*>(a.S_out2 + idx) = S[i];
     }
 }
 
