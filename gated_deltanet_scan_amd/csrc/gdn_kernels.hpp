@@ -469,7 +469,11 @@ __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
     const int b_arr = utile ? 1 : 2;                                   // LDS array of operand B
     const int a_row0 = utile ? ct * C::TC : (rt * C::TR) % C::RB;      // first block of A
     const int b_row0 = utile ? rt * C::TR - C::RB : ct * C::TC;        // first block of B
-    auto mfma_stage = [&](const unsigned char* buf) {
+    // `fresh` (first stage of an item) clears the accumulators here, after
+    // the stage's first fragment loads are issued rather than right after the
+    // previous item's epilogue: the accumulators are the data of its stores,
+    // and rewriting them makes the wave wait for those stores to complete.
+    auto mfma_stage = [&](const unsigned char* buf, bool fresh) {
         const unsigned char* sA = buf + a_arr * C::ARR;
         const unsigned char* sB = buf + b_arr * C::ARR;
 #pragma unroll 1
@@ -479,6 +483,12 @@ __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
             for (int i = 0; i < C::TR; ++i) A[i] = lds_frag<T, C::ROWB>(sA, (a_row0 + i) * 16 + r, ks, g);
 #pragma unroll
             for (int j = 0; j < C::TC; ++j) Bf[j] = lds_frag<T, C::ROWB>(sB, (b_row0 + j) * 16 + r, ks, g);
+            if constexpr (sizeof(T) == 2) {     // fp32 tiles have no registers to spare for this
+                if (ks == 0 && fresh) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    zero_acc();
+                }
+            }
 #pragma unroll
             for (int i = 0; i < C::TR; ++i)
 #pragma unroll
@@ -494,23 +504,28 @@ __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
     const uint32_t gm_lane = sizeof(T) == 2 ? (uint32_t)(256 * (g >> 1) + 16 * r + 8 * (g & 1))
                                             : (uint32_t)(1024 * (g & 1) + 256 * (g >> 1) + 16 * r);
     const uint32_t u_lane = (uint32_t)(lane * 16);
-    auto epilogue = [&](int k) {
+    // alpha of item k, loaded one item ahead of its epilogue
+    auto load_alpha = [&](int k) {
         const Item it = item_of(k);
-        float al = a.alpha[((size_t)it.b * a.F + it.f) * H + it.h];
+        return a.alpha[((size_t)it.b * a.F + it.f) * H + it.h];
+    };
+    auto epilogue = [&](int k, float al) {
+        const Item it = item_of(k);
         if (a.logits) al = sigmoid_f(al);
         const rsrc_t rw = make_rsrc(a.ws + (size_t)it.ws * W::item_bytes, (uint32_t)W::item_bytes);
+        // a wave's tile is all G or all U: two straight store sequences (a
+        // per-block branch made the compiler wait for each store to complete)
+        if (!utile) {
 #pragma unroll
-        for (int i = 0; i < C::TR; ++i) {
-            const int gb = rt * C::TR + i;
+            for (int i = 0; i < C::TR; ++i) {
+                const int gb = a_row0 + i;
 #pragma unroll
-            for (int j = 0; j < C::TC; ++j) {
-                const int jb = ct * C::TC + j;
-                const f32x4 x = acc[i][j];
-                if (gb < C::RB) {
+                for (int j = 0; j < C::TC; ++j) {
+                    const int jb = b_row0 + j;
                     // lane (r, g) holds G[16gb + 4g + t][16jb + r] = Gm^T[e][c] with e = 16jb + r:
                     // fragment (e-tile jb, kt = gb/2), lane slot 16*(2*(gb%2) + g/2) + r,
                     // values 4*(g%2) + t
-                    const f32x4 m = x * (-al);
+                    const f32x4 m = acc[i][j] * (-al);
                     const uint32_t blk = (uint32_t)(W::gm_off + (size_t)(jb * W::KS + (gb >> 1)) * W::FRAG +
                                                     512 * (gb & 1));
                     if constexpr (sizeof(T) == 2)
@@ -518,21 +533,26 @@ __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
                                                               rw, gm_lane, blk, 0);
                     else
                         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, m), rw, gm_lane, blk, 0);
-                } else {
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < C::TR; ++i)
+#pragma unroll
+                for (int j = 0; j < C::TC; ++j) {
                     // U tile (transposed): acc[i][j] is block (e block a_row0 + i, a block
                     // b_row0 + j); lane (r, g) holds U[16ga + r][16eb + 4g + t], slot 16g + r
                     const int eb = a_row0 + i, ga = b_row0 + j;
                     const uint32_t blk = (uint32_t)(W::ut_off + (size_t)(eb * W::RT + ga) * 1024);
-                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), rw, u_lane, blk, 0);
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][j]), rw, u_lane, blk, 0);
                 }
-            }
         }
     };
 
     if (nst == 0) {                                  // no tokens: G = U = 0
         if (!producer && cbusy) {
             zero_acc();
-            for (int k = 0; k < nmine; ++k) epilogue(k);
+            for (int k = 0; k < nmine; ++k) epilogue(k, load_alpha(k));
         }
         return;
     }
@@ -577,13 +597,19 @@ __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
         }
         return;
     }
-    zero_acc();
+    float al_next = load_alpha(0);
+    bool fresh = true;
+    if constexpr (sizeof(T) != 2) zero_acc();
     for (int p = 0; p < 4 * nquad; ++p) {
         if (cbusy && p >= 1 && p <= total) {
-            mfma_stage((p & 1) ? buf0 : buf1);      // stage p-1 sits in buffer (p-1)&1
+            mfma_stage((p & 1) ? buf0 : buf1, fresh);   // stage p-1 sits in buffer (p-1)&1
+            fresh = false;
             if ((p - 1) % nst == nst - 1) {
-                epilogue((p - 1) / nst);
-                zero_acc();
+                const int k = (p - 1) / nst;
+                epilogue(k, al_next);
+                fresh = true;
+                if constexpr (sizeof(T) != 2) zero_acc();
+                al_next = load_alpha(k + 1 < nmine ? k + 1 : k);
             }
         }
         __syncthreads();
