@@ -413,20 +413,34 @@ __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
     };
     // Norms, scales and the transposed LDS write of stage gs.
     auto write_stage = [&](int gs, const Stage& R, unsigned char* buf) {
-        float rho[C::TPT], xs[C::TPT];
+        // the tokens' sums of squares as independent chains (two per token),
+        // then their lane reductions side by side, then the gates: a branch
+        // inside the per-token loop kept the compiler from interleaving them
+        float ssa[C::TPT], ssb[C::TPT], bt[C::TPT], rho[C::TPT], xs[C::TPT];
 #pragma unroll
         for (int j = 0; j < C::TPT; ++j) {
-            float ss = 0.0f;
+            ssa[j] = 0.0f;
+            ssb[j] = 0.0f;
 #pragma unroll
-            for (int e = 0; e < C::FPT; ++e) {
-                const float kx = Q::get(R.k[j], e);
-                ss = fmaf(kx, kx, ss);
+            for (int e = 0; e < C::FPT; e += 2) {
+                const float k0 = Q::get(R.k[j], e), k1 = Q::get(R.k[j], e + 1);
+                ssa[j] = fmaf(k0, k0, ssa[j]);
+                ssb[j] = fmaf(k1, k1, ssb[j]);
             }
-            ss = lane_group_sum<C::SL>(ss);
-            float bt = R.bt[j];
-            if (a.logits) bt = ((gs % nst) * C::TS + tl * C::TPT + j < N) ? sigmoid_f(bt) * inv_n : 0.0f;
-            rho[j] = fminf(__builtin_amdgcn_rsqf(ss), inv_eps);   // 1 / max(|k|, eps)
-            xs[j] = bt * rho[j];
+        }
+#pragma unroll
+        for (int j = 0; j < C::TPT; ++j) ssa[j] = lane_group_sum<C::SL>(ssa[j] + ssb[j]);
+#pragma unroll
+        for (int j = 0; j < C::TPT; ++j) bt[j] = R.bt[j];
+        if (a.logits) {
+            const int t0 = (gs % nst) * C::TS + tl * C::TPT;
+#pragma unroll
+            for (int j = 0; j < C::TPT; ++j) bt[j] = (t0 + j < N) ? sigmoid_f(bt[j]) * inv_n : 0.0f;
+        }
+#pragma unroll
+        for (int j = 0; j < C::TPT; ++j) {
+            rho[j] = fminf(__builtin_amdgcn_rsqf(ssa[j]), inv_eps);   // 1 / max(|k|, eps)
+            xs[j] = bt[j] * rho[j];
         }
         unsigned char* sKH = buf;                   // rho k         (A of G)
         unsigned char* sVT = buf + C::ARR;          // v             (A of U)
