@@ -56,41 +56,6 @@ struct ProfScope {
     }
 };
 
-// ---------------------------------------------------------------- side stream
-// One non-blocking stream per device (default priority) runs the state
-// recurrence while the caller's stream runs the output pass; events order them.
-struct Side {
-    hipStream_t stream = nullptr;
-    bool failed = false;
-    std::vector<hipEvent_t> ev;
-    size_t next = 0;
-};
-std::mutex g_side_mu;
-Side g_side[64];
-
-hipStream_t side_stream(int dev) {
-    Side& sd = g_side[dev];
-    if (!sd.stream && !sd.failed) {
-        if (hipStreamCreateWithFlags(&sd.stream, hipStreamNonBlocking) != hipSuccess) {
-            sd.stream = nullptr;
-            sd.failed = true;
-        }
-    }
-    return sd.stream;
-}
-hipEvent_t side_event(int dev) {
-    Side& sd = g_side[dev];
-    if (sd.ev.size() < 64) {
-        hipEvent_t e;
-        if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return nullptr;
-        sd.ev.push_back(e);
-        return e;
-    }
-    hipEvent_t e = sd.ev[sd.next];
-    sd.next = (sd.next + 1) % sd.ev.size();
-    return e;
-}
-
 // ---------------------------------------------------------------- device checks
 struct DevInfo {
     bool known = false;
@@ -127,11 +92,6 @@ struct Plan {
     size_t carry_off = 0;    // fp32 [B][H][Dv][Dk] state carried between launches
     size_t ws_bytes = 0;
 };
-
-// Frames per state_scan / frame_output launch when the recurrence is
-// pipelined against the output pass on a second stream.
-constexpr int kPipeFrames = 32;
-constexpr bool kPipeline = false;   // overlap measured slower: both passes are L1-fill bound
 
 bool dim_ok(int D) { return D == 16 || D == 32 || D == 64 || D == 128; }
 
@@ -203,16 +163,13 @@ gdn_status launch_output(ScanArgs a, hipStream_t stream, int cus) {
     return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 
-// Launch order.  frame_gram covers a chunk of up to kMaxChunkFrames frames on
-// the caller's stream.  The recurrence then runs in sub-chunks of kPipeFrames
-// frames on the side stream; each sub-chunk's output pass waits (on the
-// caller's stream) for that sub-chunk only, so outputs of early frames overlap
-// the recurrence of later ones.  The state is carried in `carry` (S_final, or
-// the workspace's carry region).  Everything the call enqueues is ordered
-// before the caller's stream continues: the last output pass waits for the
-// last recurrence launch.
+// Launch order, per chunk of up to kMaxChunkFrames frames, all on the caller's
+// stream: frame_gram, then the recurrence (whose state is carried in `carry`:
+// S_final, or the workspace's carry region), then the output pass.
+// (Running the recurrence on a second stream in sub-chunks, overlapped with
+// the output pass, measured slower.)
 template <typename T, int D>
-gdn_status launch_all(const Plan& p, ScanArgs a, hipStream_t stream, int cus, float* carry, int dev) {
+gdn_status launch_all(const Plan& p, ScanArgs a, hipStream_t stream, int cus, float* carry) {
     const int units = (int)p.units;
     gdn_status st = GDN_OK;
     for (int f0 = 0; f0 < a.F; f0 += p.Fc) {
@@ -228,48 +185,22 @@ gdn_status launch_all(const Plan& p, ScanArgs a, hipStream_t stream, int cus, fl
             hipLaunchKernelGGL((gdn::frame_gram_kernel<T, D>), dim3(grid), dim3(1024), 0, stream, a);
         }
         if (hipGetLastError() != hipSuccess) return GDN_ERR_LAUNCH;
-
-        hipStream_t side = nullptr;
-        if (kPipeline && a.N > 0 && a.Fc > kPipeFrames) {
-            std::lock_guard<std::mutex> lk(g_side_mu);
-            side = side_stream(dev);
-        }
-        if (!side) {                                   // one stream: recurrence, then outputs
-            ScanArgs s = a;
-            s.S_out = carry;
-            if ((st = launch_state<T, D>(s, stream)) != GDN_OK) return st;
-            a.S_in = carry;
-            if ((st = launch_output<T, D>(a, stream, cus)) != GDN_OK) return st;
-            continue;
-        }
-        std::lock_guard<std::mutex> lk(g_side_mu);
-        hipEvent_t eg = side_event(dev);
-        if (!eg || hipEventRecord(eg, stream) != hipSuccess || hipStreamWaitEvent(side, eg, 0) != hipSuccess)
-            return GDN_ERR_LAUNCH;
-        for (int s0 = 0; s0 < a.Fc; s0 += kPipeFrames) {
-            ScanArgs s = a;
-            s.fsub0 = s0;
-            s.Fc = a.Fc - s0 < kPipeFrames ? a.Fc - s0 : kPipeFrames;
-            s.S_out = carry;
-            if ((st = launch_state<T, D>(s, side)) != GDN_OK) return st;
-            a.S_in = carry;
-            hipEvent_t es = side_event(dev);
-            if (!es || hipEventRecord(es, side) != hipSuccess || hipStreamWaitEvent(stream, es, 0) != hipSuccess)
-                return GDN_ERR_LAUNCH;
-            s.S_in = carry;
-            if ((st = launch_output<T, D>(s, stream, cus)) != GDN_OK) return st;
-        }
+        ScanArgs s = a;
+        s.S_out = carry;
+        if ((st = launch_state<T, D>(s, stream)) != GDN_OK) return st;
+        a.S_in = carry;
+        if ((st = launch_output<T, D>(a, stream, cus)) != GDN_OK) return st;
     }
     return GDN_OK;
 }
 
 template <typename T>
-gdn_status dispatch_d(const Plan& p, const ScanArgs& a, hipStream_t s, int cus, float* carry, int dev) {
+gdn_status dispatch_d(const Plan& p, const ScanArgs& a, hipStream_t s, int cus, float* carry) {
     switch (p.D) {
-        case 16: return launch_all<T, 16>(p, a, s, cus, carry, dev);
-        case 32: return launch_all<T, 32>(p, a, s, cus, carry, dev);
-        case 64: return launch_all<T, 64>(p, a, s, cus, carry, dev);
-        case 128: return launch_all<T, 128>(p, a, s, cus, carry, dev);
+        case 16: return launch_all<T, 16>(p, a, s, cus, carry);
+        case 32: return launch_all<T, 32>(p, a, s, cus, carry);
+        case 64: return launch_all<T, 64>(p, a, s, cus, carry);
+        case 128: return launch_all<T, 128>(p, a, s, cus, carry);
         default: return GDN_ERR_UNSUPPORTED;
     }
 }
@@ -359,10 +290,8 @@ gdn_status run(const gdn_desc* d, bool step, const void* q, const void* k, const
     // the state between launches lives in S_final, or in the workspace's carry region
     float* carry = S_final ? S_final
                            : reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + p.carry_off);
-    int dev = 0;
-    (void)hipGetDevice(&dev);
-    return d->io_dtype == GDN_BF16 ? dispatch_d<uint16_t>(p, a, stream, cus, carry, dev)
-                                   : dispatch_d<float>(p, a, stream, cus, carry, dev);
+    return d->io_dtype == GDN_BF16 ? dispatch_d<uint16_t>(p, a, stream, cus, carry)
+                                   : dispatch_d<float>(p, a, stream, cus, carry);
 }
 
 }  // namespace
