@@ -307,9 +307,9 @@ __device__ __forceinline__ float lane_group_sum(float x) {
     }
 }
 
-// Persistent workgroups of 16 waves; workgroup w takes the (b, h, f) items
-// w, w + grid, w + 2*grid, ... in frame-major order (head fastest), so the
-// heads of one frame together read each contiguous token row of [B,F,N,H,D].
+// Persistent workgroups of 16 waves walking the (b, h, f) items in
+// frame-major order (head fastest), round by round, so the heads of one frame
+// together read each contiguous token row of [B,F,N,H,D].
 // Waves 8-15 produce: each thread streams 16 bytes of features of two tokens
 // of K_f and V_f (and their betas) through registers, four stages ahead, reduces the
 // key norms over the lanes of each token, scales, and writes the stage
@@ -331,7 +331,14 @@ __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
 
     const int N = a.N, H = a.H;
     const int items = a.B * a.H * a.Fc;
-    const int nmine = (int)blockIdx.x < items ? (items - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
+    // Round k of the persistent loop covers items [k*G, (k+1)*G) (G = grid),
+    // so the heads of a frame are read together; within a round, workgroup b
+    // takes item k*G + (b + k) mod G.  The rotation walks every workgroup
+    // through all heads: a head's 256-byte rows sit at one fixed offset of
+    // every token row, and with a fixed head per workgroup the workgroups of
+    // the slower heads (measured up to 15% slower) set the kernel's time.
+    const int G = (int)gridDim.x, rounds = items / G;
+    const int nmine = rounds + (((int)blockIdx.x + rounds) % G < items - rounds * G ? 1 : 0);
     const int nst = (N + C::TS - 1) / C::TS;
     const int total = nmine * nst;                  // stages of this workgroup
     const int tid = threadIdx.x, lane = tid & 63;
@@ -343,7 +350,7 @@ __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
         int b, h, f, ws;                            // batch, head, frame, workspace item
     };
     auto item_of = [&](int k) {
-        const int x = (int)blockIdx.x + k * (int)gridDim.x;
+        const int x = k * G + ((int)blockIdx.x + k) % G;
         Item it;
         it.h = x % H;
         const int fl = (x / H) % a.Fc;
@@ -885,9 +892,13 @@ __global__ __launch_bounds__(256, 2) void frame_output_kernel(ScanArgs a) {
     using frag = typename io::frag;
     __shared__ __attribute__((aligned(16))) unsigned char smem[C::LDS];
 
-    // frame-major order, head fastest: x = ((b*Fc + fl)*tsplit + part)*H + h
+    // frame-major order, head fastest: x = ((b*Fc + fl)*tsplit + part)*H + hs,
+    // with the head rotated by the rest of the index, h = (hs + x/H) mod H:
+    // workgroups are dealt to the XCDs round-robin, and without the rotation
+    // each XCD would only ever get the same two heads (whose rows sit at
+    // fixed offsets of every token row)
     const int x = blockIdx.x;
-    const int h = x % a.H;
+    const int h = (x % a.H + x / a.H) % a.H;
     const int part = (x / a.H) % a.tsplit;
     const int fl = (x / (a.H * a.tsplit)) % a.Fc;
     const int b = x / (a.H * a.tsplit * a.Fc);
