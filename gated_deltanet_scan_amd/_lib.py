@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(_PKG, "libgdn.so")
 GDN_BF16 = 0
 GDN_F32 = 1
 GDN_FLAG_GATES_ARE_LOGITS = 0x1
-GDN_NUM_KERNELS = 4
+GDN_NUM_KERNELS = 5
 
 STATUS = {0: "GDN_OK", 1: "GDN_ERR_INVALID_ARG", 2: "GDN_ERR_UNSUPPORTED", 3: "GDN_ERR_ALIGNMENT",
           4: "GDN_ERR_ALIAS", 5: "GDN_ERR_WORKSPACE", 6: "GDN_ERR_LAUNCH", 7: "GDN_ERR_NO_DEVICE"}

@@ -18,9 +18,13 @@ using gdn::ScanArgs;
 
 constexpr int kVersion = 10000;  // 1.0.0
 
-enum KernelKind { K_GRAM = 0, K_STATE = 1, K_OUTPUT = 2, K_COPY = 3 };
+enum KernelKind { K_GRAM = 0, K_STATE = 1, K_OUTPUT = 2, K_COPY = 3, K_STEP = 4 };
 const char* const kKernelNames[GDN_NUM_KERNELS] = {"frame_gram", "state_scan", "frame_output",
-                                                   "state_copy"};
+                                                   "state_copy", "frame_step"};
+
+// The one-frame path sizes its workspace for this many CUs (MI355X has 256;
+// a device with fewer uses fewer token ranges).
+constexpr int kSizingCUs = 256;
 
 // ---------------------------------------------------------------- profiling
 struct Profiler {
@@ -90,8 +94,30 @@ struct Plan {
     int Fc = 0;              // frames per launch chunk
     size_t item_bytes = 0;   // workspace per (b, h, frame)
     size_t carry_off = 0;    // fp32 [B][H][Dv][Dk] state carried between launches
+    // one-frame path (F == 1): fp32 partial G and U per (b, h, token range),
+    // then a copy of S_in
+    int parts_max = 0;
+    size_t scopy_off = 0;
     size_t ws_bytes = 0;
 };
+
+// Token ranges of frame_gram on the one-frame path: enough (b, h, range) items
+// to give every CU one, each range a whole number of frame_gram stages.
+int gram_stage_tokens(int esz, int D) { return 16384 / (D * esz); }   // GramCfg::TS
+void step_ranges(int64_t units, int N, int ts, int cus, int* parts, int* tpart) {
+    if (N <= 0 || units <= 0) {
+        *parts = 1;
+        *tpart = N > 0 ? N : 0;
+        return;
+    }
+    const int stages = (N + ts - 1) / ts;
+    int64_t want = ((int64_t)cus + units - 1) / units;
+    int p = (int)(want < stages ? want : stages);
+    if (p < 1) p = 1;
+    const int per = ((N + p - 1) / p + ts - 1) / ts * ts;
+    *tpart = per;
+    *parts = (N + per - 1) / per;
+}
 
 bool dim_ok(int D) { return D == 16 || D == 32 || D == 64 || D == 128; }
 
@@ -116,6 +142,13 @@ gdn_status check_desc(const gdn_desc* d, bool step, Plan* p) {
     // frames per launch chunk (state_scan stages the chunk's gates in LDS)
     p->Fc = d->F < gdn::kMaxChunkFrames ? d->F : gdn::kMaxChunkFrames;
     p->item_bytes = gdn::ws_item_bytes(p->esz, p->D);
+    if (d->F == 1) {
+        int tpart = 0;
+        step_ranges(p->units, d->N, gram_stage_tokens(p->esz, p->D), kSizingCUs, &p->parts_max, &tpart);
+        p->scopy_off = ((size_t)p->units * p->parts_max * gdn::part_bytes(p->D) + 255) / 256 * 256;
+        p->ws_bytes = p->units > 0 ? p->scopy_off + (size_t)p->units * p->D * p->D * sizeof(float) : 0;
+        return GDN_OK;
+    }
     p->carry_off = ((size_t)p->units * p->Fc * p->item_bytes + 255) / 256 * 256;
     p->ws_bytes = (p->units > 0 && d->F > 0)
                       ? p->carry_off + (size_t)p->units * p->D * p->D * sizeof(float)
@@ -182,7 +215,7 @@ gdn_status launch_all(const Plan& p, ScanArgs a, hipStream_t stream, int cus, fl
             ProfScope ps(K_GRAM, stream);
             // persistent: one workgroup per CU, each streaming its share of the items
             const int grid = items < cus ? items : (cus > 0 ? cus : 256);
-            hipLaunchKernelGGL((gdn::frame_gram_kernel<T, D>), dim3(grid), dim3(1024), 0, stream, a);
+            hipLaunchKernelGGL((gdn::frame_gram_kernel<T, D, false>), dim3(grid), dim3(1024), 0, stream, a);
         }
         if (hipGetLastError() != hipSuccess) return GDN_ERR_LAUNCH;
         ScanArgs s = a;
@@ -194,8 +227,65 @@ gdn_status launch_all(const Plan& p, ScanArgs a, hipStream_t stream, int cus, fl
     return GDN_OK;
 }
 
+// One frame (F == 1): frame_gram over (b, h, token range) items, writing fp32
+// partials and copying S_in, then frame_step (state update and output pass in
+// one launch).
+template <typename T, int D>
+gdn_status launch_step(const Plan& p, ScanArgs a, hipStream_t stream, int cus) {
+    const int units = (int)p.units;
+    a.f0 = 0;
+    a.Fc = 1;
+    a.wsFc = 1;
+    a.fsub0 = 0;
+    int parts = 1, tpart = 0;
+    step_ranges(p.units, a.N, gdn::GramCfg<T, D>::TS, cus < kSizingCUs ? cus : kSizingCUs, &parts, &tpart);
+    if (parts > p.parts_max) return GDN_ERR_LAUNCH;   // cannot happen: sized for kSizingCUs
+    a.parts = parts;
+    a.tpart = tpart;
+    unsigned char* ws = a.ws;
+    a.spart = reinterpret_cast<float*>(ws);
+    float* scopy = reinterpret_cast<float*>(ws + p.scopy_off);
+    a.scopy = a.S_in ? scopy : nullptr;
+    a.ncopy = units * D * D;
+    {
+        ProfScope ps(K_GRAM, stream);
+        const int items = units * parts;
+        const int grid = items < cus ? items : (cus > 0 ? cus : 256);
+        hipLaunchKernelGGL((gdn::frame_gram_kernel<T, D, true>), dim3(grid), dim3(1024), 0, stream, a);
+    }
+    if (hipGetLastError() != hipSuccess) return GDN_ERR_LAUNCH;
+    ScanArgs s = a;
+    s.S_in = a.S_in ? scopy : nullptr;
+    // output ranges: a few workgroups per CU, at least 64 tokens each
+    const int want = 2 * (cus > 0 ? cus : 256);
+    int tsplit = (want + units - 1) / units;
+    const int maxsplit = a.N > 0 ? (a.N + 63) / 64 : 1;
+    if (tsplit > maxsplit) tsplit = maxsplit;
+    if (tsplit < 1) tsplit = 1;
+    int tchunk = a.N > 0 ? (a.N + tsplit - 1) / tsplit : 0;
+    tchunk = (tchunk + 15) / 16 * 16;
+    if (a.N > 0) tsplit = (a.N + tchunk - 1) / tchunk;
+    s.tsplit = tsplit;
+    s.tchunk = tchunk;
+    {
+        ProfScope ps(K_STEP, stream);
+        const int grid = 8 * ((units + 7) / 8) * tsplit;
+        hipLaunchKernelGGL((gdn::frame_step_kernel<T, D>), dim3(grid), dim3(gdn::StepCfg<T, D>::NTH), 0, stream, s);
+    }
+    return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
 template <typename T>
 gdn_status dispatch_d(const Plan& p, const ScanArgs& a, hipStream_t s, int cus, float* carry) {
+    if (a.F == 1) {
+        switch (p.D) {
+            case 16: return launch_step<T, 16>(p, a, s, cus);
+            case 32: return launch_step<T, 32>(p, a, s, cus);
+            case 64: return launch_step<T, 64>(p, a, s, cus);
+            case 128: return launch_step<T, 128>(p, a, s, cus);
+            default: return GDN_ERR_UNSUPPORTED;
+        }
+    }
     switch (p.D) {
         case 16: return launch_all<T, 16>(p, a, s, cus, carry);
         case 32: return launch_all<T, 32>(p, a, s, cus, carry);
@@ -287,9 +377,15 @@ gdn_status run(const gdn_desc* d, bool step, const void* q, const void* k, const
     a.wsFc = p.Fc;
     a.fsub0 = 0;
     a.tok_bytes = d->N > 0 ? (uint32_t)(((size_t)(d->N - 1) * d->H * p.D + p.D) * p.esz) : 0u;
+    a.parts = 1;
+    a.tpart = d->N;
+    a.spart = nullptr;
+    a.scopy = nullptr;
+    a.ncopy = 0;
     // the state between launches lives in S_final, or in the workspace's carry region
-    float* carry = S_final ? S_final
-                           : reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + p.carry_off);
+    float* carry = (S_final || d->F == 1)
+                       ? S_final
+                       : reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + p.carry_off);
     return d->io_dtype == GDN_BF16 ? dispatch_d<uint16_t>(p, a, stream, cus, carry)
                                    : dispatch_d<float>(p, a, stream, cus, carry);
 }

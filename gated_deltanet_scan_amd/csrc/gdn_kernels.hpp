@@ -92,6 +92,10 @@ constexpr int kNonTemporal = 2;
 // shared vector-memory counter and stalled the next frames' operand loads
 // once about half the frames were written (state_scan 124 -> 91 us).
 constexpr int kStreamStore = 2 | 16;
+// Stores of frame_gram's Gm and U: device scope (sc1).  Measured 6% faster
+// for frame_gram than the default policy, with no cost to the recurrence that
+// reads them; the non-temporal bit instead slowed those reads by half.
+constexpr int kWorkspaceStore = 16;
 __device__ __forceinline__ u32x4 bload16_nt(rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNonTemporal);
 }
@@ -211,7 +215,33 @@ struct ScanArgs {
                           // end of its last row: (N-1)*H*D*esz + D*esz (0 if N == 0)
     int logits;
     float eps;
+    // One-frame path (see frame_step_kernel): frame_gram splits each (b, h)
+    // into `parts` token ranges of `tpart` tokens (a multiple of its stage)
+    // and, when parts > 1, writes unscaled fp32 partial G and U per range to
+    // `spart`; it also copies `S_in` (ncopy floats) to `scopy` when that is
+    // not NULL.  The scan path uses parts = 1, tpart = N.
+    int parts;
+    int tpart;
+    float* spart;
+    float* scopy;
+    int ncopy;
 };
+
+// Partial G and U of one token range (one-frame path), both fp32: G in the
+// fragment-major layout of the fp32 workspace (unscaled), then U as in the
+// workspace.
+template <int D> struct PartLayout {
+    static constexpr int KS = (D + 31) / 32, RT = D / 16;
+    static constexpr size_t g_off = 0;
+    static constexpr size_t u_off = (size_t)RT * KS * 2048;
+    static constexpr size_t bytes = u_off + (size_t)RT * RT * 1024;
+    // byte offset of lane `lane`'s slot in G fragment (tile, kt), half h
+    __device__ static __forceinline__ uint32_t frag_off(int tile, int kt, int h, int lane) {
+        return (uint32_t)((tile * KS + kt) * 2048) + (uint32_t)(h * 1024 + lane * 16);
+    }
+};
+constexpr size_t part_bytes(int D) { return (size_t)(D / 16) * ((D + 31) / 32) * 2048 + (size_t)(D / 16) * (D / 16) * 1024; }
+static_assert(part_bytes(64) == PartLayout<64>::bytes && part_bytes(16) == PartLayout<16>::bytes, "partial layout");
 
 // XCD-aware placement: workgroups are dispatched round-robin over the 8 XCDs,
 // so id % 8 is the XCD.  Map ids so that groups of `per` consecutive logical
@@ -321,7 +351,9 @@ __device__ __forceinline__ float lane_group_sum(float x) {
 // an item's last stage they write Gm = -alpha G and U to the workspace.  Two
 // waves of each role per SIMD let one issue while the other waits: a single
 // wave issues VALU work far below the SIMD's rate.
-template <typename T, int D>
+// PART selects the one-frame path's variant (token ranges, fp32 partials,
+// state copy); the scan path's instantiation carries none of it.
+template <typename T, int D, bool PART>
 __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
     using C = GramCfg<T, D>;
     using io = IO<T>;
@@ -330,7 +362,8 @@ __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
     __shared__ __attribute__((aligned(16))) unsigned char smem[C::LDS];
 
     const int N = a.N, H = a.H;
-    const int items = a.B * a.H * a.Fc;
+    const int parts = PART ? a.parts : 1, tpart = PART ? a.tpart : N;
+    const int items = a.B * a.H * a.Fc * parts;
     // Round k of the persistent loop covers items [k*G, (k+1)*G) (G = grid),
     // so the heads of a frame are read together; within a round, workgroup b
     // takes item k*G + (b + k) mod G.  The rotation walks every workgroup
@@ -339,7 +372,7 @@ __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
     // the slower heads (measured up to 15% slower) set the kernel's time.
     const int G = (int)gridDim.x, rounds = items / G;
     const int nmine = rounds + (((int)blockIdx.x + rounds) % G < items - rounds * G ? 1 : 0);
-    const int nst = (N + C::TS - 1) / C::TS;
+    const int nst = (tpart + C::TS - 1) / C::TS;    // stages per item (token range)
     const int total = nmine * nst;                  // stages of this workgroup
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches and offsets
@@ -347,18 +380,24 @@ __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
     const bool producer = wave >= 8;
 
     struct Item {
-        int b, h, f, ws;                            // batch, head, frame, workspace item
+        int b, h, f, p, ws;                         // batch, head, frame, token range,
+                                                    // workspace (or partial) slot
     };
+    // item x: head fastest, then token range, frame, batch
     auto item_of = [&](int k) {
         const int x = k * G + ((int)blockIdx.x + k) % G;
         Item it;
         it.h = x % H;
-        const int fl = (x / H) % a.Fc;
-        it.b = x / (H * a.Fc);
+        const int y = x / H;
+        it.p = y % parts;
+        const int fl = (y / parts) % a.Fc;
+        it.b = y / (parts * a.Fc);
         it.f = a.f0 + fl;
-        it.ws = (it.b * H + it.h) * a.wsFc + fl;
+        it.ws = ((it.b * H + it.h) * a.wsFc + fl) * parts + it.p;
         return it;
     };
+    // tokens of item `it`'s range (the host makes every range non-empty)
+    auto range_tokens = [&](const Item& it) { return PART ? min(tpart, N - it.p * tpart) : N; };
 
     // ---- producer state (32-bit offsets: the host bounds a frame below 2 GiB)
     const int ptid = tid & (C::NP - 1);
@@ -370,7 +409,6 @@ __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
     // betas of this thread's tokens (the lanes of a token load the same value:
     // an exchange through ds_bpermute instead waited on LDS latency)
     const uint32_t b_off0 = (uint32_t)(tl * C::TPT * H * 4);
-    const uint32_t beta_bytes = N > 0 ? (uint32_t)(((N - 1) * H + 1) * 4) : 0u;
     const float inv_n = N > 0 ? 1.0f / (float)N : 0.0f;
     const float inv_eps = 1.0f / a.eps;
     // this thread's LDS write offsets (feature e, its TPT tokens), fixed for every stage
@@ -397,9 +435,12 @@ __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
     };
     auto loader_item = [&](Loader& L, int kk) {
         const Item it = item_of(kk);
-        const size_t tok0 = ((size_t)it.b * a.F + it.f) * (size_t)N;
-        L.rk = make_rsrc(static_cast<const T*>(a.k) + tok0 * rowstride + (size_t)it.h * D, a.tok_bytes);
-        L.rv = make_rsrc(static_cast<const T*>(a.v) + tok0 * rowstride + (size_t)it.h * D, a.tok_bytes);
+        const size_t tok0 = ((size_t)it.b * a.F + it.f) * (size_t)N + (size_t)it.p * tpart;
+        const int nt = range_tokens(it);
+        const uint32_t kv_bytes = nt > 0 ? (uint32_t)(((size_t)(nt - 1) * H * D + D) * C::SZ) : 0u;
+        const uint32_t beta_bytes = nt > 0 ? (uint32_t)(((nt - 1) * H + 1) * 4) : 0u;
+        L.rk = make_rsrc(static_cast<const T*>(a.k) + tok0 * rowstride + (size_t)it.h * D, kv_bytes);
+        L.rv = make_rsrc(static_cast<const T*>(a.v) + tok0 * rowstride + (size_t)it.h * D, kv_bytes);
         L.rb = make_rsrc(a.beta + tok0 * H + it.h, beta_bytes);
         L.kvo = kv_off0;
         L.bo = b_off0;
@@ -440,9 +481,9 @@ __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
 #pragma unroll
         for (int j = 0; j < C::TPT; ++j) bt[j] = R.bt[j];
         if (a.logits) {
-            const int t0 = (gs % nst) * C::TS + tl * C::TPT;
+            const int t0 = (gs % nst) * C::TS + tl * C::TPT, nt = range_tokens(item_of(gs / nst));
 #pragma unroll
-            for (int j = 0; j < C::TPT; ++j) bt[j] = (t0 + j < N) ? sigmoid_f(bt[j]) * inv_n : 0.0f;
+            for (int j = 0; j < C::TPT; ++j) bt[j] = (t0 + j < nt) ? sigmoid_f(bt[j]) * inv_n : 0.0f;
         }
 #pragma unroll
         for (int j = 0; j < C::TPT; ++j) {
@@ -532,6 +573,34 @@ __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
     };
     auto epilogue = [&](int k, float al) {
         const Item it = item_of(k);
+        if constexpr (PART) {                        // one-frame path: fp32 partials
+            using PL = PartLayout<D>;
+            const rsrc_t rp = make_rsrc(reinterpret_cast<unsigned char*>(a.spart) + (size_t)it.ws * PL::bytes,
+                                        (uint32_t)PL::bytes);
+            const uint32_t g32_lane = (uint32_t)(1024 * (g & 1) + 256 * (g >> 1) + 16 * r);
+            if (!utile) {
+#pragma unroll
+                for (int i = 0; i < C::TR; ++i)
+#pragma unroll
+                    for (int j = 0; j < C::TC; ++j) {
+                        const int gb = a_row0 + i, jb = b_row0 + j;
+                        const uint32_t blk = (uint32_t)(PL::g_off + (size_t)(jb * PL::KS + (gb >> 1)) * 2048 + 512 * (gb & 1));
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][j]), rp, g32_lane, blk,
+                                                               kWorkspaceStore);
+                    }
+            } else {
+#pragma unroll
+                for (int i = 0; i < C::TR; ++i)
+#pragma unroll
+                    for (int j = 0; j < C::TC; ++j) {
+                        const int eb = a_row0 + i, ga = b_row0 + j;
+                        const uint32_t blk = (uint32_t)(PL::u_off + (size_t)(eb * PL::RT + ga) * 1024);
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][j]), rp, u_lane, blk,
+                                                               kWorkspaceStore);
+                    }
+            }
+            return;
+        }
         if (a.logits) al = sigmoid_f(al);
         const rsrc_t rw = make_rsrc(a.ws + (size_t)it.ws * W::item_bytes, (uint32_t)W::item_bytes);
         // a wave's tile is all G or all U: two straight store sequences (a
@@ -551,9 +620,9 @@ __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
                                                     512 * (gb & 1));
                     if constexpr (sizeof(T) == 2)
                         __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf16x2(m[0], m[1]), pack_bf16x2(m[2], m[3])},
-                                                              rw, gm_lane, blk, 0);
+                                                              rw, gm_lane, blk, kWorkspaceStore);
                     else
-                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, m), rw, gm_lane, blk, 0);
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, m), rw, gm_lane, blk, kWorkspaceStore);
                 }
             }
         } else {
@@ -565,12 +634,17 @@ __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
                     // b_row0 + j); lane (r, g) holds U[16ga + r][16eb + 4g + t], slot 16g + r
                     const int eb = a_row0 + i, ga = b_row0 + j;
                     const uint32_t blk = (uint32_t)(W::ut_off + (size_t)(eb * W::RT + ga) * 1024);
-                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][j]), rw, u_lane, blk, 0);
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][j]), rw, u_lane, blk, kWorkspaceStore);
                 }
         }
     };
 
     if (nst == 0) {                                  // no tokens: G = U = 0
+        if constexpr (PART) {
+            if (producer && a.scopy)
+                for (int i = ((int)blockIdx.x * C::NP + ptid) * 4; i < a.ncopy; i += (int)gridDim.x * C::NP * 4)
+                    *reinterpret_cast<f32x4*>(a.scopy + i) = *reinterpret_cast<const f32x4*>(a.S_in + i);
+        }
         if (!producer && cbusy) {
             zero_acc();
             for (int k = 0; k < nmine; ++k) epilogue(k, load_alpha(k));
@@ -617,6 +691,17 @@ __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
             __syncthreads();
         }
         return;
+    }
+    // one-frame path: copy S_in to the workspace (the state update reads the
+    // copy, so S_out may alias S_in); the consumer waves do it while the
+    // producers fill the pipeline
+    // one-frame path: copy S_in to the workspace (the state update reads the
+    // copy, so S_out may alias S_in); the consumer waves do it while the
+    // producers fill the pipeline
+    if constexpr (PART) {
+        if (a.scopy)
+            for (int i = ((int)blockIdx.x * 512 + tid) * 4; i < a.ncopy; i += (int)gridDim.x * 512 * 4)
+                *reinterpret_cast<f32x4*>(a.scopy + i) = *reinterpret_cast<const f32x4*>(a.S_in + i);
     }
     float al_next = load_alpha(0);
     bool fresh = true;
@@ -1057,6 +1142,291 @@ __global__ __launch_bounds__(256, 2) void frame_output_kernel(ScanArgs a) {
     }
     __syncthreads();
     store_blk(nblk - 1, obase + ((nblk - 1) & 1) * C::OBUF);
+}
+
+// ================================================================== frame_step
+template <typename T, int D> struct StepCfg {
+    static constexpr int SZ = IO<T>::bytes;
+    static constexpr int NW = D / 16;               // waves: one 16-row tile of S each
+    static constexpr int NTH = 64 * NW;
+    static constexpr int KS = (D + 31) / 32;
+    static constexpr int ET = D / 16;               // 16-column tiles of S
+    static constexpr int ROWB = D * SZ + 16;        // padded LDS row (a token, or a row of S)
+    static constexpr int LPR = D * SZ / 16;         // 16-byte loads per token row
+    static constexpr int RPP = NTH / LPR;           // token rows per load pass
+    static constexpr int BT = RPP > 64 ? RPP : 64;  // tokens per LDS block
+    static constexpr int NLD = BT / RPP;            // loads per thread per block
+    static constexpr int PD = SZ == 2 ? 4 : 2;      // blocks of Q in flight
+    static constexpr int QBUF = BT * ROWB;          // one LDS block of Q (and of O)
+    static constexpr int NST = BT * LPR / NTH;      // 16-byte O stores per thread per block
+    static constexpr int NPL = SZ == 2 ? 2 : 1;     // planes of S_1 (bf16 hi, lo)
+    static constexpr int PLANE = D * ROWB;          // one plane of a D x D state
+    static constexpr int LDS_S = (1 + NPL) * PLANE; // S_0 (B operand), then the planes of S_1
+    static constexpr int LDS_O = 4 * QBUF;
+    static constexpr int LDS = LDS_S > LDS_O ? LDS_S : LDS_O;
+    static constexpr int PD0 = D * D / (4 * NTH);   // f32x4 loads per thread to stage S_0
+    static_assert(RPP >= 1 && BT % RPP == 0 && NST * NTH == BT * LPR, "block shape");
+};
+
+// One frame for streaming use, after frame_gram has written the fp32 partial
+// G and U of every token range of every (b, h).  Each workgroup owns one
+// (b, h) and one range of output tokens, and first forms the new state itself,
+//     S_1 = alpha S_0 + U + bf16(S_0) Gm,   Gm = -alpha sum_p G_p,  U = sum_p U_p
+// (the same arithmetic as the recurrence, with the partials summed in fp32 in
+// range order), so the one-frame step needs no recurrence launch: the update
+// is 2*D^3 flops, small next to the output's 2*N*D^2.  As in the recurrence,
+// wave w owns columns [16w, 16w+16) of S_1 and needs only its slice of Gm and
+// U; S_0 is staged once in LDS as the shared operand.  Then O = S_1 Q^T for
+// its tokens as in the output pass, wave w now owning output features
+// [16w, 16w+16) (S_1 as bf16 hi and lo planes, through LDS into A fragments).  The ranges of a unit share blockIdx mod 8 (one XCD), so
+// their reads of S_0 and the partials hit one L2; the first range writes S_1
+// to S_out.  S_0 is read from frame_gram's copy of S_in, so S_out may be S_in.
+template <typename T, int D>
+__global__ __launch_bounds__(64 * (D / 16), 2) void frame_step_kernel(ScanArgs a) {
+    using C = StepCfg<T, D>;
+    using io = IO<T>;
+    using frag = typename io::frag;
+    using PL = PartLayout<D>;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[C::LDS];
+
+    const int units = a.B * a.H;
+    const int x = (int)blockIdx.x, slot = x >> 3;
+    const int part = slot % a.tsplit;
+    const int bh = (slot / a.tsplit) * 8 + (x & 7);
+    if (bh >= units) return;
+    const int h = bh % a.H, b = bh / a.H;
+    const int N = a.N, H = a.H;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = lane & 15, g = lane >> 4;
+    const bool kvalid = 8 * g < D || D >= 32;      // D = 16: lanes g >= 2 carry zeros
+
+    // ---- tokens [nbeg, nend) of this unit's frame
+    // Q streams in from the start (the update below needs none of it); an
+    // empty range gets an empty buffer resource, whose loads return zeros
+    const int nbeg = part * a.tchunk;
+    const int nend = min(N, nbeg + a.tchunk);
+    const size_t rowstride = (size_t)H * D;
+    const size_t tok0 = (size_t)b * a.F * N + (nbeg < nend ? nbeg : 0);
+    const uint32_t rbytes = nbeg < nend ? (uint32_t)(((size_t)(nend - nbeg - 1) * rowstride + D) * C::SZ) : 0u;
+    const rsrc_t rq = make_rsrc(static_cast<const T*>(a.q) + tok0 * rowstride + (size_t)h * D, rbytes);
+    const rsrc_t ro = make_rsrc(static_cast<T*>(a.o) + tok0 * rowstride + (size_t)h * D, rbytes);
+    const uint32_t row_bytes = (uint32_t)(H * D * C::SZ);
+    const int nblk = (nend - nbeg + C::BT - 1) / C::BT;
+    const int lc = tid % C::LPR, lr = tid / C::LPR;
+    struct QStage {
+        u32x4 v[C::NLD];
+    };
+    auto load_blk = [&](int blk, QStage& R) {
+        const uint32_t base = (uint32_t)(blk * C::BT + lr) * row_bytes + (uint32_t)(lc * 16);
+#pragma unroll
+        for (int i = 0; i < C::NLD; ++i) R.v[i] = bload16_nt(rq, base + (uint32_t)(i * C::RPP) * row_bytes);
+    };
+    auto put_blk = [&](const QStage& R, unsigned char* buf) {
+#pragma unroll
+        for (int i = 0; i < C::NLD; ++i)
+            *reinterpret_cast<u32x4*>(buf + (lr + i * C::RPP) * C::ROWB + lc * 16) = R.v[i];
+    };
+    static_assert(C::PD % 2 == 0, "ring slot parity must match the LDS buffer parity");
+    QStage ring[C::PD];
+#pragma unroll
+    for (int j = 0; j < C::PD; ++j) load_blk(j, ring[j]);
+
+    // ---- stage S_0 in LDS as bf16 rows (operand B of the update), and load
+    //      this wave's slices of U and Gm: one batch of independent loads per
+    //      partial
+    float al = a.alpha[(size_t)b * a.F * H + h];
+    if (a.logits) al = sigmoid_f(al);
+    const float* s0 = a.S_in ? a.S_in + (size_t)bh * D * D : nullptr;
+    unsigned char* const sS0 = smem;
+    unsigned char* const sS1 = smem + C::PLANE;     // hi plane, then lo plane
+#pragma unroll
+    for (int i = 0; i < C::PD0; ++i) {
+        const int e4 = (tid + i * C::NTH) * 4, rr = e4 / D, cc = e4 % D;
+        const f32x4 v = s0 ? *reinterpret_cast<const f32x4*>(s0 + e4) : f32x4{0, 0, 0, 0};
+        if constexpr (sizeof(T) == 2)
+            *reinterpret_cast<u32x2*>(sS0 + rr * C::ROWB + cc * 2) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        else
+            *reinterpret_cast<f32x4*>(sS0 + rr * C::ROWB + cc * 4) = v;
+    }
+    // lane (r, g) of row tile i holds S_1[16 i + r][16 wave + 4 g .. + 3]
+    f32x4 sn[C::ET];
+    const int col0 = wave * 16 + 4 * g;
+#pragma unroll
+    for (int i = 0; i < C::ET; ++i)
+        sn[i] = s0 ? *reinterpret_cast<const f32x4*>(s0 + (size_t)(16 * i + r) * D + col0) * al : f32x4{0, 0, 0, 0};
+    const unsigned char* pbase = reinterpret_cast<const unsigned char*>(a.spart) + (size_t)bh * a.parts * PL::bytes;
+    f32x4 glo[C::KS], ghi[C::KS];                   // this wave's Gm^T fragments (fp32 sums)
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+        glo[ks] = f32x4{0, 0, 0, 0};
+        ghi[ks] = f32x4{0, 0, 0, 0};
+    }
+    for (int pp = 0; pp < a.parts; ++pp) {
+        const unsigned char* pg = pbase + (size_t)pp * PL::bytes;
+        f32x4 tl_[C::KS], th_[C::KS], tu[C::ET];
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+            tl_[ks] = *reinterpret_cast<const f32x4*>(pg + PL::g_off + PL::frag_off(wave, ks, 0, lane));
+            th_[ks] = *reinterpret_cast<const f32x4*>(pg + PL::g_off + PL::frag_off(wave, ks, 1, lane));
+        }
+#pragma unroll
+        for (int i = 0; i < C::ET; ++i)              // U tile (e-tile wave, a-tile i)
+            tu[i] = *reinterpret_cast<const f32x4*>(pg + PL::u_off + (size_t)(wave * PL::RT + i) * 1024 + lane * 16);
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+            glo[ks] += tl_[ks];
+            ghi[ks] += th_[ks];
+        }
+#pragma unroll
+        for (int i = 0; i < C::ET; ++i) sn[i] += tu[i];
+    }
+    frag gm[C::KS];                                 // operand A: -alpha times the sums
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+        const f32x4 lo = glo[ks] * (-al), hi = ghi[ks] * (-al);
+        if constexpr (sizeof(T) == 2)
+            gm[ks] = u32x4{pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]), pack_bf16x2(hi[0], hi[1]),
+                           pack_bf16x2(hi[2], hi[3])};
+        else
+            gm[ks] = f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        if (!kvalid) gm[ks] = io::zero();
+    }
+    __syncthreads();                                // S_0 staged
+#pragma unroll
+    for (int i = 0; i < C::ET; ++i) {
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+            const int c0 = (ks * 32 + 8 * g) % D;
+            const unsigned char* src = sS0 + (16 * i + r) * C::ROWB + c0 * C::SZ;
+            frag sb;
+            if constexpr (sizeof(T) == 2) {
+                sb = *reinterpret_cast<const u32x4*>(src);
+            } else {
+                const f32x4 lo = *reinterpret_cast<const f32x4*>(src);
+                const f32x4 hi = *reinterpret_cast<const f32x4*>(src + 16);
+                sb = f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            }
+            if (!kvalid) sb = io::zero();
+            io::mma(sn[i], gm[ks], sb);               // (S_0 Gm)^T += Gm^T S_0^T
+        }
+    }
+
+    // ---- S_out (first range only) and the planes of S_1 in LDS
+    if (part == 0 && a.S_out) {
+#pragma unroll
+        for (int i = 0; i < C::ET; ++i)
+            *reinterpret_cast<f32x4*>(a.S_out + (size_t)bh * D * D + (size_t)(16 * i + r) * D + col0) = sn[i];
+    }
+#pragma unroll
+    for (int i = 0; i < C::ET; ++i) {
+        const int off = (16 * i + r) * C::ROWB + col0 * C::SZ;
+        if constexpr (sizeof(T) == 2) {
+            const f32x4 v = sn[i];
+            const uint32_t h01 = pack_bf16x2(v[0], v[1]), h23 = pack_bf16x2(v[2], v[3]);
+            const uint32_t l01 = pack_bf16x2(v[0] - bf2f(h01 & 0xffffu), v[1] - bf2f(h01 >> 16));
+            const uint32_t l23 = pack_bf16x2(v[2] - bf2f(h23 & 0xffffu), v[3] - bf2f(h23 >> 16));
+            *reinterpret_cast<u32x2*>(sS1 + off) = u32x2{h01, h23};
+            *reinterpret_cast<u32x2*>(sS1 + C::PLANE + off) = u32x2{l01, l23};
+        } else {
+            *reinterpret_cast<f32x4*>(sS1 + off) = sn[i];
+        }
+    }
+    __syncthreads();                                // S_1 planes complete
+    // A fragments of O^T = S_1 Q^T: rows [16 wave, 16 wave + 16) of S_1
+    frag ah[C::KS], alw[C::KS];
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+        const int c0 = (ks * 32 + 8 * g) % D;
+        const unsigned char* src = sS1 + (16 * wave + r) * C::ROWB + c0 * C::SZ;
+        if constexpr (sizeof(T) == 2) {
+            ah[ks] = *reinterpret_cast<const u32x4*>(src);
+            alw[ks] = *reinterpret_cast<const u32x4*>(src + C::PLANE);
+        } else {
+            const f32x4 lo = *reinterpret_cast<const f32x4*>(src);
+            const f32x4 hi = *reinterpret_cast<const f32x4*>(src + 16);
+            ah[ks] = f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+        if (!kvalid) {
+            ah[ks] = io::zero();
+            alw[ks] = io::zero();
+        }
+    }
+    __syncthreads();                                // LDS is reused for Q and O below
+    if (nbeg >= nend) return;
+
+    auto compute_blk = [&](const unsigned char* buf, unsigned char* obuf) {
+#pragma unroll 1
+        for (int sbk = 0; sbk < C::BT / 16; ++sbk) {     // 16-token sub-blocks
+            frag bq[C::KS];
+#pragma unroll
+            for (int ks = 0; ks < C::KS; ++ks) {
+                const int c0 = (ks * 32 + 8 * g) % D;
+                const unsigned char* src = buf + (sbk * 16 + r) * C::ROWB + c0 * C::SZ;
+                if constexpr (sizeof(T) == 2) {
+                    bq[ks] = *reinterpret_cast<const u32x4*>(src);
+                } else {
+                    const f32x4 lo = *reinterpret_cast<const f32x4*>(src);
+                    const f32x4 hi = *reinterpret_cast<const f32x4*>(src + 16);
+                    bq[ks] = f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                }
+                if (!kvalid) bq[ks] = io::zero();
+            }
+            f32x4 acc = f32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int ks = 0; ks < C::KS; ++ks) {
+                io::mma(acc, ah[ks], bq[ks]);
+                if constexpr (sizeof(T) == 2) io::mma(acc, alw[ks], bq[ks]);
+            }
+            unsigned char* orow = obuf + (sbk * 16 + r) * C::ROWB;           // token sbk*16 + r
+            if constexpr (sizeof(T) == 2)
+                *reinterpret_cast<u32x2*>(orow + col0 * 2) =
+                    u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+            else
+                *reinterpret_cast<f32x4*>(orow + col0 * 4) = acc;
+        }
+    };
+    // whole rows of O block `blk` from its LDS tile; block -1 maps past the
+    // resource and is dropped
+    auto store_blk = [&](int blk, const unsigned char* obuf) {
+        const uint32_t base = blk >= 0 ? (uint32_t)(blk * C::BT) * row_bytes : 0x80000000u;
+#pragma unroll
+        for (int i = 0; i < C::NST; ++i) {
+            const int c = tid + C::NTH * i, n = c / C::LPR, pc = c % C::LPR;
+            const u32x4 val = *reinterpret_cast<const u32x4*>(obuf + n * C::ROWB + pc * 16);
+            bstore16(ro, base + (uint32_t)n * row_bytes + (uint32_t)(pc * 16), val);
+        }
+    };
+    // the pipeline of the output pass: ring slot blk % PD, LDS buffer blk & 1,
+    // one barrier per block; block blk-1's O tile is stored after the barrier
+    unsigned char* const obase = smem + 2 * C::QBUF;
+    const int nfull = nblk / C::PD;
+    for (int gi = 0; gi < nfull; ++gi) {
+#pragma unroll
+        for (int j = 0; j < C::PD; ++j) {
+            const int blk = gi * C::PD + j;
+            unsigned char* buf = smem + (j & 1) * C::QBUF;
+            put_blk(ring[j], buf);
+            __syncthreads();
+            store_blk(blk - 1, obase + ((j + 1) & 1) * C::QBUF);
+            load_blk(blk + C::PD, ring[j]);         // past the range: zeros, no traffic
+            compute_blk(buf, obase + (j & 1) * C::QBUF);
+        }
+    }
+    const int rem = nblk - nfull * C::PD;
+#pragma unroll
+    for (int j = 0; j < C::PD; ++j) {
+        if (j < rem) {
+            const int blk = nfull * C::PD + j;
+            unsigned char* buf = smem + (j & 1) * C::QBUF;
+            put_blk(ring[j], buf);
+            __syncthreads();
+            store_blk(blk - 1, obase + ((j + 1) & 1) * C::QBUF);
+            compute_blk(buf, obase + (j & 1) * C::QBUF);
+        }
+    }
+    __syncthreads();
+    store_blk(nblk - 1, obase + ((nblk - 1) & 1) * C::QBUF);
 }
 
 // ================================================================== state_copy

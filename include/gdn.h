@@ -121,12 +121,12 @@ int32_t gdn_version(void);
  * recorded event, then fills, per kernel kind k < GDN_NUM_KERNELS, the summed
  * duration in milliseconds and the number of launches.  Not thread-safe; at
  * most GDN_PROFILE_MAX_LAUNCHES launches are recorded per session. */
-#define GDN_NUM_KERNELS 4
+#define GDN_NUM_KERNELS 5
 #define GDN_PROFILE_MAX_LAUNCHES 65536
 gdn_status gdn_profile_begin(void);
 gdn_status gdn_profile_end(double* total_ms, int64_t* launches);
 /* Name of kernel kind k ("frame_gram", "state_scan", "frame_output",
- * "state_copy"), or NULL when k is out of range. */
+ * "state_copy", "frame_step"), or NULL when k is out of range. */
 const char* gdn_kernel_name(int32_t k);
 
 #ifdef __cplusplus

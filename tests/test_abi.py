@@ -46,9 +46,10 @@ def test_status_strings_and_version(lib):
         assert lib.gdn_status_string(s)
     assert lib.gdn_status_string(99) == b"unknown status"
     assert lib.gdn_version() >= 10000
-    assert [lib.gdn_kernel_name(i) for i in range(4)] == [b"frame_gram", b"state_scan",
-                                                          b"frame_output", b"state_copy"]
-    assert lib.gdn_kernel_name(4) is None and lib.gdn_kernel_name(-1) is None
+    assert [lib.gdn_kernel_name(i) for i in range(5)] == [b"frame_gram", b"state_scan",
+                                                          b"frame_output", b"state_copy",
+                                                          b"frame_step"]
+    assert lib.gdn_kernel_name(5) is None and lib.gdn_kernel_name(-1) is None
 
 
 def desc(B=1, H=2, F=3, N=5, D=16, io=_lib.GDN_BF16, flags=0, eps=1e-6, Dv=None):
@@ -64,6 +65,13 @@ def test_workspace_size(lib):
         per_frames = 2 * 3 * 5 * per_entry * 64 * 64
         assert lib.gdn_workspace_size(ctypes.byref(d)) == \
             (per_frames + 255) // 256 * 256 + 2 * 3 * 64 * 64 * 4
+    # one frame: fp32 partial G and U (8*D*D bytes) per (b, h, token range),
+    # ranges of whole 64-token stages sized for 256 CUs (here 128 units: two
+    # ranges each), rounded to 256 bytes, then a copy of S_in
+    d = desc(B=4, H=32, F=1, N=880, D=64)
+    assert lib.gdn_workspace_size(ctypes.byref(d)) == 4 * 32 * 2 * 8 * 64 * 64 + 4 * 32 * 64 * 64 * 4
+    d = desc(B=1, H=1, F=1, N=880, D=128)          # one unit: ceil(880/64) = 14 ranges
+    assert lib.gdn_workspace_size(ctypes.byref(d)) == 14 * 8 * 128 * 128 + 128 * 128 * 4
     assert lib.gdn_workspace_size(ctypes.byref(desc(D=48))) == 0
     assert lib.gdn_workspace_size(None) == 0
     assert lib.gdn_workspace_size(ctypes.byref(desc(F=0))) == 0
@@ -147,7 +155,7 @@ def test_empty_calls_do_nothing(lib):
 
 def test_profile_session_without_launches(lib):
     assert lib.gdn_profile_begin() == OK
-    ms = (ctypes.c_double * 4)()
-    n = (ctypes.c_int64 * 4)()
+    ms = (ctypes.c_double * 5)()
+    n = (ctypes.c_int64 * 5)()
     assert lib.gdn_profile_end(ms, n) == OK
-    assert list(n) == [0, 0, 0, 0] and list(ms) == [0.0] * 4
+    assert list(n) == [0] * 5 and list(ms) == [0.0] * 5

@@ -206,7 +206,10 @@ def test_guidance_sampled():
 @pytest.mark.slow
 def test_streaming_steps_match_scan_and_oracle():
     """64 calls of the single-frame step carrying fp32 state, against one
-    64-frame scan of the same frames and against the oracle."""
+    64-frame scan of the same frames and against the oracle.  The step runs
+    its own kernels (token-range partials summed in fp32, the state update
+    fused into the output pass), so it matches the scan to rounding, not bit
+    for bit; both must meet the oracle's tolerance."""
     w = inputs.make_config("streaming", seed=0)
     q, k, v, b, a, _ = inputs.to_torch(w, "cuda")
     o_scan, S_scan = api.frame_scan_fwd(q, k, v, b, a, None)
@@ -223,7 +226,9 @@ def test_streaming_steps_match_scan_and_oracle():
     torch.cuda.synchronize()
     diff = (o_steps.float() - o_scan.float()).abs().max().item()
     print("max |step - scan| on O: %g, on S: %g" % (diff, (S - S_scan).abs().max().item()))
-    assert torch.equal(o_steps, o_scan) and torch.equal(S, S_scan)
+    check(o_steps.float().cpu().numpy(), o_scan.float().cpu().numpy(), "bf16", "O steps vs scan")
+    check(S.cpu().numpy(), S_scan.cpu().numpy(), "bf16", "S steps vs scan")
     units = [(0, 0), (3, 31)]
-    o_np = o_steps.float().cpu().numpy()
-    check_units(w, o_np, S.cpu().numpy(), units, oracle_ref(w, units=units))
+    refs = oracle_ref(w, units=units)
+    check_units(w, o_steps.float().cpu().numpy(), S.cpu().numpy(), units, refs)
+    check_units(w, o_scan.float().cpu().numpy(), S_scan.cpu().numpy(), units, refs)
