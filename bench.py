@@ -6,7 +6,8 @@ head and batch item), with inputs already resident in HBM.  Prints one JSON
 line: throughput in tokens/s from a clean timed region of K steps, the
 roofline of the dominant kernel (HIP events recorded by the library around
 every launch in a second timed region of K steps), and the fp64 CPU oracle
-timed on a bounded sample of the same workload.
+timed on a bounded sample of the same workload; also the per-step GPU time of
+gdn_frame_step at the streaming workload's shape.
 
     python bench.py [--steps K] [--warmup W] [--workload full_minute]
 """
@@ -96,6 +97,61 @@ def cpu_baseline(w, budget_s: float):
                       % (fs, w.F, w.B * w.H, w.N, dt)}
 
 
+def streaming_step(frames: int, reps: int = 5):
+    """gdn_frame_step at the streaming workload's shape (B4 H32 d64 N880,
+    bf16, fp32 state carried in place): `frames` consecutive steps captured in
+    one HIP graph and replayed, so the figure is GPU time per step without the
+    Python call overhead.  Inputs are seeded Gaussians drawn on the device in
+    the workload's distributions (timing does not depend on the values)."""
+    import torch
+    from gated_deltanet_scan_amd import api
+    B, H, N, D = 4, 32, 880, 64
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    mk = lambda *sh: torch.randn(*sh, device="cuda", generator=g)
+    q = [mk(B, N, H, D).bfloat16() for _ in range(frames)]
+    k = []
+    for _ in range(frames):
+        kk = mk(B, N, H, D)
+        k.append((kk / kk.norm(dim=-1, keepdim=True)).bfloat16())
+    v = [mk(B, N, H, D).bfloat16() for _ in range(frames)]
+    beta = [torch.sigmoid(mk(B, N, H)) / N for _ in range(frames)]
+    alpha = [torch.sigmoid(mk(B, H) + 3.0) for _ in range(frames)]
+    o = [torch.empty_like(q[0]) for _ in range(frames)]
+    S = torch.zeros((B, H, D, D), dtype=torch.float32, device="cuda")
+    desc = api.make_desc(B, H, 1, N, D, torch.bfloat16)
+    ws = api.alloc_workspace(desc, q[0].device)
+    cs = torch.cuda.Stream()
+
+    def run():
+        for f in range(frames):
+            api.frame_step(q[f], k[f], v[f], beta[f], alpha[f], S, o=o[f], S_out=S, workspace=ws, stream=cs)
+    with torch.cuda.stream(cs):
+        run()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=cs):
+            run()
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / (reps * frames) * 1e3
+    # q, k, v read and o written (bf16), beta and alpha read, S read and written
+    nbytes = B * N * H * D * 2 * 4 + B * N * H * 4 + B * H * 4 + 2 * B * H * D * D * 4
+    return {"workload": "streaming (B4 H32 d64 N880, one frame per gdn_frame_step)", "us_per_step": round(us, 2),
+            "frames_timed": frames * reps, "alg_bytes_per_step": nbytes,
+            "hbm_gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "timing": "HIP graph of %d consecutive steps, replayed %d times" % (frames, reps)}
+
+
 def copy_calibration(nbytes: int, steps: int):
     """A plain device copy of known size, for scaling rocprofv3 byte counters."""
     import torch
@@ -116,6 +172,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0: skip)")
+    ap.add_argument("--stream-frames", type=int, default=16,
+                    help="frames of the streaming-step measurement (0: skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES bytes --steps times")
     args = ap.parse_args()
@@ -223,6 +281,7 @@ def main():
                          "(%.5f ms per step with the events)" % (args.steps, prof_ms / args.steps),
         "kernel_src": src_hash,
     }
+    line["streaming_step"] = streaming_step(args.stream_frames) if args.stream_frames > 0 else None
     if args.cpu_budget > 0:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
     else:

@@ -696,12 +696,16 @@ __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
     // copy, so S_out may alias S_in); the consumer waves do it while the
     // producers fill the pipeline
     // one-frame path: copy S_in to the workspace (the state update reads the
-    // copy, so S_out may alias S_in); the consumer waves do it while the
-    // producers fill the pipeline
-    if constexpr (PART) {
-        if (a.scopy)
-            for (int i = ((int)blockIdx.x * 512 + tid) * 4; i < a.ncopy; i += (int)gridDim.x * 512 * 4)
-                *reinterpret_cast<f32x4*>(a.scopy + i) = *reinterpret_cast<const f32x4*>(a.S_in + i);
+    // copy, so S_out may alias S_in).  Each consumer thread loads its first
+    // 16-byte piece before the pipeline and stores it after, so nothing waits
+    // on the load (at D = 128 the accumulators leave no register for it, and
+    // the whole copy follows the pipeline); further pieces (many (b, h) units
+    // of large D) are copied after the pipeline.
+    constexpr bool kCopyAhead = PART && D < 128;
+    const int cbase = ((int)blockIdx.x * 512 + tid) * 4, cstride = (int)gridDim.x * 512 * 4;
+    f32x4 cp0 = f32x4{0, 0, 0, 0};
+    if constexpr (kCopyAhead) {
+        if (a.scopy && cbase < a.ncopy) cp0 = *reinterpret_cast<const f32x4*>(a.S_in + cbase);
     }
     float al_next = load_alpha(0);
     bool fresh = true;
@@ -719,6 +723,17 @@ __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
             }
         }
         __syncthreads();
+    }
+    if constexpr (PART) {
+        if (a.scopy) {
+            int i0 = cbase;
+            if constexpr (kCopyAhead) {
+                if (cbase < a.ncopy) *reinterpret_cast<f32x4*>(a.scopy + cbase) = cp0;
+                i0 += cstride;
+            }
+            for (int i = i0; i < a.ncopy; i += cstride)
+                *reinterpret_cast<f32x4*>(a.scopy + i) = *reinterpret_cast<const f32x4*>(a.S_in + i);
+        }
     }
 }
 
@@ -1165,6 +1180,7 @@ template <typename T, int D> struct StepCfg {
     static constexpr int LDS_O = 4 * QBUF;
     static constexpr int LDS = LDS_S > LDS_O ? LDS_S : LDS_O;
     static constexpr int PD0 = D * D / (4 * NTH);   // f32x4 loads per thread to stage S_0
+    static constexpr int PP = D >= 128 ? 1 : 2;     // partials loaded per batch (registers)
     static_assert(RPP >= 1 && BT % RPP == 0 && NST * NTH == BT * LPR, "block shape");
 };
 
@@ -1202,8 +1218,9 @@ __global__ __launch_bounds__(64 * (D / 16), 2) void frame_step_kernel(ScanArgs a
     const bool kvalid = 8 * g < D || D >= 32;      // D = 16: lanes g >= 2 carry zeros
 
     // ---- tokens [nbeg, nend) of this unit's frame
-    // Q streams in from the start (the update below needs none of it); an
-    // empty range gets an empty buffer resource, whose loads return zeros
+    // Q streams in during the state update (it needs none of Q), issued just
+    // after the first partials so that those come back first; an empty range
+    // gets an empty buffer resource, whose loads return zeros
     const int nbeg = part * a.tchunk;
     const int nend = min(N, nbeg + a.tchunk);
     const size_t rowstride = (size_t)H * D;
@@ -1229,8 +1246,6 @@ __global__ __launch_bounds__(64 * (D / 16), 2) void frame_step_kernel(ScanArgs a
     };
     static_assert(C::PD % 2 == 0, "ring slot parity must match the LDS buffer parity");
     QStage ring[C::PD];
-#pragma unroll
-    for (int j = 0; j < C::PD; ++j) load_blk(j, ring[j]);
 
     // ---- stage S_0 in LDS as bf16 rows (operand B of the update), and load
     //      this wave's slices of U and Gm: one batch of independent loads per
@@ -1240,47 +1255,79 @@ __global__ __launch_bounds__(64 * (D / 16), 2) void frame_step_kernel(ScanArgs a
     const float* s0 = a.S_in ? a.S_in + (size_t)bh * D * D : nullptr;
     unsigned char* const sS0 = smem;
     unsigned char* const sS1 = smem + C::PLANE;     // hi plane, then lo plane
-#pragma unroll
-    for (int i = 0; i < C::PD0; ++i) {
-        const int e4 = (tid + i * C::NTH) * 4, rr = e4 / D, cc = e4 % D;
-        const f32x4 v = s0 ? *reinterpret_cast<const f32x4*>(s0 + e4) : f32x4{0, 0, 0, 0};
-        if constexpr (sizeof(T) == 2)
-            *reinterpret_cast<u32x2*>(sS0 + rr * C::ROWB + cc * 2) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-        else
-            *reinterpret_cast<f32x4*>(sS0 + rr * C::ROWB + cc * 4) = v;
-    }
-    // lane (r, g) of row tile i holds S_1[16 i + r][16 wave + 4 g .. + 3]
-    f32x4 sn[C::ET];
-    const int col0 = wave * 16 + 4 * g;
-#pragma unroll
-    for (int i = 0; i < C::ET; ++i)
-        sn[i] = s0 ? *reinterpret_cast<const f32x4*>(s0 + (size_t)(16 * i + r) * D + col0) * al : f32x4{0, 0, 0, 0};
-    const unsigned char* pbase = reinterpret_cast<const unsigned char*>(a.spart) + (size_t)bh * a.parts * PL::bytes;
-    f32x4 glo[C::KS], ghi[C::KS];                   // this wave's Gm^T fragments (fp32 sums)
+    // every load first (S_0 for LDS, S_0 and U in this wave's slice, this
+    // wave's Gm^T fragments), so that one round trip covers them: partials
+    // come PP at a time through a buffer resource that ends at the last one,
+    // so those of a batch past the end read zeros
+    const rsrc_t rp = make_rsrc(reinterpret_cast<const unsigned char*>(a.spart) + (size_t)bh * a.parts * PL::bytes,
+                                (uint32_t)(a.parts * PL::bytes));
+    f32x4 glo[C::KS], ghi[C::KS], su[C::ET];        // sums: this wave's Gm^T fragments, U slice
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
         glo[ks] = f32x4{0, 0, 0, 0};
         ghi[ks] = f32x4{0, 0, 0, 0};
     }
-    for (int pp = 0; pp < a.parts; ++pp) {
-        const unsigned char* pg = pbase + (size_t)pp * PL::bytes;
-        f32x4 tl_[C::KS], th_[C::KS], tu[C::ET];
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
-            tl_[ks] = *reinterpret_cast<const f32x4*>(pg + PL::g_off + PL::frag_off(wave, ks, 0, lane));
-            th_[ks] = *reinterpret_cast<const f32x4*>(pg + PL::g_off + PL::frag_off(wave, ks, 1, lane));
+    for (int i = 0; i < C::ET; ++i) su[i] = f32x4{0, 0, 0, 0};
+    f32x4 st0[C::PD0];
+#pragma unroll
+    for (int i = 0; i < C::PD0; ++i)
+        st0[i] = s0 ? *reinterpret_cast<const f32x4*>(s0 + (tid + i * C::NTH) * 4) : f32x4{0, 0, 0, 0};
+    f32x4 sn[C::ET];                                // lane (r, g) of row tile i: S_1[16 i + r][16 wave + 4 g ..]
+    const int col0 = wave * 16 + 4 * g;
+#pragma unroll
+    for (int i = 0; i < C::ET; ++i)
+        sn[i] = s0 ? *reinterpret_cast<const f32x4*>(s0 + (size_t)(16 * i + r) * D + col0) : f32x4{0, 0, 0, 0};
+    // one batch of PP partials: loads, then sums
+    auto load_batch = [&](int pp, f32x4 (&tg)[C::PP][2 * C::KS], f32x4 (&tu)[C::PP][C::ET]) {
+#pragma unroll
+        for (int q2 = 0; q2 < C::PP; ++q2) {
+            const uint32_t pb = (uint32_t)((pp + q2) * PL::bytes);
+#pragma unroll
+            for (int ks = 0; ks < C::KS; ++ks) {
+                tg[q2][2 * ks] = __builtin_bit_cast(f32x4, bload16(rp, pb + PL::g_off + PL::frag_off(wave, ks, 0, lane)));
+                tg[q2][2 * ks + 1] = __builtin_bit_cast(f32x4, bload16(rp, pb + PL::g_off + PL::frag_off(wave, ks, 1, lane)));
+            }
+#pragma unroll
+            for (int i = 0; i < C::ET; ++i)          // U tile (e-tile wave, a-tile i)
+                tu[q2][i] = __builtin_bit_cast(f32x4, bload16(rp, pb + (uint32_t)(PL::u_off + (wave * PL::RT + i) * 1024 + lane * 16)));
         }
+    };
+    auto add_batch = [&](const f32x4 (&tg)[C::PP][2 * C::KS], const f32x4 (&tu)[C::PP][C::ET]) {
 #pragma unroll
-        for (int i = 0; i < C::ET; ++i)              // U tile (e-tile wave, a-tile i)
-            tu[i] = *reinterpret_cast<const f32x4*>(pg + PL::u_off + (size_t)(wave * PL::RT + i) * 1024 + lane * 16);
+        for (int q2 = 0; q2 < C::PP; ++q2) {
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
-            glo[ks] += tl_[ks];
-            ghi[ks] += th_[ks];
+            for (int ks = 0; ks < C::KS; ++ks) {
+                glo[ks] += tg[q2][2 * ks];
+                ghi[ks] += tg[q2][2 * ks + 1];
+            }
+#pragma unroll
+            for (int i = 0; i < C::ET; ++i) su[i] += tu[q2][i];
         }
+    };
+    {
+        f32x4 tg[C::PP][2 * C::KS], tu[C::PP][C::ET];
+        load_batch(0, tg, tu);
 #pragma unroll
-        for (int i = 0; i < C::ET; ++i) sn[i] += tu[i];
+        for (int j = 0; j < C::PD; ++j) load_blk(j, ring[j]);
+        add_batch(tg, tu);
     }
+    for (int pp = C::PP; pp < a.parts; pp += C::PP) {
+        f32x4 tg[C::PP][2 * C::KS], tu[C::PP][C::ET];
+        load_batch(pp, tg, tu);
+        add_batch(tg, tu);
+    }
+#pragma unroll
+    for (int i = 0; i < C::PD0; ++i) {
+        const int e4 = (tid + i * C::NTH) * 4, rr = e4 / D, cc = e4 % D;
+        const f32x4 v = st0[i];
+        if constexpr (sizeof(T) == 2)
+            *reinterpret_cast<u32x2*>(sS0 + rr * C::ROWB + cc * 2) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        else
+            *reinterpret_cast<f32x4*>(sS0 + rr * C::ROWB + cc * 4) = v;
+    }
+#pragma unroll
+    for (int i = 0; i < C::ET; ++i) sn[i] = sn[i] * al + su[i];
     frag gm[C::KS];                                 // operand A: -alpha times the sums
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
