@@ -748,9 +748,11 @@ template <typename T, int D> struct StateCfg {
     static constexpr int ROWB = D * IO<T>::bytes + PADB;
     static constexpr int NPL = sizeof(T) == 2 ? 2 : 1;  // planes (hi, lo) of S in LDS
     // frames of operands in flight: the ring must fit the 6-bit vector-memory
-    // counter (63 outstanding loads and stores per wave) or every frame drains it
-    static constexpr int LOADS = KS + RTW;
-    static constexpr int PD = (48 / LOADS) < 4 ? (48 / LOADS) : 4;
+    // counter (63 outstanding loads and stores per wave) or every frame drains
+    // it, and the register file (fp32 fragments are twice as wide)
+    static constexpr int LOADS = KS * (sizeof(T) == 2 ? 1 : 2) + RTW;
+    static constexpr int PDMAX = sizeof(T) == 2 ? 8 : 4;
+    static constexpr int PD = (48 / LOADS) < PDMAX ? (48 / LOADS) : PDMAX;
     static_assert(PD >= 2, "ring too shallow");
 };
 
@@ -773,9 +775,10 @@ template <typename T, int D> struct StateCfg {
 // as the A operand (one barrier per frame), and the previous frame's planes
 // are copied to the workspace for frame_output while this frame's MFMAs run.
 // Every workgroup of a head reads all of Gm_f (32 KiB in bf16) each
-// frame; the per-CU rate of those L2 reads, not the MFMAs, bounds this kernel
-// (about 1.5 us per frame at D = 128), so more rows per workgroup do not help.
-// The operands of the next PD frames are in flight in a register ring.
+// frame, mostly from L2.  A frame takes about 0.55 us at D = 128 (bf16); the
+// operands of the next PD frames are in flight in a register ring, deep
+// enough that frames whose workspace has left the last-level cache do not
+// stall (with 4 frames in flight those ran at about 1.2 us).
 template <typename T, int D>
 __global__ __launch_bounds__(4 * D, 1) void state_scan_kernel(ScanArgs a) {  // NW*64 threads
     using C = StateCfg<T, D>;
