@@ -66,6 +66,40 @@ __device__ __forceinline__ float group_sum(float x) {
 __device__ __forceinline__ uint32_t pack_bf16x2(float x, float y) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x, y}, bf16x2));
 }
+// Remainder code of x against its bf16 rounding h (bits in the low half of
+// hb): x - h is at most half a bf16 ulp, 2^(E-134) for h's biased exponent E;
+// the code counts it in 1/256 ulps, rounded to nearest and clamped to int8.
+// h plus rem_value(code) carries x to about 2^-16 relative, in 3 bytes.
+__device__ __forceinline__ int rem_code(float x, uint32_t hb) {
+    const int e = (int)((hb >> 7) & 0xffu);
+    const float t = __builtin_rintf(__builtin_amdgcn_ldexpf(x - bf2f((uint16_t)hb), 142 - e));
+    return (int)__builtin_fminf(__builtin_fmaxf(t, -127.0f), 127.0f);
+}
+__device__ __forceinline__ float rem_value(int code, uint32_t hb) {
+    return __builtin_amdgcn_ldexpf((float)code, (int)((hb >> 7) & 0xffu) - 142);
+}
+// byte i (signed) of a dword of codes
+__device__ __forceinline__ int code_at(uint32_t w, int i) { return (int)(w << (24 - 8 * i)) >> 24; }
+__device__ __forceinline__ uint32_t pack_codes(int c0, int c1, int c2, int c3) {
+    return (uint32_t)(c0 & 0xff) | (uint32_t)(c1 & 0xff) << 8 | (uint32_t)(c2 & 0xff) << 16 | (uint32_t)c3 << 24;
+}
+// The remainders of an 8-value bf16 fragment as a bf16 fragment (exact: a
+// code times a power of two has at most 8 significant bits).
+__device__ __forceinline__ u32x4 rem_frag(u32x4 h, u32x2 c) {
+    u32x4 out;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t w = c[j >> 1];
+        out[j] = pack_bf16x2(rem_value(code_at(w, 2 * (j & 1)), h[j] & 0xffffu),
+                             rem_value(code_at(w, 2 * (j & 1) + 1), h[j] >> 16));
+    }
+    return out;
+}
+// Codes of four fp32 values against their bf16 pair dwords h01, h23.
+__device__ __forceinline__ uint32_t codes4(f32x4 x, uint32_t h01, uint32_t h23) {
+    return pack_codes(rem_code(x[0], h01 & 0xffffu), rem_code(x[1], h01 >> 16), rem_code(x[2], h23 & 0xffffu),
+                      rem_code(x[3], h23 >> 16));
+}
 // Frames per state_scan launch (alpha values are staged in LDS).
 constexpr int kMaxChunkFrames = 256;
 
@@ -166,29 +200,39 @@ template <> struct IO<float> {
 //   U      tiles in the state's register layout in state_scan: block (e-tile,
 //          a-tile) holds, in lane 16g+r, U[16a_t + r][16e_t + 4g + t] for
 //          t = 0..3 (fp32)
-//   S_f    operand of frame_output: rows a, contraction e (bf16 mode: the hi
-//          plane, then the lo plane S - hi; fp32 mode: one fp32 plane)
+//   S_f    operand of frame_output: rows a, contraction e (bf16 mode: the bf16
+//          plane, then its remainder codes (rem_code), 8 bytes per lane slot:
+//          three bytes per value at about 2^-16 relative precision; fp32
+//          mode: one fp32 plane)
 template <typename T, int D> struct WS {
+    static constexpr bool B16 = sizeof(T) == 2;
     static constexpr int KS = (D + 31) / 32;                  // contraction fragments per tile
     static constexpr int RT = D / 16;                         // 16-row tiles
-    static constexpr int NPL = sizeof(T) == 2 ? 2 : 1;        // planes per operand (hi, lo)
-    static constexpr size_t FRAG = sizeof(T) == 2 ? 1024 : 2048;
+    static constexpr size_t FRAG = B16 ? 1024 : 2048;
     static constexpr size_t OPND = (size_t)RT * KS * FRAG;    // one operand plane
     static constexpr size_t gm_off = 0;
     static constexpr size_t ut_off = OPND;
     static constexpr size_t sp_off = ut_off + (size_t)RT * RT * 1024;
-    static constexpr size_t item_bytes = sp_off + NPL * OPND;
+    static constexpr size_t sc_rel = OPND;                    // S codes, after the S plane (bf16)
+    // bf16: the codes take half a plane; the item keeps a whole one, which
+    // measured ~10 us faster for state_scan at the full-minute shape than
+    // items 16 KiB smaller (the per-head stride of its stores)
+    static constexpr size_t item_bytes = sp_off + (B16 ? 2 : 1) * OPND;
     // byte offset of lane `lane`'s slot in operand fragment (tile, kt), half h (fp32)
     __device__ static __forceinline__ uint32_t frag_off(int tile, int kt, int h, int lane) {
         return (uint32_t)((tile * KS + kt) * FRAG) + (uint32_t)(h * 1024 + lane * 16);
+    }
+    // the same slot's 8 remainder codes in the code plane of S_f (bf16)
+    __device__ static __forceinline__ uint32_t code_off(int tile, int kt, int lane) {
+        return (uint32_t)((tile * KS + kt) * 512) + (uint32_t)(lane * 8);
     }
 };
 
 // Host-side copy of the per-item workspace size (must match WS<T, D>).
 constexpr size_t ws_item_bytes(int esz, int D) {
-    const size_t KS = (size_t)(D + 31) / 32, RT = (size_t)D / 16, NPL = esz == 2 ? 2 : 1;
+    const size_t KS = (size_t)(D + 31) / 32, RT = (size_t)D / 16;
     const size_t opnd = RT * KS * (esz == 2 ? 1024 : 2048);
-    return (1 + NPL) * opnd + RT * RT * 1024;
+    return (esz == 2 ? 3 : 2) * opnd + RT * RT * 1024;
 }
 static_assert(ws_item_bytes(2, 16) == WS<uint16_t, 16>::item_bytes && ws_item_bytes(2, 128) == WS<uint16_t, 128>::item_bytes &&
                   ws_item_bytes(4, 16) == WS<float, 16>::item_bytes && ws_item_bytes(4, 64) == WS<float, 64>::item_bytes,
@@ -746,11 +790,10 @@ template <typename T, int D> struct StateCfg {
     static constexpr int KS = (D + 31) / 32;            // 32-wide contraction steps
     static constexpr int PADB = 16;                     // LDS row padding (bytes)
     static constexpr int ROWB = D * IO<T>::bytes + PADB;
-    static constexpr int NPL = sizeof(T) == 2 ? 2 : 1;  // planes (hi, lo) of S in LDS
     // frames of operands in flight: the ring must fit the 6-bit vector-memory
     // counter (63 outstanding loads and stores per wave) or every frame drains
     // it, and the register file (fp32 fragments are twice as wide)
-    static constexpr int LOADS = KS * (sizeof(T) == 2 ? 1 : 2) + RTW;
+    static constexpr int LOADS = (sizeof(T) == 2 ? KS : 2 * KS) + RTW;   // per frame
     static constexpr int PDMAX = sizeof(T) == 2 ? 8 : 4;
     static constexpr int PD = (48 / LOADS) < PDMAX ? (48 / LOADS) : PDMAX;
     static_assert(PD >= 2, "ring too shallow");
@@ -786,7 +829,7 @@ __global__ __launch_bounds__(4 * D, 1) void state_scan_kernel(ScanArgs a) {  // 
     using frag = typename io::frag;
     constexpr int ROWS = 16 * C::RTW;
     constexpr int PLANE = ROWS * C::ROWB;
-    __shared__ __attribute__((aligned(16))) unsigned char sS[2][C::NPL][PLANE];
+    __shared__ __attribute__((aligned(16))) unsigned char sS[2][PLANE];
     __shared__ float sAlpha[kMaxChunkFrames];
 
     const int units = a.B * a.H;
@@ -818,15 +861,10 @@ __global__ __launch_bounds__(4 * D, 1) void state_scan_kernel(ScanArgs a) {  // 
 #pragma unroll
         for (int i = 0; i < C::RTW; ++i) {
             const int off = (16 * i + r) * C::ROWB + col0 * io::bytes;
-            if constexpr (sizeof(T) == 2) {
-                const uint32_t h01 = pack_bf16x2(S[i][0], S[i][1]), h23 = pack_bf16x2(S[i][2], S[i][3]);
-                const uint32_t l01 = pack_bf16x2(S[i][0] - bf2f(h01 & 0xffffu), S[i][1] - bf2f(h01 >> 16));
-                const uint32_t l23 = pack_bf16x2(S[i][2] - bf2f(h23 & 0xffffu), S[i][3] - bf2f(h23 >> 16));
-                *reinterpret_cast<u32x2*>(&sS[buf][0][off]) = u32x2{h01, h23};
-                *reinterpret_cast<u32x2*>(&sS[buf][1][off]) = u32x2{l01, l23};
-            } else {
-                *reinterpret_cast<f32x4*>(&sS[buf][0][off]) = S[i];
-            }
+            if constexpr (sizeof(T) == 2)
+                *reinterpret_cast<u32x2*>(&sS[buf][off]) = u32x2{pack_bf16x2(S[i][0], S[i][1]), pack_bf16x2(S[i][2], S[i][3])};
+            else
+                *reinterpret_cast<f32x4*>(&sS[buf][off]) = S[i];
         }
     };
     put_lds(0);
@@ -863,10 +901,10 @@ __global__ __launch_bounds__(4 * D, 1) void state_scan_kernel(ScanArgs a) {  // 
     // is dropped, so the copy needs no branch.
     const rsrc_t rsp = make_rsrc(a.ws + item0 * W::item_bytes, (uint32_t)(Fc * W::item_bytes));
     constexpr int NH = sizeof(T) == 2 ? 1 : 2;          // 16-byte halves per lane slot
-    constexpr int SLOTS = C::NPL * C::RTW * C::KS * NH * 64;   // 16-byte slots per frame
+    constexpr int SLOTS = C::RTW * C::KS * NH * 64;     // 16-byte lane slots per frame
     auto copy_planes = [&](int fl, int buf) {           // S_fl, held in sS[buf], to frame fl
-        // frame -1 maps to 2 GiB: past the resource (at most 256 frames of
-        // 192 KiB) with no 32-bit overflow once the plane offset is added
+        // frame -1 maps to 2 GiB: past the resource (at most 256 frames of at
+        // most 192 KiB) with no 32-bit overflow once the plane offset is added
         const uint32_t base = fl >= 0 ? (uint32_t)fl * (uint32_t)W::item_bytes + (uint32_t)W::sp_off
                                       : 0x80000000u;
 #pragma unroll
@@ -874,12 +912,30 @@ __global__ __launch_bounds__(4 * D, 1) void state_scan_kernel(ScanArgs a) {  // 
             const int x = x0 + tid;
             if (SLOTS % (C::NW * 64) == 0 || x < SLOTS) {
                 const int l = x & 63, hh = (x >> 6) % NH, kt = (x / (64 * NH)) % C::KS;
-                const int i = (x / (64 * NH * C::KS)) % C::RTW, pl = x / (64 * NH * C::KS * C::RTW);
+                const int i = (x / (64 * NH * C::KS)) % C::RTW;
                 const int c0 = (kt * 32 + 8 * (l >> 4) + 4 * hh) % D;   // D = 16: upper lanes repeat
                 const u32x4 val =
-                    *reinterpret_cast<const u32x4*>(&sS[buf][pl][(16 * i + (l & 15)) * C::ROWB + c0 * io::bytes]);
-                __builtin_amdgcn_raw_buffer_store_b128(
-                    val, rsp, base + (uint32_t)(pl * W::OPND) + W::frag_off(rg * C::RTW + i, kt, hh, l), 0, kStreamStore);
+                    *reinterpret_cast<const u32x4*>(&sS[buf][(16 * i + (l & 15)) * C::ROWB + c0 * io::bytes]);
+                __builtin_amdgcn_raw_buffer_store_b128(val, rsp, base + W::frag_off(rg * C::RTW + i, kt, hh, l), 0,
+                                                       kStreamStore);
+            }
+        }
+    };
+    // bf16: the remainder codes of S_fl, straight from this lane's registers
+    // (four consecutive columns of one row: half of an 8-code slot), issued
+    // while the next frame's MFMAs run, so the encoding is off the frame's
+    // critical path and needs no LDS
+    auto store_codes = [&](int fl) {
+        if constexpr (sizeof(T) == 2) {
+            const uint32_t base = fl >= 0 ? (uint32_t)fl * (uint32_t)W::item_bytes + (uint32_t)(W::sp_off + W::sc_rel)
+                                          : 0x80000000u;
+#pragma unroll
+            for (int i = 0; i < C::RTW; ++i) {
+                const uint32_t h01 = pack_bf16x2(S[i][0], S[i][1]), h23 = pack_bf16x2(S[i][2], S[i][3]);
+                const int kt = col0 / 32, slot = 16 * ((col0 % 32) / 8) + r;
+                __builtin_amdgcn_raw_buffer_store_b32(
+                    codes4(S[i], h01, h23), rsp,
+                    base + W::code_off(rg * C::RTW + i, kt, slot) + (uint32_t)(4 * ((col0 / 4) & 1)), 0, kStreamStore);
             }
         }
     };
@@ -909,15 +965,16 @@ __global__ __launch_bounds__(4 * D, 1) void state_scan_kernel(ScanArgs a) {  // 
                 const int ro = (16 * i + r) * C::ROWB;
                 frag ahi;
                 if constexpr (sizeof(T) == 2)
-                    ahi = *reinterpret_cast<const u32x4*>(&sS[cur][0][ro + c0 * 2]);
+                    ahi = *reinterpret_cast<const u32x4*>(&sS[cur][ro + c0 * 2]);
                 else
-                    ahi = io::load(reinterpret_cast<const float*>(&sS[cur][0][ro + c0 * 4]));
+                    ahi = io::load(reinterpret_cast<const float*>(&sS[cur][ro + c0 * 4]));
                 if (!kvalid) ahi = io::zero();
                 io::mma(acc[ks][i], bhi, ahi);             // (S Gm)^T += Gm^T S^T
             }
         }
         if (reload) load_ops(nx, o);
         copy_planes(fl - 1, cur);                       // S_{fl-1}: overlaps the MFMAs
+        store_codes(fl - 1);                            // (S still holds S_{fl-1})
 #pragma unroll
         for (int i = 0; i < C::RTW; ++i) {
             f32x4 t = acc[0][i];
@@ -947,6 +1004,7 @@ __global__ __launch_bounds__(4 * D, 1) void state_scan_kernel(ScanArgs a) {  // 
     for (int j = 0; j < C::PD; ++j)
         if (j < rem) step(nfull * C::PD + j, ring[j], 0, false);
     copy_planes(Fc - 1, Fc & 1);                        // the last frame's S planes
+    store_codes(Fc - 1);
 
     // ---- final state (fp32, row-major [a][e])
 #pragma unroll
@@ -1055,7 +1113,7 @@ __global__ __launch_bounds__(256, 2) void frame_output_kernel(ScanArgs a) {
         for (int ks = 0; ks < C::KS; ++ks) {
             if constexpr (sizeof(T) == 2) {
                 ah[i][ks] = *reinterpret_cast<const u32x4*>(sp + W::frag_off(rt, ks, 0, lane));
-                alw[i][ks] = *reinterpret_cast<const u32x4*>(sp + W::OPND + W::frag_off(rt, ks, 0, lane));
+                alw[i][ks] = rem_frag(ah[i][ks], *reinterpret_cast<const u32x2*>(sp + W::sc_rel + W::code_off(rt, ks, lane)));
             } else {
                 const f32x4 lo = *reinterpret_cast<const f32x4*>(sp + W::frag_off(rt, ks, 0, lane));
                 const f32x4 hi = *reinterpret_cast<const f32x4*>(sp + W::frag_off(rt, ks, 1, lane));

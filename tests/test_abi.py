@@ -57,9 +57,10 @@ def desc(B=1, H=2, F=3, N=5, D=16, io=_lib.GDN_BF16, flags=0, eps=1e-6, Dv=None)
 
 
 def test_workspace_size(lib):
-    # per (b, h, frame): Gm, U and the state planes for frame_output (bf16:
-    # 2 + 4 + 2*2 bytes per matrix entry; fp32: 4 + 4 + 4), rounded to 256
-    # bytes, then one fp32 carry state per (b, h)
+    # per (b, h, frame): Gm, U and the state S_f for frame_output (bf16:
+    # 2 + 4 + 4 bytes per matrix entry, S_f as bf16 plus a one-byte remainder
+    # code in room for two; fp32: 4 + 4 + 4), rounded to 256 bytes, then one
+    # fp32 carry state per (b, h)
     for io, per_entry in ((_lib.GDN_BF16, 10), (_lib.GDN_F32, 12)):
         d = desc(B=2, H=3, F=5, N=7, D=64, io=io)
         per_frames = 2 * 3 * 5 * per_entry * 64 * 64
