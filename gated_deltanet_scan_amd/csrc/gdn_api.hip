@@ -191,8 +191,11 @@ gdn_status launch_output(ScanArgs a, hipStream_t stream, int cus) {
     tsplit = (a.N + tchunk - 1) / tchunk;
     a.tsplit = tsplit;
     a.tchunk = tchunk;
+    // the last quarter of the workgroups, at most one per CU, run as halves
+    const int units = items * tsplit, c = cus > 0 ? cus : 256;
+    a.ntail = units / 4 < c ? units / 4 : c;
     ProfScope ps(K_OUTPUT, stream);
-    hipLaunchKernelGGL((gdn::frame_output_kernel<T, D>), dim3(items * tsplit), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((gdn::frame_output_kernel<T, D>), dim3(units + a.ntail), dim3(256), 0, stream, a);
     return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 
@@ -374,6 +377,7 @@ gdn_status run(const gdn_desc* d, bool step, const void* q, const void* k, const
     a.eps = d->eps;
     a.tsplit = 1;
     a.tchunk = 16;
+    a.ntail = 0;
     a.wsFc = p.Fc;
     a.fsub0 = 0;
     a.tok_bytes = d->N > 0 ? (uint32_t)(((size_t)(d->N - 1) * d->H * p.D + p.D) * p.esz) : 0u;

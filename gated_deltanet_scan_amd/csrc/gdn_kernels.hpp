@@ -255,6 +255,8 @@ struct ScanArgs {
                           // of them this launch covers (frame_gram: 0)
     int tsplit;           // token ranges per frame in frame_output
     int tchunk;           // tokens per range (multiple of 16)
+    int ntail;            // frame_output: the last ntail (frame, range) items run
+                          // as two workgroups of half the tokens each
     uint32_t tok_bytes;   // bytes from a head's first token row of a frame to the
                           // end of its last row: (N-1)*H*D*esz + D*esz (0 if N == 0)
     int logits;
@@ -1058,7 +1060,14 @@ __global__ __launch_bounds__(256, 2) void frame_output_kernel(ScanArgs a) {
     // workgroups are dealt to the XCDs round-robin, and without the rotation
     // each XCD would only ever get the same two heads (whose rows sit at
     // fixed offsets of every token row)
-    const int x = blockIdx.x;
+    // The last ntail items are split in two halves of their tokens, dispatched
+    // last: the final, partial round of workgroups then holds half-size work.
+    int x = blockIdx.x, half = -1;
+    const int nwhole = a.B * a.Fc * a.H * a.tsplit - a.ntail;
+    if (x >= nwhole) {
+        half = (x - nwhole) & 1;
+        x = nwhole + ((x - nwhole) >> 1);
+    }
     const int h = (x % a.H + x / a.H) % a.H;
     const int part = (x / a.H) % a.tsplit;
     const int fl = (x / (a.H * a.tsplit)) % a.Fc;
@@ -1070,8 +1079,15 @@ __global__ __launch_bounds__(256, 2) void frame_output_kernel(ScanArgs a) {
     const int r = lane & 15, g = lane >> 4;
     const int wr = wave % C::NWR, wt = wave / C::NWR;
 
-    const int nbeg = part * a.tchunk;
-    const int nend = min(N, nbeg + a.tchunk);
+    int nbeg = part * a.tchunk;
+    int nend = min(N, nbeg + a.tchunk);
+    if (half >= 0) {
+        const int mid = nbeg + ((nend - nbeg + 1) / 2 + 15) / 16 * 16;
+        if (half == 0)
+            nend = min(nend, mid);
+        else
+            nbeg = mid;
+    }
     if (nbeg >= nend) return;
     const bool kvalid = 8 * g < D || D >= 32;      // D = 16: lanes g >= 2 carry zeros
 
