@@ -804,7 +804,7 @@ template <typename T, int D> struct StateCfg {
 // One workgroup owns RTW consecutive 16-row tiles of one (b, h) state (rows
 // [16*RTW*rg, 16*RTW*(rg+1))); wave w owns columns [16w, 16w+16) of them.
 // Rows of S evolve independently, so workgroups never communicate.  Per frame:
-//   S_f = alpha*S + U_f + S_hi Gm      (bf16 MFMA, fp32 accumulate)
+//   S_f = alpha*S + U_f + bf16(S) Gm   (bf16 MFMA, fp32 accumulate)
 //   (fp32 mode: S Gm with fp32 MFMA)
 // The product is formed transposed, (S Gm)^T = Gm^T S^T, with the Gm fragment
 // as operand A and the S rows as operand B, so each lane holds four
@@ -812,13 +812,15 @@ template <typename T, int D> struct StateCfg {
 // accesses are then 8 and 16 bytes wide instead of 2 and 4.
 // Gm and S enter the product rounded to bf16 once: that relative error
 // (2^-9 of S Gm, itself small next to alpha S) is of the size G already
-// carries from its bf16 operands and far below the error of U, so neither a
-// lo plane of Gm nor of S in this product buys accuracy (the lo plane of S is
-// still formed, for frame_output).  Each 32-wide contraction step accumulates
-// into its own register set, so the MFMAs of a frame do not wait on each other.
-// S stays in fp32 registers; its bf16 hi/lo split is double-buffered in LDS
-// as the A operand (one barrier per frame), and the previous frame's planes
-// are copied to the workspace for frame_output while this frame's MFMAs run.
+// carries from its bf16 operands and far below the error of U, so a low part
+// of Gm or of S in this product buys no accuracy (frame_output does take S_f
+// with a low part: the remainder codes below).  Each 32-wide contraction step
+// accumulates into its own register set, so the MFMAs of a frame do not wait
+// on each other.  S stays in fp32 registers; its bf16 rounding is
+// double-buffered in LDS as the MFMA operand (one barrier per frame); the
+// previous frame's bf16 plane is copied to the workspace for frame_output, and
+// every lane stores the remainder codes of its own four values of S, while
+// this frame's MFMAs run.
 // Every workgroup of a head reads all of Gm_f (32 KiB in bf16) each
 // frame, mostly from L2.  A frame takes about 0.55 us at D = 128 (bf16); the
 // operands of the next PD frames are in flight in a register ring, deep
@@ -1271,7 +1273,8 @@ template <typename T, int D> struct StepCfg {
 // wave w owns columns [16w, 16w+16) of S_1 and needs only its slice of Gm and
 // U; S_0 is staged once in LDS as the shared operand.  Then O = S_1 Q^T for
 // its tokens as in the output pass, wave w now owning output features
-// [16w, 16w+16) (S_1 as bf16 hi and lo planes, through LDS into A fragments).  The ranges of a unit share blockIdx mod 8 (one XCD), so
+// [16w, 16w+16) (S_1 as bf16 hi and lo planes, S_1 - hi rounded to bf16,
+// through LDS into A fragments).  The ranges of a unit share blockIdx mod 8 (one XCD), so
 // their reads of S_0 and the partials hit one L2; the first range writes S_1
 // to S_out.  S_0 is read from frame_gram's copy of S_in, so S_out may be S_in.
 template <typename T, int D>
