@@ -148,6 +148,23 @@ def test_zero_key_contributes_nothing():
     check(S, rS, "bf16", "S_F")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_more_frames_than_one_launch_chunk(dtype):
+    """300 frames run as two launch chunks (256 + 44 frames) with the state
+    carried between them, also in place (S_final is S0)."""
+    w = inputs.make(1, 2, 300, 24, 32, dtype=dtype, seed=47, s0_std=0.05)
+    o, S = run_gpu(w)
+    ro, rS = oracle_ref(w)
+    check(o, ro, dtype, "O")
+    check(S, rS, dtype, "S_F")
+    q, k, v, b, a, s0 = inputs.to_torch(w, "cuda")
+    carry = s0.clone()
+    o2, _ = api.frame_scan_fwd(q, k, v, b, a, carry, S_final=carry)
+    torch.cuda.synchronize()
+    check(o2.float().cpu().numpy(), ro, dtype, "O (in place)")
+    check(carry.cpu().numpy(), rS, dtype, "S_F (in place)")
+
+
 def test_empty_token_frames_decay_only():
     w = inputs.make(2, 3, 4, 0, 32, dtype="bf16", seed=44, s0_std=0.1)
     o, S = run_gpu(w)
