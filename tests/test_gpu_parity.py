@@ -165,6 +165,16 @@ def test_more_frames_than_one_launch_chunk(dtype):
     check(carry.cpu().numpy(), rS, dtype, "S_F (in place)")
 
 
+def test_more_units_than_cus():
+    """320 (b, h) units: more recurrence and output workgroups than stay
+    resident, and (b, h) indices past every XCD round."""
+    w = inputs.make(4, 80, 3, 20, 16, dtype="bf16", seed=48, s0_std=0.05)
+    o, S = run_gpu(w)
+    ro, rS = oracle_ref(w)
+    check(o, ro, "bf16", "O")
+    check(S, rS, "bf16", "S_F")
+
+
 def test_empty_token_frames_decay_only():
     w = inputs.make(2, 3, 4, 0, 32, dtype="bf16", seed=44, s0_std=0.1)
     o, S = run_gpu(w)

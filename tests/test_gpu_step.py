@@ -46,6 +46,7 @@ CASES = [  # B, H, N, D, dtype
     (1, 1, 880, 128, "bf16"),      # one unit: many token ranges
     (1, 3, 129, 128, "bf16"),      # a last range of one token
     (2, 4, 200, 128, "f32"),
+    (4, 80, 40, 16, "bf16"),       # 320 units: several items per frame_gram workgroup
 ]
 
 
