@@ -179,8 +179,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print("bench.py: this build runs on exactly one GPU; --gpus %d is not supported "
-              "(the scan shards by (batch, head) with no communication; see the design notes)"
+        print("bench.py: the library runs on one GPU per process; --gpus %d is not supported "
+              "(a scan would shard by (batch, head), with no communication between GPUs)"
               % args.gpus, file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
