@@ -211,8 +211,6 @@ gdn_status launch_all(const Plan& p, ScanArgs a, hipStream_t stream, int cus, fl
     for (int f0 = 0; f0 < a.F; f0 += p.Fc) {
         a.f0 = f0;
         a.Fc = a.F - f0 < p.Fc ? a.F - f0 : p.Fc;
-        a.wsFc = a.Fc;
-        a.fsub0 = 0;
         const int items = units * a.Fc;
         {
             ProfScope ps(K_GRAM, stream);
@@ -238,8 +236,6 @@ gdn_status launch_step(const Plan& p, ScanArgs a, hipStream_t stream, int cus) {
     const int units = (int)p.units;
     a.f0 = 0;
     a.Fc = 1;
-    a.wsFc = 1;
-    a.fsub0 = 0;
     int parts = 1, tpart = 0;
     step_ranges(p.units, a.N, gdn::GramCfg<T, D>::TS, cus < kSizingCUs ? cus : kSizingCUs, &parts, &tpart);
     if (parts > p.parts_max) return GDN_ERR_LAUNCH;   // cannot happen: sized for kSizingCUs
@@ -367,7 +363,6 @@ gdn_status run(const gdn_desc* d, bool step, const void* q, const void* k, const
     a.S_in = S0;
     a.o = o;
     a.S_out = S_final;
-    a.S_out2 = nullptr;
     a.ws = static_cast<unsigned char*>(workspace);
     a.B = d->B;
     a.H = d->H;
@@ -378,9 +373,6 @@ gdn_status run(const gdn_desc* d, bool step, const void* q, const void* k, const
     a.tsplit = 1;
     a.tchunk = 16;
     a.ntail = 0;
-    a.wsFc = p.Fc;
-    a.fsub0 = 0;
-    a.tok_bytes = d->N > 0 ? (uint32_t)(((size_t)(d->N - 1) * d->H * p.D + p.D) * p.esz) : 0u;
     a.parts = 1;
     a.tpart = d->N;
     a.spart = nullptr;

@@ -247,18 +247,14 @@ struct ScanArgs {
     const float* S_in;    // state entering frame f0 (NULL: zeros)
     void* o;
     float* S_out;         // state after the last frame of the launch (may equal S_in)
-    float* S_out2;        // optional second copy of that state (NULL: none)
     unsigned char* ws;
     int B, H, F, N;
-    int f0, Fc;           // frames [f0 + fsub0, f0 + fsub0 + Fc) of this launch
-    int wsFc, fsub0;      // frames per (b, h) held in the workspace, and the first
-                          // of them this launch covers (frame_gram: 0)
+    int f0, Fc;           // frames [f0, f0 + Fc) of this launch; the workspace holds
+                          // Fc frames per (b, h): item (b, h, fl) is (b*H + h)*Fc + fl
     int tsplit;           // token ranges per frame in frame_output
     int tchunk;           // tokens per range (multiple of 16)
     int ntail;            // frame_output: the last ntail (frame, range) items run
                           // as two workgroups of half the tokens each
-    uint32_t tok_bytes;   // bytes from a head's first token row of a frame to the
-                          // end of its last row: (N-1)*H*D*esz + D*esz (0 if N == 0)
     int logits;
     float eps;
     // One-frame path (see frame_step_kernel): frame_gram splits each (b, h)
@@ -439,7 +435,7 @@ __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
         const int fl = (y / parts) % a.Fc;
         it.b = y / (parts * a.Fc);
         it.f = a.f0 + fl;
-        it.ws = ((it.b * H + it.h) * a.wsFc + fl) * parts + it.p;
+        it.ws = ((it.b * H + it.h) * a.Fc + fl) * parts + it.p;
         return it;
     };
     // tokens of item `it`'s range (the host makes every range non-empty)
@@ -849,7 +845,7 @@ __global__ __launch_bounds__(4 * D, 1) void state_scan_kernel(ScanArgs a) {  // 
     const int col0 = wave * 16 + 4 * g;                 // this lane's state columns col0..col0+3
 
     for (int i = tid; i < Fc; i += C::NW * 64) {
-        const float x = a.alpha[((size_t)b * a.F + a.f0 + a.fsub0 + i) * a.H + h];
+        const float x = a.alpha[((size_t)b * a.F + a.f0 + i) * a.H + h];
         sAlpha[i] = a.logits ? sigmoid_f(x) : x;
     }
 
@@ -877,7 +873,7 @@ __global__ __launch_bounds__(4 * D, 1) void state_scan_kernel(ScanArgs a) {  // 
         frag bh_[C::KS];          // Gm for this wave's 16 columns
         f32x4 u[C::RTW];          // U of each row tile in the state's register layout
     };
-    const size_t item0 = (size_t)bh * a.wsFc + a.fsub0;
+    const size_t item0 = (size_t)bh * a.Fc;
     using W = WS<T, D>;
     // Loads of frame fl (always a valid frame: callers clamp); every load is
     // one contiguous KiB of a fragment-major workspace matrix.
@@ -1015,7 +1011,6 @@ __global__ __launch_bounds__(4 * D, 1) void state_scan_kernel(ScanArgs a) {  // 
     for (int i = 0; i < C::RTW; ++i) {
         const size_t idx = (size_t)bh * D * D + (size_t)(a0 + 16 * i + r) * D + col0;
         if (a.S_out) *reinterpret_cast<f32x4*>(a.S_out + idx) = S[i];
-        if (a.S_out2) *reinterpret_cast<f32x4*>(a.S_out2 + idx) = S[i];
     }
 }
 
@@ -1074,8 +1069,8 @@ __global__ __launch_bounds__(256, 2) void frame_output_kernel(ScanArgs a) {
     const int part = (x / a.H) % a.tsplit;
     const int fl = (x / (a.H * a.tsplit)) % a.Fc;
     const int b = x / (a.H * a.tsplit * a.Fc);
-    const int item = (b * a.H + h) * a.wsFc + a.fsub0 + fl;   // workspace item
-    const int f = a.f0 + a.fsub0 + fl;
+    const int item = (b * a.H + h) * a.Fc + fl;    // workspace item
+    const int f = a.f0 + fl;
     const int N = a.N, H = a.H;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = lane & 15, g = lane >> 4;
