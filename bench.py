@@ -97,7 +97,7 @@ def cpu_baseline(w, budget_s: float):
                       % (fs, w.F, w.B * w.H, w.N, dt)}
 
 
-def streaming_step(frames: int, reps: int = 5):
+def streaming_step(frames: int, reps: int = 40, warm: int = 10):
     """gdn_frame_step at the streaming workload's shape (B4 H32 d64 N880,
     bf16, fp32 state carried in place): `frames` consecutive steps captured in
     one HIP graph and replayed, so the figure is GPU time per step without the
@@ -133,7 +133,8 @@ def streaming_step(frames: int, reps: int = 5):
         with torch.cuda.graph(graph, stream=cs):
             run()
     torch.cuda.synchronize()
-    graph.replay()
+    for _ in range(warm):
+        graph.replay()
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -166,8 +167,8 @@ def copy_calibration(nbytes: int, steps: int):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="full_minute")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=15.0,
