@@ -98,11 +98,14 @@ def cpu_baseline(w, budget_s: float):
 
 
 def streaming_step(frames: int, reps: int = 40, warm: int = 10):
-    """gdn_frame_step at the streaming workload's shape (B4 H32 d64 N880,
-    bf16, fp32 state carried in place): `frames` consecutive steps captured in
-    one HIP graph and replayed, so the figure is GPU time per step without the
-    Python call overhead.  Inputs are seeded Gaussians drawn on the device in
-    the workload's distributions (timing does not depend on the values)."""
+    """gdn_frame_step at the streaming workload's shape (B4 H32 d64 N880, bf16,
+    fp32 state): `frames` consecutive steps captured in one HIP graph and
+    replayed, so the figure is GPU time per step without the Python call
+    overhead.  Timed twice: with the state alternating between two buffers
+    (S_out of one step is S_in of the next; the one-launch path) and carried
+    in place in one buffer (S_out == S_in; the two-launch path).  Inputs are
+    seeded Gaussians drawn on the device in the workload's distributions
+    (timing does not depend on the values)."""
     import torch
     from gated_deltanet_scan_amd import api
     B, H, N, D = 4, 32, 880, 64
@@ -118,39 +121,46 @@ def streaming_step(frames: int, reps: int = 40, warm: int = 10):
     beta = [torch.sigmoid(mk(B, N, H)) / N for _ in range(frames)]
     alpha = [torch.sigmoid(mk(B, H) + 3.0) for _ in range(frames)]
     o = [torch.empty_like(q[0]) for _ in range(frames)]
-    S = torch.zeros((B, H, D, D), dtype=torch.float32, device="cuda")
+    S = [torch.zeros((B, H, D, D), dtype=torch.float32, device="cuda") for _ in range(2)]
     desc = api.make_desc(B, H, 1, N, D, torch.bfloat16)
     ws = api.alloc_workspace(desc, q[0].device)
     cs = torch.cuda.Stream()
 
-    def run():
-        for f in range(frames):
-            api.frame_step(q[f], k[f], v[f], beta[f], alpha[f], S, o=o[f], S_out=S, workspace=ws, stream=cs)
-    with torch.cuda.stream(cs):
-        run()
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=cs):
+    def timed(nbuf: int) -> float:
+        def run():
+            for f in range(frames):
+                api.frame_step(q[f], k[f], v[f], beta[f], alpha[f], S[f % nbuf], o=o[f],
+                               S_out=S[(f + 1) % nbuf], workspace=ws, stream=cs)
+        with torch.cuda.stream(cs):
             run()
-    torch.cuda.synchronize()
-    for _ in range(warm):
-        graph.replay()
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        graph.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) / (reps * frames) * 1e3
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=cs):
+                run()
+        torch.cuda.synchronize()
+        for _ in range(warm):
+            graph.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (reps * frames) * 1e3
+
+    us = timed(2)
+    us_in_place = timed(1)
     # q, k, v read and o written (bf16), beta and alpha read, S read and written
     nbytes = B * N * H * D * 2 * 4 + B * N * H * 4 + B * H * 4 + 2 * B * H * D * D * 4
     return {"workload": "streaming (B4 H32 d64 N880, one frame per gdn_frame_step)", "us_per_step": round(us, 2),
+            "us_per_step_in_place": round(us_in_place, 2),
             "frames_timed": frames * reps, "alg_bytes_per_step": nbytes,
             "hbm_gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
             "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-            "timing": "HIP graph of %d consecutive steps, replayed %d times" % (frames, reps)}
+            "timing": "HIP graph of %d consecutive steps, replayed %d times after %d; state in two "
+                      "alternating buffers (in place: one buffer)" % (frames, reps, warm)}
 
 
 def copy_calibration(nbytes: int, steps: int):

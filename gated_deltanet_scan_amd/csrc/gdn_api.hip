@@ -228,14 +228,43 @@ gdn_status launch_all(const Plan& p, ScanArgs a, hipStream_t stream, int cus, fl
     return GDN_OK;
 }
 
-// One frame (F == 1): frame_gram over (b, h, token range) items, writing fp32
-// partials and copying S_in, then frame_step (state update and output pass in
-// one launch).
+// Output token ranges of a one-frame launch: about `want` workgroups over all
+// (b, h) units, whole 16-token blocks, at least 64 tokens each.
+inline void step_out_ranges(ScanArgs& s, int units, int want) {
+    int tsplit = (want + units - 1) / units;
+    const int maxsplit = s.N > 0 ? (s.N + 63) / 64 : 1;
+    if (tsplit > maxsplit) tsplit = maxsplit;
+    if (tsplit < 1) tsplit = 1;
+    int tchunk = s.N > 0 ? (s.N + tsplit - 1) / tsplit : 0;
+    tchunk = (tchunk + 15) / 16 * 16;
+    if (s.N > 0) tsplit = (s.N + tchunk - 1) / tchunk;
+    s.tsplit = tsplit;
+    s.tchunk = tchunk;
+}
+
+// One frame (F == 1).  bf16 with D <= 64 and a state that is not updated in
+// place: frame_step alone, every workgroup forming the frame's whole G and U
+// (measured at B4 H32 d64 N880: 25.4 against 27.1 us per step for the two
+// launches below).  Otherwise frame_gram over (b, h, token range) items,
+// writing fp32 partials and copying S_in, then frame_step (state update and
+// output pass).
 template <typename T, int D>
 gdn_status launch_step(const Plan& p, ScanArgs a, hipStream_t stream, int cus) {
     const int units = (int)p.units;
     a.f0 = 0;
     a.Fc = 1;
+    const int want = cus > 0 ? cus : 256;
+    if constexpr (sizeof(T) == 2 && D <= 64) {
+        if (a.S_in == nullptr || a.S_in != a.S_out) {
+            ScanArgs s = a;
+            step_out_ranges(s, units, want);
+            ProfScope ps(K_STEP, stream);
+            const int grid = 8 * ((units + 7) / 8) * s.tsplit;
+            hipLaunchKernelGGL((gdn::frame_step_kernel<T, D, true>), dim3(grid), dim3(gdn::StepCfg<T, D>::NTH), 0,
+                               stream, s);
+            return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+        }
+    }
     int parts = 1, tpart = 0;
     step_ranges(p.units, a.N, gdn::GramCfg<T, D>::TS, cus < kSizingCUs ? cus : kSizingCUs, &parts, &tpart);
     if (parts > p.parts_max) return GDN_ERR_LAUNCH;   // cannot happen: sized for kSizingCUs
@@ -255,23 +284,15 @@ gdn_status launch_step(const Plan& p, ScanArgs a, hipStream_t stream, int cus) {
     if (hipGetLastError() != hipSuccess) return GDN_ERR_LAUNCH;
     ScanArgs s = a;
     s.S_in = a.S_in ? scopy : nullptr;
-    // output ranges: about one workgroup per CU, at least 64 tokens each
-    // (measured at B4 H32 d64 N880: 26.6 us per step with two ranges per
-    // (b, h), 27.0 with four, 29.6 with eight)
-    const int want = cus > 0 ? cus : 256;
-    int tsplit = (want + units - 1) / units;
-    const int maxsplit = a.N > 0 ? (a.N + 63) / 64 : 1;
-    if (tsplit > maxsplit) tsplit = maxsplit;
-    if (tsplit < 1) tsplit = 1;
-    int tchunk = a.N > 0 ? (a.N + tsplit - 1) / tsplit : 0;
-    tchunk = (tchunk + 15) / 16 * 16;
-    if (a.N > 0) tsplit = (a.N + tchunk - 1) / tchunk;
-    s.tsplit = tsplit;
-    s.tchunk = tchunk;
+    // output ranges: about one workgroup per CU (measured at B4 H32 d64 N880:
+    // 26.6 us per step with two ranges per (b, h), 27.0 with four, 29.6 with
+    // eight)
+    step_out_ranges(s, units, want);
     {
         ProfScope ps(K_STEP, stream);
-        const int grid = 8 * ((units + 7) / 8) * tsplit;
-        hipLaunchKernelGGL((gdn::frame_step_kernel<T, D>), dim3(grid), dim3(gdn::StepCfg<T, D>::NTH), 0, stream, s);
+        const int grid = 8 * ((units + 7) / 8) * s.tsplit;
+        hipLaunchKernelGGL((gdn::frame_step_kernel<T, D, false>), dim3(grid), dim3(gdn::StepCfg<T, D>::NTH), 0,
+                           stream, s);
     }
     return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }

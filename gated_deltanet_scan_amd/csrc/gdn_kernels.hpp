@@ -1272,13 +1272,35 @@ template <typename T, int D> struct StepCfg {
 // through LDS into A fragments).  The ranges of a unit share blockIdx mod 8 (one XCD), so
 // their reads of S_0 and the partials hit one L2; the first range writes S_1
 // to S_out.  S_0 is read from frame_gram's copy of S_in, so S_out may be S_in.
-template <typename T, int D>
+//
+// FUSED (bf16, D <= 64): the whole step in this one launch.  Each workgroup
+// first forms the frame's entire G and U itself (phase A): K, V and beta of
+// all N tokens of its (b, h) stream through registers, two tokens per thread
+// and PDA 64-token blocks ahead, and are written transposed ([feature][token],
+// rho k, beta rho k and v in bf16) into a double-buffered LDS tile, from which
+// wave w forms the G tiles of columns [16w, 16w+16) and the U^T tiles of rows
+// [16w, 16w+16) with MFMA.  The G tile of rows c lands in each lane as four
+// consecutive c (4g..4g+3) of one column e: so the fragment of Gm^T for a
+// 32-wide step holds c = 4g+t and 16+4g+t, and the S_0 fragment that meets it
+// in the update takes the same columns (a fixed permutation of the
+// contraction, the same on both operands); U^T lands already in the state's
+// register layout.  The ranges of a (b, h) share one XCD, so their reads of
+// K and V are served by one L2.  Nothing is written between launches, and S_0
+// is read straight from S_in: the host takes this path only when S_out does
+// not alias S_in.
+template <typename T, int D, bool FUSED>
 __global__ __launch_bounds__(64 * (D / 16), 2) void frame_step_kernel(ScanArgs a) {
     using C = StepCfg<T, D>;
     using io = IO<T>;
     using frag = typename io::frag;
     using PL = PartLayout<D>;
-    __shared__ __attribute__((aligned(16))) unsigned char smem[C::LDS];
+    static_assert(!FUSED || (sizeof(T) == 2 && D <= 64), "the one-launch step is bf16, D <= 64");
+    constexpr int BTA = 64;                          // phase A: tokens per block
+    constexpr int ROWA = BTA * 2;                    //   bytes per LDS row (one feature)
+    constexpr int ARRA = D * ROWA;                   //   one transposed array
+    constexpr int LDSA = FUSED ? 2 * 3 * ARRA : 0;   //   rho K, beta rho K, V; double-buffered
+    constexpr int LDSF = C::LDS > LDSA ? C::LDS : LDSA;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[LDSF];
 
     const int units = a.B * a.H;
     const int x = (int)blockIdx.x, slot = x >> 3;
@@ -1334,8 +1356,6 @@ __global__ __launch_bounds__(64 * (D / 16), 2) void frame_step_kernel(ScanArgs a
     // wave's Gm^T fragments), so that one round trip covers them: partials
     // come PP at a time through a buffer resource that ends at the last one,
     // so those of a batch past the end read zeros
-    const rsrc_t rp = make_rsrc(reinterpret_cast<const unsigned char*>(a.spart) + (size_t)bh * a.parts * PL::bytes,
-                                (uint32_t)(a.parts * PL::bytes));
     f32x4 glo[C::KS], ghi[C::KS], su[C::ET];        // sums: this wave's Gm^T fragments, U slice
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
@@ -1353,44 +1373,160 @@ __global__ __launch_bounds__(64 * (D / 16), 2) void frame_step_kernel(ScanArgs a
 #pragma unroll
     for (int i = 0; i < C::ET; ++i)
         sn[i] = s0 ? *reinterpret_cast<const f32x4*>(s0 + (size_t)(16 * i + r) * D + col0) : f32x4{0, 0, 0, 0};
-    // one batch of PP partials: loads, then sums
-    auto load_batch = [&](int pp, f32x4 (&tg)[C::PP][2 * C::KS], f32x4 (&tu)[C::PP][C::ET]) {
-#pragma unroll
-        for (int q2 = 0; q2 < C::PP; ++q2) {
-            const uint32_t pb = (uint32_t)((pp + q2) * PL::bytes);
-#pragma unroll
-            for (int ks = 0; ks < C::KS; ++ks) {
-                tg[q2][2 * ks] = __builtin_bit_cast(f32x4, bload16(rp, pb + PL::g_off + PL::frag_off(wave, ks, 0, lane)));
-                tg[q2][2 * ks + 1] = __builtin_bit_cast(f32x4, bload16(rp, pb + PL::g_off + PL::frag_off(wave, ks, 1, lane)));
+    if constexpr (!FUSED) {
+        const rsrc_t rp = make_rsrc(reinterpret_cast<const unsigned char*>(a.spart) + (size_t)bh * a.parts * PL::bytes,
+                                    (uint32_t)(a.parts * PL::bytes));
+        // one batch of PP partials: loads, then sums
+        auto load_batch = [&](int pp, f32x4 (&tg)[C::PP][2 * C::KS], f32x4 (&tu)[C::PP][C::ET]) {
+    #pragma unroll
+            for (int q2 = 0; q2 < C::PP; ++q2) {
+                const uint32_t pb = (uint32_t)((pp + q2) * PL::bytes);
+    #pragma unroll
+                for (int ks = 0; ks < C::KS; ++ks) {
+                    tg[q2][2 * ks] = __builtin_bit_cast(f32x4, bload16(rp, pb + PL::g_off + PL::frag_off(wave, ks, 0, lane)));
+                    tg[q2][2 * ks + 1] = __builtin_bit_cast(f32x4, bload16(rp, pb + PL::g_off + PL::frag_off(wave, ks, 1, lane)));
+                }
+    #pragma unroll
+                for (int i = 0; i < C::ET; ++i)          // U tile (e-tile wave, a-tile i)
+                    tu[q2][i] = __builtin_bit_cast(f32x4, bload16(rp, pb + (uint32_t)(PL::u_off + (wave * PL::RT + i) * 1024 + lane * 16)));
             }
-#pragma unroll
-            for (int i = 0; i < C::ET; ++i)          // U tile (e-tile wave, a-tile i)
-                tu[q2][i] = __builtin_bit_cast(f32x4, bload16(rp, pb + (uint32_t)(PL::u_off + (wave * PL::RT + i) * 1024 + lane * 16)));
-        }
-    };
-    auto add_batch = [&](const f32x4 (&tg)[C::PP][2 * C::KS], const f32x4 (&tu)[C::PP][C::ET]) {
-#pragma unroll
-        for (int q2 = 0; q2 < C::PP; ++q2) {
-#pragma unroll
-            for (int ks = 0; ks < C::KS; ++ks) {
-                glo[ks] += tg[q2][2 * ks];
-                ghi[ks] += tg[q2][2 * ks + 1];
+        };
+        auto add_batch = [&](const f32x4 (&tg)[C::PP][2 * C::KS], const f32x4 (&tu)[C::PP][C::ET]) {
+    #pragma unroll
+            for (int q2 = 0; q2 < C::PP; ++q2) {
+    #pragma unroll
+                for (int ks = 0; ks < C::KS; ++ks) {
+                    glo[ks] += tg[q2][2 * ks];
+                    ghi[ks] += tg[q2][2 * ks + 1];
+                }
+    #pragma unroll
+                for (int i = 0; i < C::ET; ++i) su[i] += tu[q2][i];
             }
-#pragma unroll
-            for (int i = 0; i < C::ET; ++i) su[i] += tu[q2][i];
+        };
+        {
+            f32x4 tg[C::PP][2 * C::KS], tu[C::PP][C::ET];
+            load_batch(0, tg, tu);
+    #pragma unroll
+            for (int j = 0; j < C::PD; ++j) load_blk(j, ring[j]);
+            add_batch(tg, tu);
         }
-    };
-    {
-        f32x4 tg[C::PP][2 * C::KS], tu[C::PP][C::ET];
-        load_batch(0, tg, tu);
+        for (int pp = C::PP; pp < a.parts; pp += C::PP) {
+            f32x4 tg[C::PP][2 * C::KS], tu[C::PP][C::ET];
+            load_batch(pp, tg, tu);
+            add_batch(tg, tu);
+        }
+    } else {
+        // ---- phase A: G (columns 16w..) and U^T (rows 16w..) of the whole frame
+        constexpr int GPT = D / 8;                   // 16-byte feature groups per token
+        constexpr int PDA = 3;                       // blocks of K, V and beta in flight
+        static_assert(32 * GPT == C::NTH, "two tokens per thread per block");
+        constexpr int RT = D / 16;
+        const int fgrp = tid % GPT, tp = tid / GPT;  // features 8 fgrp.., tokens 2 tp, 2 tp + 1
+        const int nba = (N + BTA - 1) / BTA;
+        const float inv_eps = 1.0f / a.eps, inv_n = N > 0 ? 1.0f / (float)N : 0.0f;
+        const size_t tokf = (size_t)b * a.F * N;     // the frame's first token (F == 1)
+        const uint32_t fbytes = N > 0 ? (uint32_t)(((size_t)(N - 1) * rowstride + D) * 2) : 0u;
+        const rsrc_t rk = make_rsrc(static_cast<const T*>(a.k) + tokf * rowstride + (size_t)h * D, fbytes);
+        const rsrc_t rv = make_rsrc(static_cast<const T*>(a.v) + tokf * rowstride + (size_t)h * D, fbytes);
+        const rsrc_t rb = make_rsrc(a.beta + tokf * H + h, N > 0 ? (uint32_t)(((size_t)(N - 1) * H + 1) * 4) : 0u);
+        struct KV {
+            u32x4 k0, k1, v0, v1;
+            float b0, b1;
+        };
+        auto load_kv = [&](int blk, KV& q2) {       // rows past N read as zeros
+            const uint32_t t0 = (uint32_t)(blk * BTA + 2 * tp);
+            const uint32_t o0 = t0 * row_bytes + (uint32_t)(fgrp * 16);
+            q2.k0 = bload16(rk, o0);
+            q2.k1 = bload16(rk, o0 + row_bytes);
+            q2.v0 = bload16(rv, o0);
+            q2.v1 = bload16(rv, o0 + row_bytes);
+            q2.b0 = bload4f(rb, t0 * (uint32_t)H * 4u);
+            q2.b1 = bload4f(rb, (t0 + 1u) * (uint32_t)H * 4u);
+        };
+        // key norms over the token's GPT lanes; rho k, beta rho k (bf16) and v
+        // written transposed, the two tokens of a thread as one dword
+        auto put_kv = [&](const KV& q2, unsigned char* buf) {
+            float n0 = 0.f, n1 = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float x0 = bf2f((uint16_t)(q2.k0[e >> 1] >> (16 * (e & 1))));
+                const float x1 = bf2f((uint16_t)(q2.k1[e >> 1] >> (16 * (e & 1))));
+                n0 += x0 * x0;
+                n1 += x1 * x1;
+            }
+            n0 = group_sum<GPT>(n0);
+            n1 = group_sum<GPT>(n1);
+            // 1 / max(|k|, eps) and beta (logits: sigmoid / N), as frame_gram forms them
+            const float r0 = fminf(__builtin_amdgcn_rsqf(n0), inv_eps), r1 = fminf(__builtin_amdgcn_rsqf(n1), inv_eps);
+            const float be0 = a.logits ? sigmoid_f(q2.b0) * inv_n : q2.b0;
+            const float be1 = a.logits ? sigmoid_f(q2.b1) * inv_n : q2.b1;
+            const float s0b = be0 * r0, s1b = be1 * r1;
+            const int t = 2 * tp;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int sh = 16 * (e & 1);
+                const uint32_t kb0 = (q2.k0[e >> 1] >> sh) & 0xffffu, kb1 = (q2.k1[e >> 1] >> sh) & 0xffffu;
+                const float x0 = bf2f((uint16_t)kb0), x1 = bf2f((uint16_t)kb1);
+                const int off = lds_chunk<ROWA>(8 * fgrp + e, t >> 3) + (t & 7) * 2;
+                *reinterpret_cast<uint32_t*>(buf + off) = pack_bf16x2(r0 * x0, r1 * x1);
+                *reinterpret_cast<uint32_t*>(buf + ARRA + off) = pack_bf16x2(s0b * x0, s1b * x1);
+                *reinterpret_cast<uint32_t*>(buf + 2 * ARRA + off) =
+                    ((q2.v0[e >> 1] >> sh) & 0xffffu) | (((q2.v1[e >> 1] >> sh) & 0xffffu) << 16);
+            }
+        };
+        f32x4 accg[RT], accu[RT];
+#pragma unroll
+        for (int i = 0; i < RT; ++i) {
+            accg[i] = f32x4{0, 0, 0, 0};
+            accu[i] = f32x4{0, 0, 0, 0};
+        }
+        auto mfma_blk = [&](const unsigned char* buf) {
+#pragma unroll
+            for (int ks = 0; ks < BTA / 32; ++ks) {
+                const frag bx = lds_frag<T, ROWA>(buf + ARRA, 16 * wave + r, ks, g);        // beta rho K^T, rows e
+#pragma unroll
+                for (int mt = 0; mt < RT; ++mt)                                             // G[c][e]
+                    io::mma(accg[mt], lds_frag<T, ROWA>(buf, 16 * mt + r, ks, g), bx);
+#pragma unroll
+                for (int i = 0; i < RT; ++i)                                                // U^T[e][a]
+                    io::mma(accu[i], bx, lds_frag<T, ROWA>(buf + 2 * ARRA, 16 * i + r, ks, g));
+            }
+        };
+        KV ring_a[PDA];
+#pragma unroll
+        for (int j = 0; j < PDA; ++j) load_kv(j, ring_a[j]);
+        const int nfa = nba / PDA;
+        for (int gi = 0; gi < nfa; ++gi) {
+#pragma unroll
+            for (int j = 0; j < PDA; ++j) {
+                const int blk = gi * PDA + j;
+                unsigned char* buf = smem + (blk & 1) * 3 * ARRA;
+                put_kv(ring_a[j], buf);
+                __syncthreads();
+                load_kv(blk + PDA, ring_a[j]);       // past the frame: zeros, no traffic
+                mfma_blk(buf);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < PDA; ++j) {
+            const int blk = nfa * PDA + j;
+            if (blk < nba) {
+                unsigned char* buf = smem + (blk & 1) * 3 * ARRA;
+                put_kv(ring_a[j], buf);
+                __syncthreads();
+                mfma_blk(buf);
+            }
+        }
+        __syncthreads();                             // the LDS is staged with S_0 next
 #pragma unroll
         for (int j = 0; j < C::PD; ++j) load_blk(j, ring[j]);
-        add_batch(tg, tu);
-    }
-    for (int pp = C::PP; pp < a.parts; pp += C::PP) {
-        f32x4 tg[C::PP][2 * C::KS], tu[C::PP][C::ET];
-        load_batch(pp, tg, tu);
-        add_batch(tg, tu);
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+            glo[ks] = accg[2 * ks];
+            ghi[ks] = 2 * ks + 1 < RT ? accg[2 * ks + 1] : f32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int i = 0; i < C::ET; ++i) su[i] = accu[i];
     }
 #pragma unroll
     for (int i = 0; i < C::PD0; ++i) {
@@ -1412,7 +1548,7 @@ __global__ __launch_bounds__(64 * (D / 16), 2) void frame_step_kernel(ScanArgs a
                            pack_bf16x2(hi[2], hi[3])};
         else
             gm[ks] = f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        if (!kvalid) gm[ks] = io::zero();
+        if (!FUSED && !kvalid) gm[ks] = io::zero();
     }
     __syncthreads();                                // S_0 staged
 #pragma unroll
@@ -1422,14 +1558,20 @@ __global__ __launch_bounds__(64 * (D / 16), 2) void frame_step_kernel(ScanArgs a
             const int c0 = (ks * 32 + 8 * g) % D;
             const unsigned char* src = sS0 + (16 * i + r) * C::ROWB + c0 * C::SZ;
             frag sb;
-            if constexpr (sizeof(T) == 2) {
+            if constexpr (FUSED) {                  // columns 32ks + 4g + t, 32ks + 16 + 4g + t
+                const unsigned char* row = sS0 + (16 * i + r) * C::ROWB;
+                const u32x2 lo = *reinterpret_cast<const u32x2*>(row + (ks * 32 + 4 * g) * 2);
+                const u32x2 hi = ks * 32 + 16 < D ? *reinterpret_cast<const u32x2*>(row + (ks * 32 + 16 + 4 * g) * 2)
+                                                  : u32x2{0u, 0u};
+                sb = u32x4{lo[0], lo[1], hi[0], hi[1]};
+            } else if constexpr (sizeof(T) == 2) {
                 sb = *reinterpret_cast<const u32x4*>(src);
             } else {
                 const f32x4 lo = *reinterpret_cast<const f32x4*>(src);
                 const f32x4 hi = *reinterpret_cast<const f32x4*>(src + 16);
                 sb = f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
             }
-            if (!kvalid) sb = io::zero();
+            if (!FUSED && !kvalid) sb = io::zero();
             io::mma(sn[i], gm[ks], sb);               // (S_0 Gm)^T += Gm^T S_0^T
         }
     }
