@@ -1418,7 +1418,8 @@ __global__ __launch_bounds__(64 * (D / 16), 2) void frame_step_kernel(ScanArgs a
     } else {
         // ---- phase A: G (columns 16w..) and U^T (rows 16w..) of the whole frame
         constexpr int GPT = D / 8;                   // 16-byte feature groups per token
-        constexpr int PDA = 3;                       // blocks of K, V and beta in flight
+        constexpr int PDA = 4;                       // blocks of K, V and beta in flight (measured
+                                                     // best: 3 and 6 are ~1 us slower, 5 spills)
         static_assert(32 * GPT == C::NTH, "two tokens per thread per block");
         constexpr int RT = D / 16;
         const int fgrp = tid % GPT, tp = tid / GPT;  // features 8 fgrp.., tokens 2 tp, 2 tp + 1

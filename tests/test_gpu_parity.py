@@ -231,26 +231,30 @@ def test_guidance_sampled():
 
 
 @pytest.mark.slow
-def test_streaming_steps_match_scan_and_oracle():
+@pytest.mark.parametrize("carry", ["in_place", "two_buffers"])
+def test_streaming_steps_match_scan_and_oracle(carry):
     """64 calls of the single-frame step carrying fp32 state, against one
     64-frame scan of the same frames and against the oracle.  The step runs
-    its own kernels (token-range partials summed in fp32, the state update
-    fused into the output pass), so it matches the scan to rounding, not bit
-    for bit; both must meet the oracle's tolerance."""
+    its own kernels (in place: token-range partials summed in fp32, the state
+    update fused into the output pass; in two alternating buffers: one launch
+    that forms each frame's G and U itself), so it matches the scan to
+    rounding, not bit for bit; both must meet the oracle's tolerance."""
     w = inputs.make_config("streaming", seed=0)
     q, k, v, b, a, _ = inputs.to_torch(w, "cuda")
     o_scan, S_scan = api.frame_scan_fwd(q, k, v, b, a, None)
-    S = torch.zeros_like(S_scan)
+    bufs = [torch.zeros_like(S_scan)] + ([torch.full_like(S_scan, float("nan"))] if carry == "two_buffers" else [])
     o_steps = torch.empty_like(o_scan)
     desc = api.make_desc(w.B, w.H, 1, w.N, w.Dk, q.dtype)
     ws = api.alloc_workspace(desc, q.device)
     for f in range(w.F):
         # each streamed frame arrives as its own tensor
+        S_in, S_out = bufs[f % len(bufs)], bufs[(f + 1) % len(bufs)]
         of, _ = api.frame_step(q[:, f].contiguous(), k[:, f].contiguous(), v[:, f].contiguous(),
-                               b[:, f].contiguous(), a[:, f].contiguous(), S, S_out=S,
+                               b[:, f].contiguous(), a[:, f].contiguous(), S_in, S_out=S_out,
                                workspace=ws)
         o_steps[:, f] = of
     torch.cuda.synchronize()
+    S = bufs[w.F % len(bufs)]
     diff = (o_steps.float() - o_scan.float()).abs().max().item()
     print("max |step - scan| on O: %g, on S: %g" % (diff, (S - S_scan).abs().max().item()))
     check(o_steps.float().cpu().numpy(), o_scan.float().cpu().numpy(), "bf16", "O steps vs scan")
