@@ -244,7 +244,7 @@ inline void step_out_ranges(ScanArgs& s, int units, int want) {
 
 // One frame (F == 1).  bf16 with D <= 64 and a state that is not updated in
 // place: frame_step alone, every workgroup forming the frame's whole G and U
-// (measured at B4 H32 d64 N880: 24.4 against 26.7 us per step for the two
+// (measured at B4 H32 d64 N880: 23.8 against 26.7 us per step for the two
 // launches below).  Otherwise frame_gram over (b, h, token range) items,
 // writing fp32 partials and copying S_in, then frame_step (state update and
 // output pass).

@@ -1495,7 +1495,15 @@ __global__ __launch_bounds__(64 * (D / 16), 2) void frame_step_kernel(ScanArgs a
         };
         KV ring_a[PDA];
 #pragma unroll
-        for (int j = 0; j < PDA; ++j) load_kv(j, ring_a[j]);
+        for (int j = 0; j < PDA; ++j) {
+            load_kv(j, ring_a[j]);
+            // keep each block's six loads together: issued in the loop's own
+            // order (K, V, beta per block), the wait for a block's beta stays
+            // exact; left free, the compiler moved every beta load behind all
+            // K and V loads here, and the waits it then had to share with the
+            // loop drained most of the ring before each block's beta was used
+            asm volatile("" ::: "memory");
+        }
         const int nfa = nba / PDA;
         for (int gi = 0; gi < nfa; ++gi) {
 #pragma unroll
