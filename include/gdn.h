@@ -99,7 +99,9 @@ gdn_status gdn_frame_scan_fwd(const gdn_desc* d,
  * state from S_in (NULL means zeros) to S_out.  S_out may equal S_in.  The
  * streaming workflow calls it once per incoming latent frame (the WorldFoundry
  * "SANA-WM" page, section "What it is for": the streaming pipeline advances
- * the rollout window by window). */
+ * the rollout window by window).  For bf16 with Dk <= 64, a state kept in two
+ * buffers that alternate as S_in and S_out runs as one kernel launch; an
+ * in-place S_out == S_in takes two (the state is first copied aside). */
 gdn_status gdn_frame_step(const gdn_desc* d,
                           const void* q, const void* k, const void* v,
                           const float* beta, const float* alpha,
