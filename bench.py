@@ -17,6 +17,7 @@ import argparse
 import hashlib
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -77,8 +78,9 @@ def load_traffic(kernel: str, workload: str, src_hash: str, launches_per_step: i
     return c.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, budget_s: float):
-    """The fp64 oracle on the first F_s frames of every (b, h) of the workload."""
+def oracle_timing(w, budget_s: float):
+    """The fp64 oracle on the first F_s frames of every (b, h) of workload w,
+    F_s chosen so the run takes about budget_s seconds: (tokens/s, F_s, s)."""
     import numpy as np
     import oracle
     sl = lambda x, n: np.ascontiguousarray(x[:, :n])
@@ -91,10 +93,87 @@ def cpu_baseline(w, budget_s: float):
     t = time.perf_counter()
     oracle.scan(*args)
     dt = time.perf_counter() - t
-    return {"value": w.B * fs * w.N / dt, "unit": "tokens/s", "cores": oracle.max_threads(),
+    return w.B * fs * w.N / dt, fs, dt
+
+
+def cpu_model() -> str:
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except Exception:
+        pass
+    return "unknown"
+
+
+def single_thread_runs(budget_s: float):
+    """The oracle on one thread (a child process with OMP_NUM_THREADS=1) on the
+    tiny fp32 workload (whole) and on a bounded sample of the short clip."""
+    code = ("import json, sys; sys.path.insert(0, %r); import bench, oracle;"
+            "from gated_deltanet_scan_amd import inputs; out = {};"
+            "[out.__setitem__(n, bench.oracle_timing(inputs.make_config(n), %r))"
+            " for n in ('tiny_fp32', 'short_clip')];"
+            "out['threads'] = oracle.max_threads(); print(json.dumps(out))") % (ROOT, budget_s)
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
+                       timeout=600)
+    if r.returncode != 0:
+        return {"error": r.stderr[-300:]}
+    res = json.loads(r.stdout.strip().splitlines()[-1])
+    out = {"threads": res.pop("threads")}
+    for name, (tps, fs, dt) in res.items():
+        out[name] = {"tokens_per_s": round(tps, 1), "frames": fs, "seconds": round(dt, 3)}
+    return out
+
+
+def cpu_baseline(w, budget_s: float):
+    """The fp64 oracle on the first F_s frames of every (b, h) of the workload,
+    on every host core, plus one-thread runs of the two small workloads."""
+    import oracle
+    tps, fs, dt = oracle_timing(w, budget_s)
+    return {"value": tps, "unit": "tokens/s", "cores": oracle.max_threads(),
             "kind": "oracle",
             "sample": "first %d of %d frames, all %d (b,h) units, %d tokens/frame: %.2f s"
-                      % (fs, w.F, w.B * w.H, w.N, dt)}
+                      % (fs, w.F, w.B * w.H, w.N, dt),
+            "cpu_model": cpu_model(), "nproc": os.cpu_count(),
+            "single_thread": single_thread_runs(min(budget_s, 5.0))}
+
+
+def measured_peaks():
+    """What this GPU reaches on plain work, as a second yardstick next to the
+    published peaks: a 1 GiB device-to-device copy (torch copy_, bytes read
+    plus written per second) and a 8192^3 bf16 matrix product (torch.matmul,
+    hipBLASLt).  Run before the warm-up, so they also bring the clocks up."""
+    import torch
+    n = 1 << 28
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    a = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
+
+    def best(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return min(ts)
+
+    t_copy = best(lambda: y.copy_(x), 20)
+    t_mm = best(lambda: torch.matmul(a, b), 10)
+    del x, y, a, b
+    torch.cuda.empty_cache()
+    return {"copy_gbs": round(2 * 4 * n / t_copy / 1e9, 1),
+            "gemm_bf16_tfs": round(2 * 8192 ** 3 / t_mm / 1e12, 1),
+            "how": "best of 20 copies of 1 GiB (read + write bytes) and of 10 bf16 8192^3 "
+                   "torch.matmul, HIP events"}
 
 
 def streaming_step(frames: int, reps: int = 40, warm: int = 10):
@@ -187,6 +266,10 @@ def main():
                     help="frames of the streaming-step measurement (0: skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES bytes --steps times")
+    ap.add_argument("--flush", choices=["auto", "on", "off"], default="auto",
+                    help="write a 1 GiB buffer before every timed step, so no input is left "
+                         "in the 256 MB last-level cache (auto: when the workload moves less "
+                         "than 1 GiB); each step is then timed by its own HIP events")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -207,6 +290,7 @@ def main():
     torch.cuda.set_device(0)
     w = inputs.make_config(args.workload, seed=args.seed)
     q, k, v, beta, alpha, S0 = inputs.to_torch(w, "cuda")
+    peaks = measured_peaks()      # right before the warm-up: the clocks come up here
     o = torch.empty_like(q)
     S_final = torch.empty((w.B, w.H, w.Dv, w.Dk), dtype=torch.float32, device="cuda")
     desc = api.make_desc(w.B, w.H, w.F, w.N, w.Dk, q.dtype)
@@ -217,6 +301,10 @@ def main():
         api.frame_scan_fwd(q, k, v, beta, alpha, S0, o=o, S_final=S_final, workspace=ws,
                            stream=stream)
 
+    total_bytes, per_kernel_bytes, flops, flops_kernel = algorithmic(w)
+    flush = args.flush == "on" or (args.flush == "auto" and total_bytes < (1 << 30))
+    junk = torch.empty(1 << 28, dtype=torch.float32, device="cuda") if flush else None
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -224,21 +312,30 @@ def main():
     def timed(profiled: bool):
         # K steps bracketed by synchronisation; with `profiled` the library
         # also records a HIP event pair around every kernel launch (on the
-        # launch stream), which adds a few microseconds between kernels
+        # launch stream), which adds a few microseconds between kernels.
+        # With the flush, each step is timed by its own events and the 1 GiB
+        # write before it is outside them.
         if profiled:
             api.profile_begin()
-        ev0 = torch.cuda.Event(enable_timing=True)
-        ev1 = torch.cuda.Event(enable_timing=True)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps if flush else 1)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        ev0.record(stream)
-        for _ in range(args.steps):
-            step()
-        ev1.record(stream)
+        if flush:
+            for e0, e1 in ev:
+                junk.fill_(1.0)
+                e0.record(stream)
+                step()
+                e1.record(stream)
+        else:
+            ev[0][0].record(stream)
+            for _ in range(args.steps):
+                step()
+            ev[0][1].record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         kern = api.profile_end() if profiled else None
-        return ev0.elapsed_time(ev1), wall, kern
+        return sum(e0.elapsed_time(e1) for e0, e1 in ev), wall, kern
 
     # throughput from a clean timed region; per-kernel durations from a second
     # timed region of the same K steps with per-launch events
@@ -246,7 +343,6 @@ def main():
     prof_ms, _, kern = timed(True)
     ms_per_step = gpu_ms / args.steps
 
-    total_bytes, per_kernel_bytes, flops, flops_kernel = algorithmic(w)
     tokens = w.B * w.F * w.N
     value = tokens / (ms_per_step * 1e-3)
 
@@ -269,7 +365,9 @@ def main():
     traffic = load_traffic(dom, args.workload, src_hash, dom_launches_per_step)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": dom, "alg_bytes_per_launch": int(dom_bytes)}
+                "kernel": dom, "alg_bytes_per_launch": int(dom_bytes),
+                "scope": "the dominant kernel alone, on the bytes it must move; the whole "
+                         "scan against the same peak is path_roofline"}
     path_gbs = total_bytes / (ms_per_step * 1e-3) / 1e9
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -283,7 +381,14 @@ def main():
                           "achieved": round(path_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                           "frac": round(path_gbs / HBM_PEAK_GBS, 4),
                           "mfma_frac": round(flops / (ms_per_step * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4),
-                          "alg_flops_per_step": flops},
+                          "alg_flops_per_step": flops,
+                          "frac_of_measured_copy": round(path_gbs / peaks["copy_gbs"], 4),
+                          "mfma_frac_of_measured_gemm": round(
+                              flops / (ms_per_step * 1e-3) / 1e12 / peaks["gemm_bf16_tfs"], 4),
+                          "target": "frac >= 0.5 (ms_per_step <= %.4f)"
+                                    % (total_bytes / (0.5 * HBM_PEAK_GBS * 1e9) * 1e3)},
+        "measured_peaks": peaks,
+        "llc_flush": flush,
         "frame_steps_per_s": round(w.B * w.F / (ms_per_step * 1e-3), 1),
         "head_frame_steps_per_s": round(w.B * w.H * w.F / (ms_per_step * 1e-3), 1),
         "kernels": kernels,

@@ -32,7 +32,8 @@ def _check(t: torch.Tensor, name: str, dtype, shape):
         raise ValueError("%s must be contiguous" % name)
 
 
-def make_desc(B, H, F, N, D, dtype: torch.dtype, *, gates_are_logits=False, eps=1e-6) -> GdnDesc:
+def make_desc(B, H, F, N, D, dtype: torch.dtype, *, gates_are_logits=False, eps=1e-6,
+              normalize_keys=True) -> GdnDesc:
     if dtype == torch.bfloat16:
         io = _lib.GDN_BF16
     elif dtype == torch.float32:
@@ -40,6 +41,8 @@ def make_desc(B, H, F, N, D, dtype: torch.dtype, *, gates_are_logits=False, eps=
     else:
         raise TypeError("q/k/v must be bfloat16 or float32")
     flags = _lib.GDN_FLAG_GATES_ARE_LOGITS if gates_are_logits else 0
+    if not normalize_keys:
+        flags |= _lib.GDN_FLAG_NO_KEY_NORM
     return GdnDesc(B, H, F, N, D, D, io, flags, float(eps))
 
 
@@ -52,11 +55,20 @@ def alloc_workspace(desc: GdnDesc, device) -> Optional[torch.Tensor]:
     return torch.empty(n, dtype=torch.uint8, device=device) if n > 0 else None
 
 
+def _check_workspace(workspace, device):
+    if workspace is None:
+        return
+    if not isinstance(workspace, torch.Tensor):
+        raise TypeError("workspace must be a torch.Tensor")
+    if workspace.device != device:
+        raise ValueError("workspace must be on %s (got %s)" % (device, workspace.device))
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor")
+
+
 def _run(fn_name, q, k, v, beta, alpha, S_in, o, S_out, workspace, desc, stream):
     lib = _lib.load()
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel()
     st = getattr(lib, fn_name)(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
                                _ptr(alpha), _ptr(S_in), _ptr(o), _ptr(S_out), _ptr(workspace),
                                ctypes.c_size_t(ws_bytes), ctypes.c_void_p(stream.cuda_stream))
@@ -64,8 +76,12 @@ def _run(fn_name, q, k, v, beta, alpha, S_in, o, S_out, workspace, desc, stream)
         raise GdnError(st, fn_name)
 
 
+def _launch_stream(stream, device):
+    return torch.cuda.current_stream(device) if stream is None else stream
+
+
 def frame_scan_fwd(q, k, v, beta, alpha, S0=None, *, gates_are_logits: bool = False,
-                   eps: float = 1e-6, o=None, S_final=None, workspace=None,
+                   eps: float = 1e-6, normalize_keys: bool = True, o=None, S_final=None, workspace=None,
                    return_state: bool = True, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Whole-clip frame-wise GDN scan.
 
@@ -81,23 +97,29 @@ def frame_scan_fwd(q, k, v, beta, alpha, S0=None, *, gates_are_logits: bool = Fa
     _check(alpha, "alpha", torch.float32, (B, F, H))
     if S0 is not None:
         _check(S0, "S0", torch.float32, (B, H, D, D))
-    desc = make_desc(B, H, F, N, D, q.dtype, gates_are_logits=gates_are_logits, eps=eps)
-    if o is None:
-        o = torch.empty_like(q)
-    else:
+    desc = make_desc(B, H, F, N, D, q.dtype, gates_are_logits=gates_are_logits, eps=eps,
+                     normalize_keys=normalize_keys)
+    if o is not None:
         _check(o, "o", q.dtype, (B, F, N, H, D))
-    if S_final is None and return_state:
-        S_final = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
-    elif S_final is not None:
+    if S_final is not None:
         _check(S_final, "S_final", torch.float32, (B, H, D, D))
-    if workspace is None:
-        workspace = alloc_workspace(desc, q.device)
-    _run("gdn_frame_scan_fwd", q, k, v, beta, alpha, S0, o, S_final, workspace, desc, stream)
+    _check_workspace(workspace, q.device)
+    stream = _launch_stream(stream, q.device)
+    # Buffers allocated here belong to the launch stream, so torch's caching
+    # allocator never hands them to other work while the kernels still run.
+    with torch.cuda.stream(stream):
+        if o is None:
+            o = torch.empty_like(q)
+        if S_final is None and return_state:
+            S_final = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
+        if workspace is None:
+            workspace = alloc_workspace(desc, q.device)
+        _run("gdn_frame_scan_fwd", q, k, v, beta, alpha, S0, o, S_final, workspace, desc, stream)
     return o, S_final
 
 
 def frame_step(q, k, v, beta, alpha, S_in=None, *, gates_are_logits: bool = False,
-               eps: float = 1e-6, o=None, S_out=None, workspace=None, stream=None):
+               eps: float = 1e-6, normalize_keys: bool = True, o=None, S_out=None, workspace=None, stream=None):
     """One frame of the scan for streaming use.
 
     q, k, v: [B,N,H,D] (or [B,1,N,H,D]); beta: [B,N,H] (or [B,1,N,H]);
@@ -120,15 +142,22 @@ def frame_step(q, k, v, beta, alpha, S_in=None, *, gates_are_logits: bool = Fals
     _check(alpha, "alpha", torch.float32, (B, 1, H))
     if S_in is not None:
         _check(S_in, "S_in", torch.float32, (B, H, D, D))
-    desc = make_desc(B, H, 1, N, D, q.dtype, gates_are_logits=gates_are_logits, eps=eps)
-    if o is None:
-        o = torch.empty_like(q)
-    if S_out is None:
-        S_out = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
-    _check(S_out, "S_out", torch.float32, (B, H, D, D))
-    if workspace is None:
-        workspace = alloc_workspace(desc, q.device)
-    _run("gdn_frame_step", q, k, v, beta, alpha, S_in, o, S_out, workspace, desc, stream)
+    if o is not None:
+        _check(o, "o", q.dtype, (B, 1, N, H, D))
+    if S_out is not None:
+        _check(S_out, "S_out", torch.float32, (B, H, D, D))
+    _check_workspace(workspace, q.device)
+    desc = make_desc(B, H, 1, N, D, q.dtype, gates_are_logits=gates_are_logits, eps=eps,
+                     normalize_keys=normalize_keys)
+    stream = _launch_stream(stream, q.device)
+    with torch.cuda.stream(stream):   # allocations belong to the launch stream
+        if o is None:
+            o = torch.empty_like(q)
+        if S_out is None:
+            S_out = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
+        if workspace is None:
+            workspace = alloc_workspace(desc, q.device)
+        _run("gdn_frame_step", q, k, v, beta, alpha, S_in, o, S_out, workspace, desc, stream)
     return (o.squeeze(1) if squeeze else o), S_out
 
 

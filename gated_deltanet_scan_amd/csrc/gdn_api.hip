@@ -6,6 +6,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -28,7 +29,7 @@ constexpr int kSizingCUs = 256;
 
 // ---------------------------------------------------------------- profiling
 struct Profiler {
-    bool on = false;
+    std::atomic<bool> on{false};
     std::vector<hipEvent_t> pool;   // created lazily, reused across sessions
     std::vector<int> kind;          // kernel kind of each recorded pair
     size_t used = 0;                // pairs used in this session
@@ -125,7 +126,7 @@ gdn_status check_desc(const gdn_desc* d, bool step, Plan* p) {
     if (!d) return GDN_ERR_INVALID_ARG;
     if (d->B < 0 || d->H < 0 || d->F < 0 || d->N < 0) return GDN_ERR_INVALID_ARG;
     if (d->io_dtype != GDN_BF16 && d->io_dtype != GDN_F32) return GDN_ERR_INVALID_ARG;
-    if ((d->flags & ~GDN_FLAG_GATES_ARE_LOGITS) != 0) return GDN_ERR_INVALID_ARG;
+    if ((d->flags & ~(GDN_FLAG_GATES_ARE_LOGITS | GDN_FLAG_NO_KEY_NORM)) != 0) return GDN_ERR_INVALID_ARG;
     if (!(d->eps > 0.0f) || !isfinite(d->eps)) return GDN_ERR_INVALID_ARG;
     if (step && d->F != 1) return GDN_ERR_INVALID_ARG;
     if (d->Dk < 1 || d->Dv < 1) return GDN_ERR_INVALID_ARG;
@@ -395,6 +396,7 @@ gdn_status run(const gdn_desc* d, bool step, const void* q, const void* k, const
     a.F = d->F;
     a.N = d->N;
     a.logits = (d->flags & GDN_FLAG_GATES_ARE_LOGITS) ? 1 : 0;
+    a.raw_keys = (d->flags & GDN_FLAG_NO_KEY_NORM) ? 1 : 0;
     a.eps = d->eps;
     a.tsplit = 1;
     a.tchunk = 16;

@@ -256,6 +256,7 @@ struct ScanArgs {
     int ntail;            // frame_output: the last ntail (frame, range) items run
                           // as two workgroups of half the tokens each
     int logits;
+    int raw_keys;         // keys used as given (no L2 normalisation)
     float eps;
     // One-frame path (see frame_step_kernel): frame_gram splits each (b, h)
     // into `parts` token ranges of `tpart` tokens (a multiple of its stage)
@@ -529,7 +530,7 @@ __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
         }
 #pragma unroll
         for (int j = 0; j < C::TPT; ++j) {
-            rho[j] = fminf(__builtin_amdgcn_rsqf(ssa[j]), inv_eps);   // 1 / max(|k|, eps)
+            rho[j] = a.raw_keys ? 1.0f : fminf(__builtin_amdgcn_rsqf(ssa[j]), inv_eps);   // 1 / max(|k|, eps)
             xs[j] = bt[j] * rho[j];
         }
         unsigned char* sKH = buf;                   // rho k         (A of G)
@@ -734,9 +735,6 @@ __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
         }
         return;
     }
-    // one-frame path: copy S_in to the workspace (the state update reads the
-    // copy, so S_out may alias S_in); the consumer waves do it while the
-    // producers fill the pipeline
     // one-frame path: copy S_in to the workspace (the state update reads the
     // copy, so S_out may alias S_in).  Each consumer thread loads its first
     // 16-byte piece before the pipeline and stores it after, so nothing waits
@@ -1458,7 +1456,8 @@ __global__ __launch_bounds__(64 * (D / 16), 2) void frame_step_kernel(ScanArgs a
             n0 = group_sum<GPT>(n0);
             n1 = group_sum<GPT>(n1);
             // 1 / max(|k|, eps) and beta (logits: sigmoid / N), as frame_gram forms them
-            const float r0 = fminf(__builtin_amdgcn_rsqf(n0), inv_eps), r1 = fminf(__builtin_amdgcn_rsqf(n1), inv_eps);
+            const float r0 = a.raw_keys ? 1.0f : fminf(__builtin_amdgcn_rsqf(n0), inv_eps);
+            const float r1 = a.raw_keys ? 1.0f : fminf(__builtin_amdgcn_rsqf(n1), inv_eps);
             const float be0 = a.logits ? sigmoid_f(q2.b0) * inv_n : q2.b0;
             const float be1 = a.logits ? sigmoid_f(q2.b1) * inv_n : q2.b1;
             const float s0b = be0 * r0, s1b = be1 * r1;

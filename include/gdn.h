@@ -70,6 +70,14 @@ typedef enum gdn_dtype { GDN_BF16 = 0, GDN_F32 = 1 } gdn_dtype;
 
 /* beta and alpha hold logits; the library applies sigmoid(.)/N and sigmoid(.). */
 #define GDN_FLAG_GATES_ARE_LOGITS 0x1u
+/* Use the keys as given: k^_i = k_i, no L2 normalisation (and eps is unused).
+ * Key normalisation is on by default (flag clear), which is the operator above;
+ * a caller whose keys already have unit norm may skip it with this flag. */
+#define GDN_FLAG_NO_KEY_NORM 0x2u
+
+/* Determinism.  Every call is bitwise reproducible: the same inputs on the same
+ * device give the same bits, whatever ran before (no atomics, no data-dependent
+ * scheduling).  There is no flag for it because there is no other mode. */
 
 typedef struct gdn_desc {
     int32_t B, H, F, N, Dk, Dv; /* batch, heads, frames, tokens per frame, key/value dims */
@@ -80,7 +88,18 @@ typedef struct gdn_desc {
 
 /* Bytes of device workspace gdn_frame_scan_fwd / gdn_frame_step need for this
  * descriptor (0 when none is needed).  Returns 0 for an invalid descriptor;
- * the compute calls report the reason. */
+ * the compute calls report the reason.
+ *
+ * The workspace is required, not optional.  The scan runs as three kernels
+ * (per-frame Gram and U products over all frames at once, then the serial
+ * state recurrence, then the per-frame output products), which hand per-frame
+ * d x d operands to each other through this memory: per (b, h, frame) about
+ * 10*Dk*Dv bytes in bf16 mode (12*Dk*Dv in fp32 mode), for at most 256 frames
+ * per launch, plus one fp32 state per (b, h).  At B1 H16 d128 and 121 frames
+ * that is 318 MB.  A single persistent kernel holding the state on chip would
+ * need none, but it would run on B*H*Dv/16 workgroups (128 at that shape, half
+ * the GPU) and re-read every token of K once per row tile of the state; the
+ * split design streams each token byte once on every compute unit. */
 size_t gdn_workspace_size(const gdn_desc* d);
 
 /* Whole-clip scan: frames 1..F of every (b, h) from S0 (NULL means zeros).
@@ -100,8 +119,11 @@ gdn_status gdn_frame_scan_fwd(const gdn_desc* d,
  * streaming workflow calls it once per incoming latent frame (the WorldFoundry
  * "SANA-WM" page, section "What it is for": the streaming pipeline advances
  * the rollout window by window).  For bf16 with Dk <= 64, a state kept in two
- * buffers that alternate as S_in and S_out runs as one kernel launch; an
- * in-place S_out == S_in takes two (the state is first copied aside). */
+ * buffers that alternate as S_in and S_out runs as one kernel launch and uses
+ * no workspace; an in-place S_out == S_in (and every other shape) takes two
+ * launches that pass fp32 partial sums of G and U, one per token range, and a
+ * copy of S_in through the workspace, which is why this call takes workspace
+ * arguments (gdn_workspace_size with F == 1 gives its size). */
 gdn_status gdn_frame_step(const gdn_desc* d,
                           const void* q, const void* k, const void* v,
                           const float* beta, const float* alpha,

@@ -25,7 +25,9 @@
  * Every token of a frame sees the same S_{f-1} (the frame is one step) and the
  * output of a frame reads the post-update state S_f.  With N = 1 this is the
  * token-level gated delta rule.  With gates_are_logits the inputs are logits:
- * alpha = sigmoid(a), beta = sigmoid(b) / N.
+ * alpha = sigmoid(a), beta = sigmoid(b) / N.  With normalize_k == 0 the keys
+ * are used as given (k^_i = k_i), the library's option for callers whose keys
+ * already have unit norm.
  *
  * Layouts (row-major, last index fastest):
  *     q, k  [B][F][N][H][Dk]      v, o  [B][F][N][H][Dv]
@@ -51,7 +53,7 @@ int gdn_oracle_scan(int B, int H, int F, int N, int Dk, int Dv,
                     const double *q, const double *k, const double *v,
                     const double *beta, const double *alpha,
                     const double *S0, double eps, int gates_are_logits,
-                    double *o, double *S_final)
+                    int normalize_k, double *o, double *S_final)
 {
     if (B < 0 || H < 0 || F < 0 || N < 0 || Dk < 1 || Dv < 1 || !(eps > 0.0))
         return -1;
@@ -88,6 +90,7 @@ int gdn_oracle_scan(int B, int H, int F, int N, int Dk, int Dv,
                     for (int c = 0; c < Dk; ++c) ss += ki[c] * ki[c];
                     double nrm = sqrt(ss);
                     double den = nrm > eps ? nrm : eps;
+                    if (!normalize_k) den = 1.0;   /* keys used as given */
                     for (int c = 0; c < Dk; ++c) kh[(size_t)i * Dk + c] = ki[c] / den;
                     double bi = beta[tok0 + (size_t)i * sN + h];
                     bt[i] = gates_are_logits ? sigmoid(bi) / (double)N : bi;

@@ -18,7 +18,7 @@ from test_gpu_parity import check, oracle_ref
 pytestmark = pytest.mark.gpu
 
 
-def step_gpu(w, *, logits=False, in_place=False, s0=True, beta=None, alpha=None):
+def step_gpu(w, *, logits=False, in_place=False, s0=True, beta=None, alpha=None, raw_keys=False):
     q, k, v, b, a, S0 = inputs.to_torch(w, "cuda")
     if beta is not None:
         b = torch.from_numpy(np.ascontiguousarray(beta, dtype=np.float32)).cuda()
@@ -30,7 +30,7 @@ def step_gpu(w, *, logits=False, in_place=False, s0=True, beta=None, alpha=None)
     else:
         S_out = torch.full((w.B, w.H, w.Dv, w.Dk), float("nan"), dtype=torch.float32, device="cuda")
     o, S = api.frame_step(q[:, 0], k[:, 0], v[:, 0], b[:, 0], a[:, 0], S_in, S_out=S_out,
-                          gates_are_logits=logits)
+                          gates_are_logits=logits, normalize_keys=not raw_keys)
     torch.cuda.synchronize()
     assert S.data_ptr() == S_out.data_ptr()
     return o.float().cpu().numpy()[:, None], S.cpu().numpy()
@@ -100,3 +100,16 @@ def test_scan_of_one_frame_uses_the_same_path():
     ro, rS = oracle_ref(w)
     check(o1.float().cpu().numpy(), ro, "bf16", "O")
     check(S1.cpu().numpy(), rS, "bf16", "S_F")
+
+
+@pytest.mark.parametrize("D,in_place", [(64, False), (64, True), (128, False)])
+def test_step_raw_keys(D, in_place):
+    """Keys used as given, on the one-launch path (D = 64, two buffers) and on
+    the two-launch path (in place, and D = 128)."""
+    w = inputs.make(2, 3, 1, 200, D, dtype="bf16", seed=460 + D, s0_std=0.05)
+    scale = np.random.default_rng(461).uniform(0.3, 0.6, w.k.shape[:-1] + (1,)).astype(np.float32)
+    w.k = inputs.round_bf16(w.k * scale)
+    o, S = step_gpu(w, in_place=in_place, raw_keys=True)
+    ro, rS = oracle_ref(w, raw_keys=True)
+    check(o, ro, "bf16", "O")
+    check(S, rS, "bf16", "S_out")

@@ -40,9 +40,10 @@ def rand_case(B=1, H=2, F=3, N=5, Dk=6, Dv=5, seed=0, s0=True):
 
 
 # ---------------------------------------------------------------- independent routes
-def token_rule(q, k, v, beta, alpha, S0, eps=1e-6):
+def token_rule(q, k, v, beta, alpha, S0, eps=1e-6, normalize=True):
     """Textbook gated delta rule, one token per step (valid when N == 1):
-    s <- alpha * (s - beta (s k^) k^T) + beta v k^T ;  o = s q."""
+    s <- alpha * (s - beta (s k^) k^T) + beta v k^T ;  o = s q.
+    normalize=False takes k^ = k (the keys as given)."""
     B, F, N, H, Dk = q.shape
     assert N == 1
     Dv = v.shape[-1]
@@ -53,7 +54,8 @@ def token_rule(q, k, v, beta, alpha, S0, eps=1e-6):
             s = np.zeros((Dv, Dk)) if S0 is None else S0[b, h].copy()
             for f in range(F):
                 kk = k[b, f, 0, h]
-                kk = kk / max(np.linalg.norm(kk), eps)
+                if normalize:
+                    kk = kk / max(np.linalg.norm(kk), eps)
                 bt, al = beta[b, f, 0, h], alpha[b, f, h]
                 s = al * (s - bt * np.outer(s @ kk, kk)) + bt * np.outer(v[b, f, 0, h], kk)
                 o[b, f, 0, h] = s @ q[b, f, 0, h]
@@ -61,7 +63,7 @@ def token_rule(q, k, v, beta, alpha, S0, eps=1e-6):
     return o, Sf
 
 
-def rank_one_route(q, k, v, beta, alpha, S0, eps=1e-6):
+def rank_one_route(q, k, v, beta, alpha, S0, eps=1e-6, normalize=True):
     """Frame update as a sum of per-token rank-one corrections, all read from
     the same frozen state; no Gram matrix is ever formed."""
     B, F, N, H, Dk = q.shape
@@ -76,7 +78,8 @@ def rank_one_route(q, k, v, beta, alpha, S0, eps=1e-6):
                 write = np.zeros((Dv, Dk))
                 for i in range(N):
                     kk = k[b, f, i, h]
-                    kk = kk / max(np.linalg.norm(kk), eps)
+                    if normalize:
+                        kk = kk / max(np.linalg.norm(kk), eps)
                     bt = beta[b, f, i, h]
                     corr += bt * np.outer(s @ kk, kk)
                     write += bt * np.outer(v[b, f, i, h], kk)
@@ -172,6 +175,34 @@ def test_unrolled_product_form():
     o, S = oracle.scan(q, k, v, beta, alpha, S0)
     o2, S2 = unrolled_route(q, k, v, beta, alpha, S0)
     assert rel(o, o2) < 1e-12 and rel(S, S2) < 1e-12
+
+
+# ---------------------------------------------------------------- keys as given
+@pytest.mark.parametrize("seed", [0, 1])
+def test_raw_keys_token_rule_and_rank_one(seed):
+    """normalize_keys=False: the textbook rule and the rank-one route with the
+    raw (non-unit) keys, whose norms here lie well away from 1."""
+    q, k, v, beta, alpha, S0 = rand_case(B=1, H=2, F=5, N=1, Dk=5, Dv=4, seed=seed)
+    k *= np.random.default_rng(seed + 30).uniform(0.3, 0.6, k.shape[:-1] + (1,))
+    o, S = oracle.scan(q, k, v, beta, alpha, S0, normalize_keys=False)
+    o2, S2 = token_rule(q, k, v, beta, alpha, S0, normalize=False)
+    assert rel(o, o2) < 1e-12 and rel(S, S2) < 1e-12
+    o3, S3 = oracle.scan(q, k, v, beta, alpha, S0)
+    assert rel(S3, S) > 1e-2                      # the two modes really differ
+    q, k, v, beta, alpha, S0 = rand_case(B=1, H=2, F=3, N=6, Dk=5, Dv=4, seed=seed + 5)
+    k *= 0.4
+    o, S = oracle.scan(q, k, v, beta, alpha, S0, normalize_keys=False)
+    o2, S2 = rank_one_route(q, k, v, beta, alpha, S0, normalize=False)
+    assert rel(o, o2) < 1e-12 and rel(S, S2) < 1e-12
+
+
+def test_raw_unit_keys_equal_normalised():
+    """With keys of unit norm, using them as given equals normalising them."""
+    q, k, v, beta, alpha, S0 = rand_case(B=2, H=2, F=3, N=5, Dk=6, Dv=4, seed=31)
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    o, S = oracle.scan(q, k, v, beta, alpha, S0)
+    o2, S2 = oracle.scan(q, k, v, beta, alpha, S0, normalize_keys=False)
+    assert rel(o2, o) < 1e-14 and rel(S2, S) < 1e-14
 
 
 # ---------------------------------------------------------------- closed forms
