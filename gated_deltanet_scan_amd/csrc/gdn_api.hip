@@ -171,9 +171,10 @@ template <typename T, int D>
 gdn_status launch_state(ScanArgs a, hipStream_t stream) {
     using SC = gdn::StateCfg<T, D>;
     const int units = a.B * a.H;
-    const int grid = 8 * ((units + 7) / 8) * SC::RG;
+    // one workgroup per (b, h, row slab); the slabs of a unit share an XCD
+    const int grid = 8 * ((units + 7) / 8) * SC::ET;
     ProfScope ps(K_STATE, stream);
-    hipLaunchKernelGGL((gdn::state_scan_kernel<T, D>), dim3(grid), dim3(SC::NW * 64), 0, stream, a);
+    hipLaunchKernelGGL((gdn::state_scan_kernel<T, D>), dim3(grid), dim3(SC::NTH), 0, stream, a);
     return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 

@@ -8,10 +8,10 @@
 //                 normalises keys, and forms  Gm_f = -alpha_f * G_f  and U_f
 //                 with MFMA (fp32 accumulate).  Writes them to the workspace in
 //                 the exact operand layouts state_scan loads.
-//   state_scan    one workgroup per (b, h, 16-row tile of S): keeps its rows of
-//                 S resident across the sequential frame loop and applies
+//   state_scan    one wave per (b, h, 16-row slab of S): keeps its rows of S
+//                 in registers across the sequential frame loop and applies
 //                 S <- alpha S + S Gm_f + U_f.  Rows of S evolve independently,
-//                 so tiles never communicate.  Emits S_f for every frame.
+//                 so slabs never communicate.  Emits S_f for every frame.
 //   frame_output  one workgroup per (b, h, f, token range): O_f = Q_f S_f^T.
 //
 // G and U contract over tokens, so frame_gram transposes K and V through LDS;
@@ -19,12 +19,19 @@
 // memory, so their operands load straight from global memory.
 //
 // MFMA fragment convention (v_mfma_f32_16x16x32_bf16): lane l = 16*g + r holds,
-// for operand A (16 x 32), row r and contraction indices 8g..8g+7; for operand
-// B (32 x 16), column r and the same 8 contraction indices.  A and B always use
-// the same contraction order, so the product is exact whatever order the
-// hardware assigns inside a lane.  The 16x16 fp32 result sits in lane l as rows
+// for operand A (16 x 32), row r and eight contraction indices; for operand B
+// (32 x 16), column r and the same eight.  A and B always use the same
+// contraction order, so the product is exact whatever order the hardware
+// assigns inside a lane.  The 16x16 fp32 result sits in lane l as rows
 // 4g..4g+3 of column r.  The fp32 I/O mode keeps the same 8-value fragments and
 // issues eight v_mfma_f32_16x16x4_f32, one per fragment element.
+//
+// Two contraction orders are used.  Natural: lane group g takes indices
+// 8g..8g+7 of a 32-wide step.  Split: lane group g takes 4g..4g+3 and
+// 16+4g..16+4g+3, i.e. the four values a lane holds in each of two adjacent
+// 16x16 results.  The state products (S Gm in the recurrence, Q S^T in the
+// output pass) contract over the columns of S in the split order, so that a
+// lane's own two result blocks of S are already its operand fragment.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -65,40 +72,6 @@ __device__ __forceinline__ float group_sum(float x) {
 // Two floats to two bf16 (round to nearest even) in one dword, x in the low half.
 __device__ __forceinline__ uint32_t pack_bf16x2(float x, float y) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x, y}, bf16x2));
-}
-// Remainder code of x against its bf16 rounding h (bits in the low half of
-// hb): x - h is at most half a bf16 ulp, 2^(E-134) for h's biased exponent E;
-// the code counts it in 1/256 ulps, rounded to nearest and clamped to int8.
-// h plus rem_value(code) carries x to about 2^-16 relative, in 3 bytes.
-__device__ __forceinline__ int rem_code(float x, uint32_t hb) {
-    const int e = (int)((hb >> 7) & 0xffu);
-    const float t = __builtin_rintf(__builtin_amdgcn_ldexpf(x - bf2f((uint16_t)hb), 142 - e));
-    return (int)__builtin_fminf(__builtin_fmaxf(t, -127.0f), 127.0f);
-}
-__device__ __forceinline__ float rem_value(int code, uint32_t hb) {
-    return __builtin_amdgcn_ldexpf((float)code, (int)((hb >> 7) & 0xffu) - 142);
-}
-// byte i (signed) of a dword of codes
-__device__ __forceinline__ int code_at(uint32_t w, int i) { return (int)(w << (24 - 8 * i)) >> 24; }
-__device__ __forceinline__ uint32_t pack_codes(int c0, int c1, int c2, int c3) {
-    return (uint32_t)(c0 & 0xff) | (uint32_t)(c1 & 0xff) << 8 | (uint32_t)(c2 & 0xff) << 16 | (uint32_t)c3 << 24;
-}
-// The remainders of an 8-value bf16 fragment as a bf16 fragment (exact: a
-// code times a power of two has at most 8 significant bits).
-__device__ __forceinline__ u32x4 rem_frag(u32x4 h, u32x2 c) {
-    u32x4 out;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const uint32_t w = c[j >> 1];
-        out[j] = pack_bf16x2(rem_value(code_at(w, 2 * (j & 1)), h[j] & 0xffffu),
-                             rem_value(code_at(w, 2 * (j & 1) + 1), h[j] >> 16));
-    }
-    return out;
-}
-// Codes of four fp32 values against their bf16 pair dwords h01, h23.
-__device__ __forceinline__ uint32_t codes4(f32x4 x, uint32_t h01, uint32_t h23) {
-    return pack_codes(rem_code(x[0], h01 & 0xffffu), rem_code(x[1], h01 >> 16), rem_code(x[2], h23 & 0xffffu),
-                      rem_code(x[3], h23 >> 16));
 }
 // Frames per state_scan launch (alpha values are staged in LDS).
 constexpr int kMaxChunkFrames = 256;
@@ -195,15 +168,17 @@ template <> struct IO<float> {
 // as 64 consecutive 16-byte lane slots (bf16: one 1 KiB block; fp32: two
 // 1 KiB blocks with values 0-3 and 4-7 of every lane), so that every 64-lane
 // load or store of it touches one contiguous KiB.
-//   Gm^T   operand of state_scan: rows e, contraction c; Gm^T[e][c] = -alpha G[c][e]
-//          (one plane: bf16, rounded to nearest even, or fp32)
+//   Gm^T   operand A of state_scan: fragment (e-tile j, step kk), lane 16g+r:
+//          Gm^T[16j + r][c] for the split order's c of step kk, where
+//          Gm^T[e][c] = -alpha G[c][e] (bf16, rounded to nearest even, or
+//          fp32).  At D = 16 the second half of each slot is never written.
 //   U      tiles in the state's register layout in state_scan: block (e-tile,
 //          a-tile) holds, in lane 16g+r, U[16a_t + r][16e_t + 4g + t] for
 //          t = 0..3 (fp32)
-//   S_f    operand of frame_output: rows a, contraction e (bf16 mode: the bf16
-//          plane, then its remainder codes (rem_code), 8 bytes per lane slot:
-//          three bytes per value at about 2^-16 relative precision; fp32
-//          mode: one fp32 plane)
+//   S_f    operand A of frame_output: fragment (a-tile, step kk), lane 16g+r:
+//          S_f[16a_t + r][c] in the split order, fp32 in both modes (2 KiB
+//          per fragment, values 0-3 and 4-7 of every lane in two 1 KiB
+//          halves); frame_output splits it into bf16 high and low parts
 template <typename T, int D> struct WS {
     static constexpr bool B16 = sizeof(T) == 2;
     static constexpr int KS = (D + 31) / 32;                  // contraction fragments per tile
@@ -213,18 +188,10 @@ template <typename T, int D> struct WS {
     static constexpr size_t gm_off = 0;
     static constexpr size_t ut_off = OPND;
     static constexpr size_t sp_off = ut_off + (size_t)RT * RT * 1024;
-    static constexpr size_t sc_rel = OPND;                    // S codes, after the S plane (bf16)
-    // bf16: the codes take half a plane; the item keeps a whole one, which
-    // measured ~10 us faster for state_scan at the full-minute shape than
-    // items 16 KiB smaller (the per-head stride of its stores)
-    static constexpr size_t item_bytes = sp_off + (B16 ? 2 : 1) * OPND;
+    static constexpr size_t item_bytes = sp_off + (size_t)RT * KS * 2048;   // S_f is fp32
     // byte offset of lane `lane`'s slot in operand fragment (tile, kt), half h (fp32)
     __device__ static __forceinline__ uint32_t frag_off(int tile, int kt, int h, int lane) {
         return (uint32_t)((tile * KS + kt) * FRAG) + (uint32_t)(h * 1024 + lane * 16);
-    }
-    // the same slot's 8 remainder codes in the code plane of S_f (bf16)
-    __device__ static __forceinline__ uint32_t code_off(int tile, int kt, int lane) {
-        return (uint32_t)((tile * KS + kt) * 512) + (uint32_t)(lane * 8);
     }
 };
 
@@ -232,7 +199,7 @@ template <typename T, int D> struct WS {
 constexpr size_t ws_item_bytes(int esz, int D) {
     const size_t KS = (size_t)(D + 31) / 32, RT = (size_t)D / 16;
     const size_t opnd = RT * KS * (esz == 2 ? 1024 : 2048);
-    return (esz == 2 ? 3 : 2) * opnd + RT * RT * 1024;
+    return opnd + RT * RT * 1024 + RT * KS * 2048;
 }
 static_assert(ws_item_bytes(2, 16) == WS<uint16_t, 16>::item_bytes && ws_item_bytes(2, 128) == WS<uint16_t, 128>::item_bytes &&
                   ws_item_bytes(4, 16) == WS<float, 16>::item_bytes && ws_item_bytes(4, 64) == WS<float, 64>::item_bytes,
@@ -605,9 +572,6 @@ __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
     // resource: each block's offset splits into a compile-time part (scalar
     // soffset) and one per-lane part, so no per-block addresses stay live.
     using W = WS<T, D>;
-    // per-lane parts: Gm slot 16*(2*(gb%2) + g/2) + r holding values 4*(g%2)..
-    const uint32_t gm_lane = sizeof(T) == 2 ? (uint32_t)(256 * (g >> 1) + 16 * r + 8 * (g & 1))
-                                            : (uint32_t)(1024 * (g & 1) + 256 * (g >> 1) + 16 * r);
     const uint32_t u_lane = (uint32_t)(lane * 16);
     // alpha of item k, loaded one item ahead of its epilogue
     auto load_alpha = [&](int k) {
@@ -655,17 +619,17 @@ __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
 #pragma unroll
                 for (int j = 0; j < C::TC; ++j) {
                     const int jb = b_row0 + j;
-                    // lane (r, g) holds G[16gb + 4g + t][16jb + r] = Gm^T[e][c] with e = 16jb + r:
-                    // fragment (e-tile jb, kt = gb/2), lane slot 16*(2*(gb%2) + g/2) + r,
-                    // values 4*(g%2) + t
+                    // lane (r, g) holds G[16gb + 4g + t][16jb + r] = Gm^T[e][c] with e = 16jb + r
+                    // and c = 32(gb/2) + 16(gb%2) + 4g + t: in the split order that is
+                    // fragment (e-tile jb, step gb/2), this lane's own slot, half gb%2
                     const f32x4 m = acc[i][j] * (-al);
-                    const uint32_t blk = (uint32_t)(W::gm_off + (size_t)(jb * W::KS + (gb >> 1)) * W::FRAG +
-                                                    512 * (gb & 1));
+                    const uint32_t blk = (uint32_t)(W::gm_off + (size_t)(jb * W::KS + (gb >> 1)) * W::FRAG);
                     if constexpr (sizeof(T) == 2)
                         __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf16x2(m[0], m[1]), pack_bf16x2(m[2], m[3])},
-                                                              rw, gm_lane, blk, kWorkspaceStore);
+                                                              rw, u_lane, blk + 8 * (gb & 1), kWorkspaceStore);
                     else
-                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, m), rw, gm_lane, blk, kWorkspaceStore);
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, m), rw, u_lane,
+                                                               blk + 1024 * (gb & 1), kWorkspaceStore);
                 }
             }
         } else {
@@ -779,236 +743,204 @@ __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
 
 // ================================================================== state_scan
 template <typename T, int D> struct StateCfg {
-    static constexpr int RT = D / 16;                   // row tiles per (b, h)
-    static constexpr int RTW = 1;                       // row tiles per workgroup (2 measured slower)
-    static constexpr int RG = RT / RTW;                 // workgroups per (b, h)
-    static constexpr int NW = D / 16;                   // waves: one 16-column tile each
+    static constexpr bool B16 = sizeof(T) == 2;
+    static constexpr int ET = D / 16;                   // 16-column blocks of a slab (and slabs per state)
     static constexpr int KS = (D + 31) / 32;            // 32-wide contraction steps
-    static constexpr int PADB = 16;                     // LDS row padding (bytes)
-    static constexpr int ROWB = D * IO<T>::bytes + PADB;
-    // frames of operands in flight: the ring must fit the 6-bit vector-memory
-    // counter (63 outstanding loads and stores per wave) or every frame drains
-    // it, and the register file (fp32 fragments are twice as wide)
-    static constexpr int LOADS = (sizeof(T) == 2 ? KS : 2 * KS) + RTW;   // per frame
-    static constexpr int PDMAX = sizeof(T) == 2 ? 8 : 4;
-    static constexpr int PD = (48 / LOADS) < PDMAX ? (48 / LOADS) : PDMAX;
+    static constexpr int NC = ET >= 2 ? ET / 2 : 1;     // waves; wave c owns blocks 2c, 2c+1
+    static constexpr int BPW = ET / NC;                 // blocks per wave (2, or 1 at D = 16)
+    static constexpr int FRAGB = B16 ? 1 : 2;           // 16-byte loads per Gm fragment and lane
+    static constexpr int LOADS = BPW * KS * FRAGB + BPW;    // per wave and frame: Gm^T rows, U blocks
+    static constexpr int STORES = 2;                    // per wave and frame: its half-fragments of S_f
+    // frames of operands in flight: the 6-bit vector-memory counter (63) and
+    // ~256 registers bound the ring
+    static constexpr int PD0 = 60 / (LOADS + STORES);
+    static constexpr int PDR = 256 / (LOADS * 4);
+    static constexpr int PD = (PD0 < PDR ? PD0 : PDR) > 8 ? 8 : (PD0 < PDR ? PD0 : PDR);
+    static constexpr int NTH = 64 * NC;
     static_assert(PD >= 2, "ring too shallow");
 };
 
-// One workgroup owns RTW consecutive 16-row tiles of one (b, h) state (rows
-// [16*RTW*rg, 16*RTW*(rg+1))); wave w owns columns [16w, 16w+16) of them.
-// Rows of S evolve independently, so workgroups never communicate.  Per frame:
-//   S_f = alpha*S + U_f + bf16(S) Gm   (bf16 MFMA, fp32 accumulate)
-//   (fp32 mode: S Gm with fp32 MFMA)
-// The product is formed transposed, (S Gm)^T = Gm^T S^T, with the Gm fragment
-// as operand A and the S rows as operand B, so each lane holds four
-// consecutive columns of one row of S: the state's LDS, workspace and global
-// accesses are then 8 and 16 bytes wide instead of 2 and 4.
-// Gm and S enter the product rounded to bf16 once: that relative error
-// (2^-9 of S Gm, itself small next to alpha S) is of the size G already
-// carries from its bf16 operands and far below the error of U, so a low part
-// of Gm or of S in this product buys no accuracy (frame_output does take S_f
-// with a low part: the remainder codes below).  Each 32-wide contraction step
-// accumulates into its own register set, so the MFMAs of a frame do not wait
-// on each other.  S stays in fp32 registers; its bf16 rounding is
-// double-buffered in LDS as the MFMA operand (one barrier per frame); the
-// previous frame's bf16 plane is copied to the workspace for frame_output, and
-// every lane stores the remainder codes of its own four values of S, while
-// this frame's MFMAs run.
-// Every workgroup of a head reads all of Gm_f (32 KiB in bf16) each
-// frame, mostly from L2.  A frame takes about 0.55 us at D = 128 (bf16); the
-// operands of the next PD frames are in flight in a register ring, deep
-// enough that frames whose workspace has left the last-level cache do not
-// stall (with 4 frames in flight those ran at about 1.2 us).
+// One workgroup per slab of 16 rows of one (b, h) state, S[16 at + r][*].
+// Its NC waves split the slab's columns: wave c holds blocks 2c and 2c+1 as
+// fp32 result blocks in registers (lane 16g+r of block j: columns 16j + 4g ..
+// +3 of row 16 at + r) and per frame applies
+//     S_f = alpha S + U_f + bf16(S) Gm        (Gm = -alpha G, bf16 MFMA)
+// to them, formed transposed, (S Gm)^T = Gm^T S^T: operand A a Gm^T fragment
+// of its rows, operand B a bf16 fragment of S in the split contraction order
+// (blocks 2kk and 2kk+1 for step kk: wave c's own two blocks form fragment c,
+// so S never needs re-laying out).  Each wave then writes its fragment of the
+// new S to a double-buffered LDS exchange and reads the others' after the
+// frame's one barrier.  Gm and S enter the product rounded to bf16 once: that
+// relative error (2^-9 of S Gm, itself small next to alpha S) is of the size
+// G already carries from its bf16 operands and far below the error of U, so a
+// low part of Gm or of S in this product buys no accuracy.  (fp32 mode: fp32
+// MFMA and fp32 fragments.)  Every wave also stores its blocks of S_f as an
+// fp32 plane for frame_output.
+// Each wave loads its own operands (its rows of Gm_f^T and its blocks of U_f)
+// PD frames ahead into a register ring; splitting a slab over several waves
+// is what keeps enough loads in flight, one wave's counter holding little more
+// than one frame.  Rows of S evolve independently, so the workgroups of a
+// state never communicate; the slabs of a head share an XCD (workgroup index
+// mod 8), so its Gm^T rows come from one L2.
 template <typename T, int D>
-__global__ __launch_bounds__(4 * D, 1) void state_scan_kernel(ScanArgs a) {  // NW*64 threads
+__global__ __launch_bounds__(256, 1) void state_scan_kernel(ScanArgs a) {   // NTH <= 256 threads
     using C = StateCfg<T, D>;
     using io = IO<T>;
     using frag = typename io::frag;
-    constexpr int ROWS = 16 * C::RTW;
-    constexpr int PLANE = ROWS * C::ROWB;
-    __shared__ __attribute__((aligned(16))) unsigned char sS[2][PLANE];
+    using W = WS<T, D>;
+    static_assert(C::NTH <= 256, "block size");
+    __shared__ __attribute__((aligned(16))) unsigned char sX[2][C::KS][64 * sizeof(frag)];
     __shared__ float sAlpha[kMaxChunkFrames];
 
     const int units = a.B * a.H;
-    const int id = xcd_remap(blockIdx.x, C::RG, units * C::RG);
+    const int id = xcd_remap(blockIdx.x, C::ET, units * C::ET);
     if (id < 0) return;
-    const int rg = id % C::RG;
-    const int bh = id / C::RG;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int at = id % C::ET;                          // row slab
+    const int bh = id / C::ET;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int c = __builtin_amdgcn_readfirstlane(tid >> 6);   // this wave's fragment
     const int r = lane & 15, g = lane >> 4;
-    const int a0 = rg * ROWS;                           // first state row of this workgroup
     const int h = bh % a.H, b = bh / a.H;
     const int Fc = a.Fc;
-    const int col0 = wave * 16 + 4 * g;                 // this lane's state columns col0..col0+3
+    const int row = 16 * at + r;
+    const uint32_t lo16 = (uint32_t)(lane * 16);
 
-    for (int i = tid; i < Fc; i += C::NW * 64) {
+    for (int i = tid; i < Fc; i += C::NTH) {
         const float x = a.alpha[((size_t)b * a.F + a.f0 + i) * a.H + h];
         sAlpha[i] = a.logits ? sigmoid_f(x) : x;
     }
+    // this unit's workspace items through one buffer resource
+    const size_t item0 = (size_t)bh * Fc;
+    const rsrc_t rws = make_rsrc(a.ws + item0 * W::item_bytes, (uint32_t)(Fc * W::item_bytes));
 
-    // ---- initial state: registers (lane (r, g) of tile i: row a0 + 16i + r,
-    //      columns col0..col0+3) and LDS (row-major planes, operand layout)
-    f32x4 S[C::RTW];
-    const float* sin = a.S_in ? a.S_in + (size_t)bh * D * D : nullptr;
+    // this wave's blocks of S (fp32) and the fragment they form
+    f32x4 S[C::BPW];
+    const float* sin = a.S_in ? a.S_in + (size_t)bh * D * D + (size_t)row * D : nullptr;
 #pragma unroll
-    for (int i = 0; i < C::RTW; ++i)
-        S[i] = sin ? *reinterpret_cast<const f32x4*>(sin + (size_t)(a0 + 16 * i + r) * D + col0)
-                   : f32x4{0, 0, 0, 0};
-    auto put_lds = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < C::RTW; ++i) {
-            const int off = (16 * i + r) * C::ROWB + col0 * io::bytes;
-            if constexpr (sizeof(T) == 2)
-                *reinterpret_cast<u32x2*>(&sS[buf][off]) = u32x2{pack_bf16x2(S[i][0], S[i][1]), pack_bf16x2(S[i][2], S[i][3])};
-            else
-                *reinterpret_cast<f32x4*>(&sS[buf][off]) = S[i];
-        }
+    for (int q = 0; q < C::BPW; ++q) {
+        const int jb = c * C::BPW + q;
+        S[q] = sin ? *reinterpret_cast<const f32x4*>(sin + 16 * jb + 4 * g) : f32x4{0, 0, 0, 0};
+    }
+    auto own_frag = [&]() {
+        const f32x4 x = S[0];
+        const f32x4 y = C::BPW > 1 ? S[C::BPW - 1] : f32x4{0, 0, 0, 0};
+        if constexpr (C::B16)
+            return frag{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+        else
+            return frag{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
     };
-    put_lds(0);
+    auto put_x = [&](int buf, const frag& f) { *reinterpret_cast<frag*>(&sX[buf][c][lane * sizeof(frag)]) = f; };
+    auto get_x = [&](int buf, int kk) { return *reinterpret_cast<const frag*>(&sX[buf][kk][lane * sizeof(frag)]); };
+    put_x(0, own_frag());
 
     struct Ops {
-        frag bh_[C::KS];          // Gm for this wave's 16 columns
-        f32x4 u[C::RTW];          // U of each row tile in the state's register layout
+        frag gm[C::KS][C::BPW];
+        f32x4 u[C::BPW];
     };
-    const size_t item0 = (size_t)bh * a.Fc;
-    using W = WS<T, D>;
-    // Loads of frame fl (always a valid frame: callers clamp); every load is
-    // one contiguous KiB of a fragment-major workspace matrix.
-    auto load_ops = [&](int fl, Ops& o) {
-        const unsigned char* wsi = a.ws + (item0 + fl) * W::item_bytes;
+    auto load_ops = [&](int fl, Ops& o) {             // fl is always a valid frame
+        const uint32_t base = (uint32_t)fl * (uint32_t)W::item_bytes;
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
-            if constexpr (sizeof(T) == 2) {
-                o.bh_[ks] = *reinterpret_cast<const u32x4*>(wsi + W::gm_off + W::frag_off(wave, ks, 0, lane));
-            } else {
-                const f32x4 lo = *reinterpret_cast<const f32x4*>(wsi + W::gm_off + W::frag_off(wave, ks, 0, lane));
-                const f32x4 hi = *reinterpret_cast<const f32x4*>(wsi + W::gm_off + W::frag_off(wave, ks, 1, lane));
-                o.bh_[ks] = f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        for (int kk = 0; kk < C::KS; ++kk)
+#pragma unroll
+            for (int q = 0; q < C::BPW; ++q) {
+                const int jb = c * C::BPW + q;
+                const uint32_t off = base + (uint32_t)(W::gm_off + (size_t)(jb * C::KS + kk) * W::FRAG);
+                if constexpr (C::B16) {
+                    o.gm[kk][q] = __builtin_amdgcn_raw_buffer_load_b128(rws, lo16, off, 0);
+                } else {
+                    const f32x4 lo = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rws, lo16, off, 0));
+                    const f32x4 hi = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rws, lo16, off + 1024, 0));
+                    o.gm[kk][q] = f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                }
             }
-        }
 #pragma unroll
-        for (int i = 0; i < C::RTW; ++i)
-            o.u[i] = *reinterpret_cast<const f32x4*>(wsi + W::ut_off +
-                                                     (size_t)(wave * W::RT + rg * C::RTW + i) * 1024 + lane * 16);
-    };
-    const bool kvalid = 8 * g < D || D >= 32;          // D = 16: lanes g >= 2 carry zeros
-
-    // Workspace S planes of this unit's frames through a buffer resource: the
-    // copy issued for frame -1 (before the first frame) falls outside it and
-    // is dropped, so the copy needs no branch.
-    const rsrc_t rsp = make_rsrc(a.ws + item0 * W::item_bytes, (uint32_t)(Fc * W::item_bytes));
-    constexpr int NH = sizeof(T) == 2 ? 1 : 2;          // 16-byte halves per lane slot
-    constexpr int SLOTS = C::RTW * C::KS * NH * 64;     // 16-byte lane slots per frame
-    auto copy_planes = [&](int fl, int buf) {           // S_fl, held in sS[buf], to frame fl
-        // frame -1 maps to 2 GiB: past the resource (at most 256 frames of at
-        // most 192 KiB) with no 32-bit overflow once the plane offset is added
-        const uint32_t base = fl >= 0 ? (uint32_t)fl * (uint32_t)W::item_bytes + (uint32_t)W::sp_off
-                                      : 0x80000000u;
-#pragma unroll
-        for (int x0 = 0; x0 < SLOTS; x0 += C::NW * 64) {
-            const int x = x0 + tid;
-            if (SLOTS % (C::NW * 64) == 0 || x < SLOTS) {
-                const int l = x & 63, hh = (x >> 6) % NH, kt = (x / (64 * NH)) % C::KS;
-                const int i = (x / (64 * NH * C::KS)) % C::RTW;
-                const int c0 = (kt * 32 + 8 * (l >> 4) + 4 * hh) % D;   // D = 16: upper lanes repeat
-                const u32x4 val =
-                    *reinterpret_cast<const u32x4*>(&sS[buf][(16 * i + (l & 15)) * C::ROWB + c0 * io::bytes]);
-                __builtin_amdgcn_raw_buffer_store_b128(val, rsp, base + W::frag_off(rg * C::RTW + i, kt, hh, l), 0,
-                                                       kStreamStore);
-            }
+        for (int q = 0; q < C::BPW; ++q) {
+            const int jb = c * C::BPW + q;
+            o.u[q] = __builtin_bit_cast(
+                f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                           rws, lo16, base + (uint32_t)(W::ut_off + (size_t)(jb * W::RT + at) * 1024), 0));
         }
     };
-    // bf16: the remainder codes of S_fl, straight from this lane's registers
-    // (four consecutive columns of one row: half of an 8-code slot), issued
-    // while the next frame's MFMAs run, so the encoding is off the frame's
-    // critical path and needs no LDS
-    auto store_codes = [&](int fl) {
-        if constexpr (sizeof(T) == 2) {
-            const uint32_t base = fl >= 0 ? (uint32_t)fl * (uint32_t)W::item_bytes + (uint32_t)(W::sp_off + W::sc_rel)
-                                          : 0x80000000u;
-#pragma unroll
-            for (int i = 0; i < C::RTW; ++i) {
-                const uint32_t h01 = pack_bf16x2(S[i][0], S[i][1]), h23 = pack_bf16x2(S[i][2], S[i][3]);
-                const int kt = col0 / 32, slot = 16 * ((col0 % 32) / 8) + r;
-                __builtin_amdgcn_raw_buffer_store_b32(
-                    codes4(S[i], h01, h23), rsp,
-                    base + W::code_off(rg * C::RTW + i, kt, slot) + (uint32_t)(4 * ((col0 / 4) & 1)), 0, kStreamStore);
-            }
-        }
+    // this wave's blocks of S_fl as half-fragments of the fp32 plane read by
+    // frame_output (fragment (at, c), halves 0 and 1; zeros past the slab at
+    // D = 16).  Frame -1 maps past the resource (at most 256 frames of at most
+    // 192 KiB) and is dropped, so the first call needs no branch.
+    auto store_state = [&](int fl) {
+        const uint32_t base = fl >= 0 ? (uint32_t)fl * (uint32_t)W::item_bytes + (uint32_t)W::sp_off : 0x80000000u;
+        const uint32_t off = base + (uint32_t)((at * C::KS + c) * 2048);
+        const f32x4 y = C::BPW > 1 ? S[C::BPW - 1] : f32x4{0, 0, 0, 0};
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, S[0]), rws, lo16, off, kStreamStore);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, y), rws, lo16, off + 1024, kStreamStore);
     };
-
-    // One frame.  The ring slot `o` is reloaded with frame `nx` as soon as this
-    // frame's MFMAs have been issued, so the loads stream through L1 while the
-    // wave writes the new state to LDS and waits at the barrier.
-    auto step = [&](int fl, Ops& o, int nx, bool reload) {
-        const int cur = fl & 1;                         // buffer holding S_{fl-1}
+    // One frame.  Every fragment of S_{fl-1}, this wave's own included, is read
+    // from the exchange buffer written before the previous barrier (register
+    // arrays are only ever indexed by compile-time constants: an index
+    // depending on the wave would put them in scratch memory).
+    auto step = [&](int fl, Ops& o, Ops& prev, int nx, bool reload) {
+        const int xb = fl & 1;                          // exchange buffer holding S_{fl-1}
+        frag bs[C::KS];
+#pragma unroll
+        for (int kk = 0; kk < C::KS; ++kk) bs[kk] = get_x(xb, kk);
+        if (reload) load_ops(nx, prev);                 // the slot frame fl-1 used
+        store_state(fl - 1);                            // S still holds S_{fl-1}
         const float al = sAlpha[fl];
-        f32x4 acc[C::KS][C::RTW];                       // one chain per contraction step
+        f32x4 acc[C::BPW];
 #pragma unroll
-        for (int i = 0; i < C::RTW; ++i) {
-            acc[0][i] = S[i] * al + o.u[i];
+        for (int q = 0; q < C::BPW; ++q) acc[q] = S[q] * al + o.u[q];
 #pragma unroll
-            for (int ks = 1; ks < C::KS; ++ks) acc[ks][i] = f32x4{0, 0, 0, 0};
-        }
+        for (int kk = 0; kk < C::KS; ++kk)
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
-            const int c0 = (ks * 32 + 8 * g) % D;
-            frag bhi = o.bh_[ks];
-            if constexpr (D < 32) {                    // unwritten upper lanes of the fragment
-                if (!kvalid) bhi = io::zero();
+            for (int q = 0; q < C::BPW; ++q) {
+                frag ga = o.gm[kk][q];
+                if constexpr (D < 32) {                 // the unwritten second half of each slot
+                    if constexpr (C::B16) {
+                        ga[2] = 0u;
+                        ga[3] = 0u;
+                    } else {
+                        ga[4] = ga[5] = ga[6] = ga[7] = 0.0f;
+                    }
+                }
+                io::mma(acc[q], ga, bs[kk]);            // (S Gm)^T += Gm^T S^T
             }
 #pragma unroll
-            for (int i = 0; i < C::RTW; ++i) {
-                const int ro = (16 * i + r) * C::ROWB;
-                frag ahi;
-                if constexpr (sizeof(T) == 2)
-                    ahi = *reinterpret_cast<const u32x4*>(&sS[cur][ro + c0 * 2]);
-                else
-                    ahi = io::load(reinterpret_cast<const float*>(&sS[cur][ro + c0 * 4]));
-                if (!kvalid) ahi = io::zero();
-                io::mma(acc[ks][i], bhi, ahi);             // (S Gm)^T += Gm^T S^T
-            }
-        }
-        if (reload) load_ops(nx, o);
-        copy_planes(fl - 1, cur);                       // S_{fl-1}: overlaps the MFMAs
-        store_codes(fl - 1);                            // (S still holds S_{fl-1})
-#pragma unroll
-        for (int i = 0; i < C::RTW; ++i) {
-            f32x4 t = acc[0][i];
-#pragma unroll
-            for (int ks = 1; ks < C::KS; ++ks) t += acc[ks][i];
-            S[i] = t;
-        }
-        put_lds(cur ^ 1);
-        __syncthreads();                                // S_fl visible; S_{fl-1} reads done
+        for (int q = 0; q < C::BPW; ++q) S[q] = acc[q];
+        put_x(xb ^ 1, own_frag());
+        __syncthreads();                                // fragments of S_fl visible
     };
 
+    // ring slot j holds frame fl with fl % PD == j; at the start of frame fl
+    // the slot of frame fl-1 is free and takes frame fl-1+PD
     Ops ring[C::PD];
 #pragma unroll
-    for (int j = 0; j < C::PD; ++j) load_ops(j < Fc ? j : Fc - 1, ring[j]);
-    __syncthreads();                                    // alpha and S_in staged
+    for (int j = 0; j < C::PD - 1; ++j) {
+        load_ops(j < Fc ? j : Fc - 1, ring[j]);
+        __builtin_amdgcn_sched_barrier(0);              // keep the frames in issue order
+    }
+    __syncthreads();                                    // alphas and S_0 fragments staged
     const int nfull = Fc / C::PD;
     for (int gi = 0; gi < nfull; ++gi) {
 #pragma unroll
         for (int j = 0; j < C::PD; ++j) {
             const int fl = gi * C::PD + j;
-            const int nx = fl + C::PD;
-            step(fl, ring[j], nx < Fc ? nx : Fc - 1, true);
+            const int nx = fl - 1 + C::PD;
+            step(fl, ring[j], ring[(j + C::PD - 1) % C::PD], nx < Fc ? nx : Fc - 1, true);
         }
     }
     const int rem = Fc - nfull * C::PD;
 #pragma unroll
-    for (int j = 0; j < C::PD; ++j)
-        if (j < rem) step(nfull * C::PD + j, ring[j], 0, false);
-    copy_planes(Fc - 1, Fc & 1);                        // the last frame's S planes
-    store_codes(Fc - 1);
+    for (int j = 0; j < C::PD; ++j) {
+        if (j < rem) {
+            const int fl = nfull * C::PD + j, nx = fl - 1 + C::PD;
+            step(fl, ring[j], ring[(j + C::PD - 1) % C::PD], nx < Fc ? nx : Fc - 1, true);
+        }
+    }
+    store_state(Fc - 1);
 
     // ---- final state (fp32, row-major [a][e])
+    if (a.S_out) {
+        float* so = a.S_out + (size_t)bh * D * D + (size_t)row * D;
 #pragma unroll
-    for (int i = 0; i < C::RTW; ++i) {
-        const size_t idx = (size_t)bh * D * D + (size_t)(a0 + 16 * i + r) * D + col0;
-        if (a.S_out) *reinterpret_cast<f32x4*>(a.S_out + idx) = S[i];
+        for (int q = 0; q < C::BPW; ++q) *reinterpret_cast<f32x4*>(so + 16 * (c * C::BPW + q) + 4 * g) = S[q];
     }
 }
 
@@ -1084,7 +1016,6 @@ __global__ __launch_bounds__(256, 2) void frame_output_kernel(ScanArgs a) {
             nbeg = mid;
     }
     if (nbeg >= nend) return;
-    const bool kvalid = 8 * g < D || D >= 32;      // D = 16: lanes g >= 2 carry zeros
 
     // token range [nbeg, nend) of this head through buffer resources: rows past
     // nend read as zeros and their stores are dropped
@@ -1122,17 +1053,22 @@ __global__ __launch_bounds__(256, 2) void frame_output_kernel(ScanArgs a) {
         const int rt = wr * C::RPW + i;
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
-            if constexpr (sizeof(T) == 2) {
-                ah[i][ks] = *reinterpret_cast<const u32x4*>(sp + W::frag_off(rt, ks, 0, lane));
-                alw[i][ks] = rem_frag(ah[i][ks], *reinterpret_cast<const u32x2*>(sp + W::sc_rel + W::code_off(rt, ks, lane)));
+            const unsigned char* src = sp + (size_t)(rt * C::KS + ks) * 2048 + lane * 16;
+            const f32x4 x = *reinterpret_cast<const f32x4*>(src);
+            const f32x4 y = *reinterpret_cast<const f32x4*>(src + 1024);
+            if constexpr (sizeof(T) == 2) {             // hi and lo bf16 parts of the fp32 state
+                ah[i][ks] = u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(y[0], y[1]),
+                                  pack_bf16x2(y[2], y[3])};
+                f32x8 rest;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    rest[t] = x[t] - io::get(ah[i][ks], t);
+                    rest[4 + t] = y[t] - io::get(ah[i][ks], 4 + t);
+                }
+                alw[i][ks] = u32x4{pack_bf16x2(rest[0], rest[1]), pack_bf16x2(rest[2], rest[3]),
+                                   pack_bf16x2(rest[4], rest[5]), pack_bf16x2(rest[6], rest[7])};
             } else {
-                const f32x4 lo = *reinterpret_cast<const f32x4*>(sp + W::frag_off(rt, ks, 0, lane));
-                const f32x4 hi = *reinterpret_cast<const f32x4*>(sp + W::frag_off(rt, ks, 1, lane));
-                ah[i][ks] = f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            }
-            if (!kvalid) {
-                ah[i][ks] = io::zero();
-                alw[i][ks] = io::zero();
+                ah[i][ks] = f32x8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
             }
         }
     }
@@ -1143,16 +1079,17 @@ __global__ __launch_bounds__(256, 2) void frame_output_kernel(ScanArgs a) {
             frag bq[C::KS];
 #pragma unroll
             for (int ks = 0; ks < C::KS; ++ks) {
-                const int c0 = (ks * 32 + 8 * g) % D;
-                const unsigned char* src = buf + (sb * 16 + r) * C::ROWB + c0 * C::SZ;
+                // split order: features 32ks + 4g.. and 32ks + 16 + 4g.. (none at D = 16)
+                const unsigned char* src = buf + (sb * 16 + r) * C::ROWB + (ks * 32 + 4 * g) * C::SZ;
                 if constexpr (sizeof(T) == 2) {
-                    bq[ks] = *reinterpret_cast<const u32x4*>(src);
+                    const u32x2 lo = *reinterpret_cast<const u32x2*>(src);
+                    const u32x2 hi = D >= 32 ? *reinterpret_cast<const u32x2*>(src + 32) : u32x2{0u, 0u};
+                    bq[ks] = u32x4{lo[0], lo[1], hi[0], hi[1]};
                 } else {
                     const f32x4 lo = *reinterpret_cast<const f32x4*>(src);
-                    const f32x4 hi = *reinterpret_cast<const f32x4*>(src + 16);
+                    const f32x4 hi = D >= 32 ? *reinterpret_cast<const f32x4*>(src + 64) : f32x4{0, 0, 0, 0};
                     bq[ks] = f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                 }
-                if (!kvalid) bq[ks] = io::zero();
             }
             f32x4 acc[C::RPW];
 #pragma unroll
