@@ -73,6 +73,40 @@ __device__ __forceinline__ float group_sum(float x) {
 __device__ __forceinline__ uint32_t pack_bf16x2(float x, float y) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x, y}, bf16x2));
 }
+// Remainder code of x against its bf16 rounding h (bits in the low half of
+// hb): x - h is at most half a bf16 ulp, 2^(E-134) for h's biased exponent E;
+// the code counts it in 1/256 ulps, rounded to nearest and clamped to int8.
+// h plus rem_value(code) carries x to about 2^-16 relative, in 3 bytes.
+__device__ __forceinline__ int rem_code(float x, uint32_t hb) {
+    const int e = (int)((hb >> 7) & 0xffu);
+    const float t = __builtin_rintf(__builtin_amdgcn_ldexpf(x - bf2f((uint16_t)hb), 142 - e));
+    return (int)__builtin_fminf(__builtin_fmaxf(t, -127.0f), 127.0f);
+}
+__device__ __forceinline__ float rem_value(int code, uint32_t hb) {
+    return __builtin_amdgcn_ldexpf((float)code, (int)((hb >> 7) & 0xffu) - 142);
+}
+// byte i (signed) of a dword of codes
+__device__ __forceinline__ int code_at(uint32_t w, int i) { return (int)(w << (24 - 8 * i)) >> 24; }
+__device__ __forceinline__ uint32_t pack_codes(int c0, int c1, int c2, int c3) {
+    return (uint32_t)(c0 & 0xff) | (uint32_t)(c1 & 0xff) << 8 | (uint32_t)(c2 & 0xff) << 16 | (uint32_t)c3 << 24;
+}
+// The remainders of an 8-value bf16 fragment as a bf16 fragment (exact: a
+// code times a power of two has at most 8 significant bits).
+__device__ __forceinline__ u32x4 rem_frag(u32x4 h, u32x2 c) {
+    u32x4 out;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t w = c[j >> 1];
+        out[j] = pack_bf16x2(rem_value(code_at(w, 2 * (j & 1)), h[j] & 0xffffu),
+                             rem_value(code_at(w, 2 * (j & 1) + 1), h[j] >> 16));
+    }
+    return out;
+}
+// Codes of four fp32 values against their bf16 pair dwords h01, h23.
+__device__ __forceinline__ uint32_t codes4(f32x4 x, uint32_t h01, uint32_t h23) {
+    return pack_codes(rem_code(x[0], h01 & 0xffffu), rem_code(x[1], h01 >> 16), rem_code(x[2], h23 & 0xffffu),
+                      rem_code(x[3], h23 >> 16));
+}
 // Frames per state_scan launch (alpha values are staged in LDS).
 constexpr int kMaxChunkFrames = 256;
 
@@ -176,9 +210,10 @@ template <> struct IO<float> {
 //          a-tile) holds, in lane 16g+r, U[16a_t + r][16e_t + 4g + t] for
 //          t = 0..3 (fp32)
 //   S_f    operand A of frame_output: fragment (a-tile, step kk), lane 16g+r:
-//          S_f[16a_t + r][c] in the split order, fp32 in both modes (2 KiB
-//          per fragment, values 0-3 and 4-7 of every lane in two 1 KiB
-//          halves); frame_output splits it into bf16 high and low parts
+//          S_f[16a_t + r][c] in the split order (bf16 mode: the bf16 plane,
+//          then its remainder codes (rem_code), 8 bytes per lane slot: three
+//          bytes per value at about 2^-16 relative precision; fp32 mode: one
+//          fp32 plane)
 template <typename T, int D> struct WS {
     static constexpr bool B16 = sizeof(T) == 2;
     static constexpr int KS = (D + 31) / 32;                  // contraction fragments per tile
@@ -188,10 +223,17 @@ template <typename T, int D> struct WS {
     static constexpr size_t gm_off = 0;
     static constexpr size_t ut_off = OPND;
     static constexpr size_t sp_off = ut_off + (size_t)RT * RT * 1024;
-    static constexpr size_t item_bytes = sp_off + (size_t)RT * KS * 2048;   // S_f is fp32
+    static constexpr size_t sc_rel = OPND;                    // S codes, after the S plane (bf16)
+    // bf16: the codes take half a plane; the item keeps a whole one (round
+    // item strides measured faster for the recurrence's stores)
+    static constexpr size_t item_bytes = sp_off + (B16 ? 2 : 1) * OPND;
     // byte offset of lane `lane`'s slot in operand fragment (tile, kt), half h (fp32)
     __device__ static __forceinline__ uint32_t frag_off(int tile, int kt, int h, int lane) {
         return (uint32_t)((tile * KS + kt) * FRAG) + (uint32_t)(h * 1024 + lane * 16);
+    }
+    // the same slot's 8 remainder codes in the code plane of S_f (bf16)
+    __device__ static __forceinline__ uint32_t code_off(int tile, int kt, int lane) {
+        return (uint32_t)((tile * KS + kt) * 512) + (uint32_t)(lane * 8);
     }
 };
 
@@ -199,7 +241,7 @@ template <typename T, int D> struct WS {
 constexpr size_t ws_item_bytes(int esz, int D) {
     const size_t KS = (size_t)(D + 31) / 32, RT = (size_t)D / 16;
     const size_t opnd = RT * KS * (esz == 2 ? 1024 : 2048);
-    return opnd + RT * RT * 1024 + RT * KS * 2048;
+    return (esz == 2 ? 3 : 2) * opnd + RT * RT * 1024;
 }
 static_assert(ws_item_bytes(2, 16) == WS<uint16_t, 16>::item_bytes && ws_item_bytes(2, 128) == WS<uint16_t, 128>::item_bytes &&
                   ws_item_bytes(4, 16) == WS<float, 16>::item_bytes && ws_item_bytes(4, 64) == WS<float, 64>::item_bytes,
@@ -613,23 +655,43 @@ __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
         // a wave's tile is all G or all U: two straight store sequences (a
         // per-block branch made the compiler wait for each store to complete)
         if (!utile) {
+            // lane (r, g) of block (gb, jb) holds G[16gb + 4g + t][16jb + r] = Gm^T[e][c] with
+            // e = 16jb + r and c = 32(gb/2) + 16(gb%2) + 4g + t: in the split order that is
+            // fragment (e-tile jb, step gb/2), this lane's own slot, half gb%2.  With two
+            // or more row blocks per wave the two halves of a slot (row blocks 2i, 2i+1)
+            // belong to this wave and each slot is stored whole (bf16: one 16-byte store; a
+            // half-slot store leaves every line it touches half written, and the cache then
+            // reads the line from memory to complete it)
+            constexpr int RSTEP = C::TR >= 2 ? 2 : 1;
+            static_assert(C::TR == 1 || C::TR % 2 == 0, "row blocks pair up into slots");
 #pragma unroll
-            for (int i = 0; i < C::TR; ++i) {
+            for (int i = 0; i < C::TR; i += RSTEP) {
                 const int gb = a_row0 + i;
 #pragma unroll
                 for (int j = 0; j < C::TC; ++j) {
                     const int jb = b_row0 + j;
-                    // lane (r, g) holds G[16gb + 4g + t][16jb + r] = Gm^T[e][c] with e = 16jb + r
-                    // and c = 32(gb/2) + 16(gb%2) + 4g + t: in the split order that is
-                    // fragment (e-tile jb, step gb/2), this lane's own slot, half gb%2
                     const f32x4 m = acc[i][j] * (-al);
                     const uint32_t blk = (uint32_t)(W::gm_off + (size_t)(jb * W::KS + (gb >> 1)) * W::FRAG);
-                    if constexpr (sizeof(T) == 2)
+                    if constexpr (RSTEP == 2) {
+                        const f32x4 m1 = acc[i + RSTEP - 1][j] * (-al);
+                        if constexpr (sizeof(T) == 2) {
+                            __builtin_amdgcn_raw_buffer_store_b128(
+                                u32x4{pack_bf16x2(m[0], m[1]), pack_bf16x2(m[2], m[3]), pack_bf16x2(m1[0], m1[1]),
+                                      pack_bf16x2(m1[2], m1[3])},
+                                rw, u_lane, blk, kWorkspaceStore);
+                        } else {
+                            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, m), rw, u_lane, blk,
+                                                                   kWorkspaceStore);
+                            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, m1), rw, u_lane,
+                                                                   blk + 1024, kWorkspaceStore);
+                        }
+                    } else if constexpr (sizeof(T) == 2) {
                         __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf16x2(m[0], m[1]), pack_bf16x2(m[2], m[3])},
                                                               rw, u_lane, blk + 8 * (gb & 1), kWorkspaceStore);
-                    else
+                    } else {
                         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, m), rw, u_lane,
                                                                blk + 1024 * (gb & 1), kWorkspaceStore);
+                    }
                 }
             }
         } else {
@@ -861,16 +923,24 @@ __global__ __launch_bounds__(256, 1) void state_scan_kernel(ScanArgs a) {   // N
                            rws, lo16, base + (uint32_t)(W::ut_off + (size_t)(jb * W::RT + at) * 1024), 0));
         }
     };
-    // this wave's blocks of S_fl as half-fragments of the fp32 plane read by
-    // frame_output (fragment (at, c), halves 0 and 1; zeros past the slab at
-    // D = 16).  Frame -1 maps past the resource (at most 256 frames of at most
-    // 192 KiB) and is dropped, so the first call needs no branch.
-    auto store_state = [&](int fl) {
+    // this wave's fragment (at, c) of S_fl for frame_output (zeros past the
+    // slab at D = 16): bf16 mode the high plane (the fragment just exchanged)
+    // and the remainder codes, fp32 mode the two halves of the fp32 plane.
+    // Frame -1 maps past the resource (at most 256 frames of at most 192 KiB)
+    // and is dropped, so the first call needs no branch.
+    auto store_state = [&](int fl, const frag& hi) {
         const uint32_t base = fl >= 0 ? (uint32_t)fl * (uint32_t)W::item_bytes + (uint32_t)W::sp_off : 0x80000000u;
-        const uint32_t off = base + (uint32_t)((at * C::KS + c) * 2048);
         const f32x4 y = C::BPW > 1 ? S[C::BPW - 1] : f32x4{0, 0, 0, 0};
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, S[0]), rws, lo16, off, kStreamStore);
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, y), rws, lo16, off + 1024, kStreamStore);
+        if constexpr (C::B16) {
+            __builtin_amdgcn_raw_buffer_store_b128(hi, rws, lo16, base + (uint32_t)((at * C::KS + c) * 1024), kStreamStore);
+            const u32x2 codes{codes4(S[0], hi[0], hi[1]), C::BPW > 1 ? codes4(y, hi[2], hi[3]) : 0u};
+            __builtin_amdgcn_raw_buffer_store_b64(codes, rws, (uint32_t)(lane * 8),
+                                                  base + (uint32_t)(W::sc_rel + (at * C::KS + c) * 512), kStreamStore);
+        } else {
+            const uint32_t off = base + (uint32_t)((at * C::KS + c) * 2048);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, S[0]), rws, lo16, off, kStreamStore);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, y), rws, lo16, off + 1024, kStreamStore);
+        }
     };
     // One frame.  Every fragment of S_{fl-1}, this wave's own included, is read
     // from the exchange buffer written before the previous barrier (register
@@ -882,7 +952,7 @@ __global__ __launch_bounds__(256, 1) void state_scan_kernel(ScanArgs a) {   // N
 #pragma unroll
         for (int kk = 0; kk < C::KS; ++kk) bs[kk] = get_x(xb, kk);
         if (reload) load_ops(nx, prev);                 // the slot frame fl-1 used
-        store_state(fl - 1);                            // S still holds S_{fl-1}
+        store_state(fl - 1, bs[c]);                     // S still holds S_{fl-1}
         const float al = sAlpha[fl];
         f32x4 acc[C::BPW];
 #pragma unroll
@@ -934,7 +1004,7 @@ __global__ __launch_bounds__(256, 1) void state_scan_kernel(ScanArgs a) {   // N
             step(fl, ring[j], ring[(j + C::PD - 1) % C::PD], nx < Fc ? nx : Fc - 1, true);
         }
     }
-    store_state(Fc - 1);
+    store_state(Fc - 1, own_frag());
 
     // ---- final state (fp32, row-major [a][e])
     if (a.S_out) {
@@ -1053,21 +1123,12 @@ __global__ __launch_bounds__(256, 2) void frame_output_kernel(ScanArgs a) {
         const int rt = wr * C::RPW + i;
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
-            const unsigned char* src = sp + (size_t)(rt * C::KS + ks) * 2048 + lane * 16;
-            const f32x4 x = *reinterpret_cast<const f32x4*>(src);
-            const f32x4 y = *reinterpret_cast<const f32x4*>(src + 1024);
-            if constexpr (sizeof(T) == 2) {             // hi and lo bf16 parts of the fp32 state
-                ah[i][ks] = u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(y[0], y[1]),
-                                  pack_bf16x2(y[2], y[3])};
-                f32x8 rest;
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    rest[t] = x[t] - io::get(ah[i][ks], t);
-                    rest[4 + t] = y[t] - io::get(ah[i][ks], 4 + t);
-                }
-                alw[i][ks] = u32x4{pack_bf16x2(rest[0], rest[1]), pack_bf16x2(rest[2], rest[3]),
-                                   pack_bf16x2(rest[4], rest[5]), pack_bf16x2(rest[6], rest[7])};
+            if constexpr (sizeof(T) == 2) {             // high plane and the low part from the codes
+                ah[i][ks] = *reinterpret_cast<const u32x4*>(sp + W::frag_off(rt, ks, 0, lane));
+                alw[i][ks] = rem_frag(ah[i][ks], *reinterpret_cast<const u32x2*>(sp + W::sc_rel + W::code_off(rt, ks, lane)));
             } else {
+                const f32x4 x = *reinterpret_cast<const f32x4*>(sp + W::frag_off(rt, ks, 0, lane));
+                const f32x4 y = *reinterpret_cast<const f32x4*>(sp + W::frag_off(rt, ks, 1, lane));
                 ah[i][ks] = f32x8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
             }
         }
