@@ -63,6 +63,10 @@ def load():
         fn = getattr(lib, name)
         fn.argtypes = [dp, vp, vp, vp, fp, fp, fp, vp, fp, vp, sz, vp]
         fn.restype = ctypes.c_int
+    lib.gdn_frame_scan_fwd_static.argtypes = [dp, vp, vp, vp, fp, fp, fp, vp, fp, vp]
+    lib.gdn_frame_scan_fwd_static.restype = ctypes.c_int
+    lib.gdn_static_scratch_bytes.argtypes = []
+    lib.gdn_static_scratch_bytes.restype = sz
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_status_string.restype = ctypes.c_char_p
     lib.gdn_version.argtypes = []

@@ -118,6 +118,40 @@ def frame_scan_fwd(q, k, v, beta, alpha, S0=None, *, gates_are_logits: bool = Fa
     return o, S_final
 
 
+def frame_scan_fwd_static(q, k, v, beta, alpha, S0=None, *, gates_are_logits: bool = False,
+                          eps: float = 1e-6, normalize_keys: bool = True, o=None, S_final=None,
+                          return_state: bool = True, stream=None):
+    """frame_scan_fwd through gdn_frame_scan_fwd_static: the library's own static
+    scratch instead of a workspace.  The C entry point allocates nothing; pass
+    o and S_final to keep this wrapper from allocating them with torch."""
+    B, F, N, H, D = q.shape
+    _check(q, "q", q.dtype, (B, F, N, H, D))
+    _check(k, "k", q.dtype, (B, F, N, H, D))
+    _check(v, "v", q.dtype, (B, F, N, H, D))
+    _check(beta, "beta", torch.float32, (B, F, N, H))
+    _check(alpha, "alpha", torch.float32, (B, F, H))
+    if S0 is not None:
+        _check(S0, "S0", torch.float32, (B, H, D, D))
+    if o is not None:
+        _check(o, "o", q.dtype, (B, F, N, H, D))
+    if S_final is not None:
+        _check(S_final, "S_final", torch.float32, (B, H, D, D))
+    desc = make_desc(B, H, F, N, D, q.dtype, gates_are_logits=gates_are_logits, eps=eps,
+                     normalize_keys=normalize_keys)
+    stream = _launch_stream(stream, q.device)
+    with torch.cuda.stream(stream):
+        if o is None:
+            o = torch.empty_like(q)
+        if S_final is None and return_state:
+            S_final = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
+        st = _lib.load().gdn_frame_scan_fwd_static(
+            ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha), _ptr(S0),
+            _ptr(o), _ptr(S_final), ctypes.c_void_p(stream.cuda_stream))
+    if st != 0:
+        raise GdnError(st, "gdn_frame_scan_fwd_static")
+    return o, S_final
+
+
 def frame_step(q, k, v, beta, alpha, S_in=None, *, gates_are_logits: bool = False,
                eps: float = 1e-6, normalize_keys: bool = True, o=None, S_out=None, workspace=None, stream=None):
     """One frame of the scan for streaming use.

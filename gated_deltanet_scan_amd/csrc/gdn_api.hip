@@ -122,7 +122,9 @@ void step_ranges(int64_t units, int N, int ts, int cus, int* parts, int* tpart) 
 
 bool dim_ok(int D) { return D == 16 || D == 32 || D == 64 || D == 128; }
 
-gdn_status check_desc(const gdn_desc* d, bool step, Plan* p) {
+// fc_cap bounds the frames per launch chunk (the static-scratch entry point
+// sizes its chunks to fit the scratch array).
+gdn_status check_desc(const gdn_desc* d, bool step, Plan* p, int fc_cap = gdn::kMaxChunkFrames) {
     if (!d) return GDN_ERR_INVALID_ARG;
     if (d->B < 0 || d->H < 0 || d->F < 0 || d->N < 0) return GDN_ERR_INVALID_ARG;
     if (d->io_dtype != GDN_BF16 && d->io_dtype != GDN_F32) return GDN_ERR_INVALID_ARG;
@@ -141,7 +143,7 @@ gdn_status check_desc(const gdn_desc* d, bool step, Plan* p) {
     p->esz = d->io_dtype == GDN_BF16 ? 2 : 4;
     p->units = (int64_t)d->B * d->H;
     // frames per launch chunk (state_scan stages the chunk's gates in LDS)
-    p->Fc = d->F < gdn::kMaxChunkFrames ? d->F : gdn::kMaxChunkFrames;
+    p->Fc = d->F < fc_cap ? d->F : fc_cap;
     p->item_bytes = gdn::ws_item_bytes(p->esz, p->D);
     if (d->F == 1) {
         int tpart = 0;
@@ -322,12 +324,64 @@ gdn_status dispatch_d(const Plan& p, const ScanArgs& a, hipStream_t s, int cus, 
     }
 }
 
+// ---------------------------------------------------------------- static scratch
+// The allocation-free entry point's workspace: one array per device, held
+// until the process ends.  Host code never passes `scratch` itself to a
+// kernel (in host code it is only a stand-in for the device symbol); it
+// passes the device address that hipGetSymbolAddress returns, looked up once
+// per device with that device current.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];
+
+gdn_status scratch_for_device(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return GDN_ERR_NO_DEVICE;
+    if (dev >= 64) return GDN_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return GDN_ERR_NO_DEVICE;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return GDN_OK;
+}
+
+// Frames per chunk that fit the static scratch: every chunk's items plus the
+// carried state (0 when not even one frame fits).
+int scratch_chunk_cap(const gdn_desc* d) {
+    Plan p;
+    if (check_desc(d, false, &p) != GDN_OK || p.units <= 0) return gdn::kMaxChunkFrames;
+    const size_t carry = (size_t)p.units * p.D * p.D * sizeof(float) + 256;
+    if (carry >= kScratchBytes) return 0;
+    const size_t per_frame = (size_t)p.units * p.item_bytes;
+    const size_t cap = (kScratchBytes - carry) / per_frame;
+    return cap < (size_t)gdn::kMaxChunkFrames ? (int)cap : gdn::kMaxChunkFrames;
+}
+
 gdn_status run(const gdn_desc* d, bool step, const void* q, const void* k, const void* v,
                const float* beta, const float* alpha, const float* S0, void* o, float* S_final,
-               void* workspace, size_t workspace_bytes, void* stream_v) {
+               void* workspace, size_t workspace_bytes, void* stream_v, bool static_ws = false) {
     Plan p;
-    gdn_status st = check_desc(d, step, &p);
+    int fc_cap = gdn::kMaxChunkFrames;
+    if (static_ws) {
+        fc_cap = scratch_chunk_cap(d);
+        if (fc_cap < 1 && d && d->F > 1) return GDN_ERR_WORKSPACE;   // one frame does not fit
+        if (fc_cap < 1) fc_cap = 1;
+    }
+    gdn_status st = check_desc(d, step, &p, fc_cap);
     if (st != GDN_OK) return st;
+    if (static_ws) {
+        if (p.ws_bytes > kScratchBytes) return GDN_ERR_WORKSPACE;
+        workspace = nullptr;
+        workspace_bytes = 0;
+        if (p.ws_bytes > 0 && p.units > 0) {
+            if ((st = scratch_for_device(&workspace)) != GDN_OK) return st;
+            workspace_bytes = kScratchBytes;
+        }
+    }
 
     const size_t ntok = (size_t)d->B * d->F * d->N * d->H;
     const size_t tok_bytes = ntok * (size_t)p.D * p.esz;
@@ -430,6 +484,14 @@ gdn_status gdn_frame_scan_fwd(const gdn_desc* d, const void* q, const void* k, c
                               float* S_final, void* workspace, size_t workspace_bytes, void* stream) {
     return run(d, false, q, k, v, beta, alpha, S0, o, S_final, workspace, workspace_bytes, stream);
 }
+
+gdn_status gdn_frame_scan_fwd_static(const gdn_desc* d, const void* q, const void* k, const void* v,
+                                     const float* beta, const float* alpha, const float* S0, void* o,
+                                     float* S_final, void* stream) {
+    return run(d, false, q, k, v, beta, alpha, S0, o, S_final, nullptr, 0, stream, true);
+}
+
+size_t gdn_static_scratch_bytes(void) { return kScratchBytes; }
 
 gdn_status gdn_frame_step(const gdn_desc* d, const void* q, const void* k, const void* v,
                           const float* beta, const float* alpha, const float* S_in, void* o,

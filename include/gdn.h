@@ -132,6 +132,30 @@ gdn_status gdn_frame_step(const gdn_desc* d,
                           void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/* Allocation-free scan, for callers that cannot allocate device memory or be
+ * handed a workspace: code under HIP graph capture, tight serving loops and
+ * harnesses that forbid allocation.  The same operation and arguments as
+ * gdn_frame_scan_fwd, with the library's own scratch in place of a
+ * workspace: a static device array of gdn_static_scratch_bytes() bytes
+ * (64 MiB) on every GPU the library runs on, held until the process ends.
+ * The frames are processed in chunks sized to fit it, so the results equal
+ * gdn_frame_scan_fwd's bit for bit.  GDN_ERR_WORKSPACE when even one frame's
+ * operands (about 10*Dk*Dv bytes per (b, h) in bf16 mode, 12*Dk*Dv in fp32
+ * mode, plus 4*Dk*Dv per (b, h) of carried state) do not fit.  The scratch
+ * needs no clearing: every byte a kernel reads was written earlier in the
+ * same call.  All calls on one GPU share its array: calls that can overlap on
+ * one GPU (several streams, several host threads) race and must be ordered by
+ * the caller.  Calls no allocation routine. */
+gdn_status gdn_frame_scan_fwd_static(const gdn_desc* d,
+                                     const void* q, const void* k, const void* v,
+                                     const float* beta, const float* alpha,
+                                     const float* S0,
+                                     void* o, float* S_final,
+                                     void* stream);
+
+/* Size in bytes of the static scratch array gdn_frame_scan_fwd_static uses. */
+size_t gdn_static_scratch_bytes(void);
+
 /* Human-readable name of a status code (static storage). */
 const char* gdn_status_string(gdn_status s);
 

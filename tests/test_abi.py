@@ -160,3 +160,21 @@ def test_profile_session_without_launches(lib):
     n = (ctypes.c_int64 * 5)()
     assert lib.gdn_profile_end(ms, n) == OK
     assert list(n) == [0] * 5 and list(ms) == [0.0] * 5
+
+
+def test_static_scratch_rejects_what_does_not_fit(lib):
+    """gdn_frame_scan_fwd_static: the scratch holds at least one frame for
+    moderate shapes; a shape whose single frame of operands exceeds it is
+    refused on the host before any launch (no pointer is touched)."""
+    assert lib.gdn_static_scratch_bytes() == 64 << 20
+    # B1 H512 d128: one frame of workspace items is 512 x 160 KiB = 80 MiB
+    d = desc(B=1, H=512, F=2, N=1, D=128)
+    p = [P[n] for n in ["q", "k", "v", "beta", "alpha", "S0", "o", "S_final"]]
+    assert lib.gdn_frame_scan_fwd_static(ctypes.byref(d), *p, None) == WORKSPACE
+    # invalid descriptors report as for the workspace entry point
+    assert lib.gdn_frame_scan_fwd_static(None, *p, None) == INVALID
+    assert lib.gdn_frame_scan_fwd_static(ctypes.byref(desc(D=48)), *p, None) == UNSUPPORTED
+    # nothing to compute: accepted without touching any pointer
+    d0 = desc(B=0)
+    assert lib.gdn_frame_scan_fwd_static(ctypes.byref(d0), None, None, None, None, None, None,
+                                         None, None, None) == OK
