@@ -46,7 +46,7 @@ def _load():
         lib = ctypes.CDLL(path)
         dp = ctypes.POINTER(ctypes.c_double)
         lib.gdn_oracle_scan.argtypes = [ctypes.c_int] * 6 + [dp] * 6 + [
-            ctypes.c_double, ctypes.c_int, ctypes.c_int, dp, dp]
+            ctypes.c_double, ctypes.c_int, ctypes.c_int, ctypes.c_int, dp, dp]
         lib.gdn_oracle_scan.restype = ctypes.c_int
         lib.gdn_oracle_max_threads.argtypes = []
         lib.gdn_oracle_max_threads.restype = ctypes.c_int
@@ -67,12 +67,13 @@ def max_threads() -> int:
 
 
 def scan(q, k, v, beta, alpha, S0=None, *, eps: float = 1e-6,
-         gates_are_logits: bool = False, normalize_keys: bool = True):
+         gates_are_logits: bool = False, normalize_keys: bool = True, reverse: bool = False):
     """Run the whole scan in fp64.
 
     q, k: [B,F,N,H,Dk]; v: [B,F,N,H,Dv]; beta: [B,F,N,H]; alpha: [B,F,H];
     S0: [B,H,Dv,Dk] or None (zeros).  Any real dtype; values are upcast
-    exactly to float64.  normalize_keys=False uses the keys as given.
+    exactly to float64.  normalize_keys=False uses the keys as given;
+    reverse=True walks the frames from last to first.
     Returns (o [B,F,N,H,Dv], S_final [B,H,Dv,Dk]) as float64 arrays.
     """
     q, k, v, beta, alpha = (_f64(x) for x in (q, k, v, beta, alpha))
@@ -91,7 +92,7 @@ def scan(q, k, v, beta, alpha, S0=None, *, eps: float = 1e-6,
     rc = _load().gdn_oracle_scan(B, H, F, N, Dk, Dv, _ptr(q), _ptr(k), _ptr(v),
                                  _ptr(beta), _ptr(alpha), _ptr(S0), float(eps),
                                  int(bool(gates_are_logits)), int(bool(normalize_keys)),
-                                 _ptr(o), _ptr(S_final))
+                                 int(bool(reverse)), _ptr(o), _ptr(S_final))
     if rc != 0:
         raise RuntimeError("gdn_oracle_scan failed with code %d" % rc)
     return o, S_final

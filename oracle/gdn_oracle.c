@@ -29,6 +29,13 @@
  * are used as given (k^_i = k_i), the library's option for callers whose keys
  * already have unit norm.
  *
+ * Reverse direction (reverse != 0): the same recurrence walked from the last
+ * frame to the first, S entering at frame F and S_final leaving after frame 1
+ * (the "bidirectional" weights on the WorldFoundry "SANA-WM" page, sections
+ * "What it is for" and "Running in WorldFoundry", scan in both directions;
+ * the pages do not say how the two are combined, so each direction is a scan
+ * of its own):  S_f = alpha_f * S_{f+1} (I - G_f) + U_f,  O_f = Q_f S_f^T.
+ *
  * Layouts (row-major, last index fastest):
  *     q, k  [B][F][N][H][Dk]      v, o  [B][F][N][H][Dv]
  *     beta  [B][F][N][H]          alpha [B][F][H]
@@ -53,7 +60,7 @@ int gdn_oracle_scan(int B, int H, int F, int N, int Dk, int Dv,
                     const double *q, const double *k, const double *v,
                     const double *beta, const double *alpha,
                     const double *S0, double eps, int gates_are_logits,
-                    int normalize_k, double *o, double *S_final)
+                    int normalize_k, int reverse, double *o, double *S_final)
 {
     if (B < 0 || H < 0 || F < 0 || N < 0 || Dk < 1 || Dv < 1 || !(eps > 0.0))
         return -1;
@@ -78,7 +85,8 @@ int gdn_oracle_scan(int B, int H, int F, int N, int Dk, int Dv,
                     S[(size_t)a * Dk + e] =
                         S0 ? S0[(((size_t)b * H + h) * Dv + a) * Dk + e] : 0.0;
 
-            for (int f = 0; f < F; ++f) {
+            for (int step = 0; step < F; ++step) {
+                const int f = reverse ? F - 1 - step : step;   /* frame of this step */
                 const size_t tok0 = (size_t)b * sB + (size_t)f * sF; /* token 0, head 0 */
                 double al = alpha[((size_t)b * F + f) * H + h];
                 if (gates_are_logits) al = sigmoid(al);

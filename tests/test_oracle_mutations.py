@@ -26,6 +26,7 @@ MUTATIONS = {
     "alpha_of_wrong_head": [("double al = alpha[((size_t)b * F + f) * H + h];",
                              "double al = alpha[((size_t)b * F + f) * H];")],
     "beta_logit_not_divided": [("sigmoid(bi) / (double)N", "sigmoid(bi)")],
+    "reverse_flag_ignored": [("const int f = reverse ? F - 1 - step : step;", "const int f = step;")],
     "raw_keys_flag_ignored": [("if (!normalize_k) den = 1.0;", "if (!normalize_k) den = den;")],
     "eps_added_not_clamped": [("double den = nrm > eps ? nrm : eps;", "double den = nrm + eps;")],
     "gram_transposed_write": [("const double s = bt[i] * vi[a];\n                        for (int e = 0; e < Dk; ++e) Ua[e] += s * ki[e];",

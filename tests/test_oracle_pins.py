@@ -205,6 +205,34 @@ def test_raw_unit_keys_equal_normalised():
     assert rel(o2, o) < 1e-14 and rel(S2, S) < 1e-14
 
 
+# ---------------------------------------------------------------- reverse direction
+def test_reverse_is_forward_on_reversed_frames():
+    """The reverse scan equals the forward scan of the frames in reverse order
+    (outputs reversed back), from the same initial state."""
+    q, k, v, beta, alpha, S0 = rand_case(B=2, H=2, F=5, N=4, Dk=5, Dv=4, seed=32)
+    o, S = oracle.scan(q, k, v, beta, alpha, S0, reverse=True)
+    fl = lambda x: np.ascontiguousarray(x[:, ::-1])
+    o2, S2 = oracle.scan(fl(q), fl(k), fl(v), fl(beta), fl(alpha), S0)
+    assert rel(o, fl(o2)) < 1e-14 and rel(S, S2) < 1e-14
+    o3, S3 = oracle.scan(q, k, v, beta, alpha, S0)
+    assert rel(S3, S) > 1e-3                      # the directions really differ
+
+
+def test_reverse_token_rule_at_N1():
+    """At N = 1 the reverse scan is the textbook rule walked from the last frame."""
+    q, k, v, beta, alpha, S0 = rand_case(B=1, H=2, F=6, N=1, Dk=4, Dv=3, seed=33)
+    o, S = oracle.scan(q, k, v, beta, alpha, S0, reverse=True)
+    for b in range(1):
+        for h in range(2):
+            s = S0[b, h].copy()
+            for f in range(5, -1, -1):
+                kk = k[b, f, 0, h] / np.linalg.norm(k[b, f, 0, h])
+                bt, al = beta[b, f, 0, h], alpha[b, f, h]
+                s = al * (s - bt * np.outer(s @ kk, kk)) + bt * np.outer(v[b, f, 0, h], kk)
+                np.testing.assert_allclose(o[b, f, 0, h], s @ q[b, f, 0, h], rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(S[b, h], s, rtol=1e-12, atol=1e-12)
+
+
 # ---------------------------------------------------------------- closed forms
 def test_pure_decay_closed_form():
     q, k, v, beta, alpha, S0 = rand_case(B=2, H=2, F=6, N=4, Dk=5, Dv=3, seed=4)
