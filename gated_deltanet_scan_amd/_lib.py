@@ -16,6 +16,7 @@ GDN_BF16 = 0
 GDN_F32 = 1
 GDN_FLAG_GATES_ARE_LOGITS = 0x1
 GDN_FLAG_NO_KEY_NORM = 0x2
+GDN_FLAG_REVERSE = 0x4
 GDN_NUM_KERNELS = 5
 
 STATUS = {0: "GDN_OK", 1: "GDN_ERR_INVALID_ARG", 2: "GDN_ERR_UNSUPPORTED", 3: "GDN_ERR_ALIGNMENT",

@@ -33,7 +33,7 @@ def _check(t: torch.Tensor, name: str, dtype, shape):
 
 
 def make_desc(B, H, F, N, D, dtype: torch.dtype, *, gates_are_logits=False, eps=1e-6,
-              normalize_keys=True) -> GdnDesc:
+              normalize_keys=True, reverse=False) -> GdnDesc:
     if dtype == torch.bfloat16:
         io = _lib.GDN_BF16
     elif dtype == torch.float32:
@@ -43,6 +43,8 @@ def make_desc(B, H, F, N, D, dtype: torch.dtype, *, gates_are_logits=False, eps=
     flags = _lib.GDN_FLAG_GATES_ARE_LOGITS if gates_are_logits else 0
     if not normalize_keys:
         flags |= _lib.GDN_FLAG_NO_KEY_NORM
+    if reverse:
+        flags |= _lib.GDN_FLAG_REVERSE
     return GdnDesc(B, H, F, N, D, D, io, flags, float(eps))
 
 
@@ -81,12 +83,14 @@ def _launch_stream(stream, device):
 
 
 def frame_scan_fwd(q, k, v, beta, alpha, S0=None, *, gates_are_logits: bool = False,
-                   eps: float = 1e-6, normalize_keys: bool = True, o=None, S_final=None, workspace=None,
+                   eps: float = 1e-6, normalize_keys: bool = True, reverse: bool = False,
+                   o=None, S_final=None, workspace=None,
                    return_state: bool = True, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Whole-clip frame-wise GDN scan.
 
     q, k: [B,F,N,H,D]; v: [B,F,N,H,D] (bf16 or fp32, all the same dtype);
     beta: [B,F,N,H] fp32; alpha: [B,F,H] fp32; S0: [B,H,D,D] fp32 or None.
+    reverse=True runs the recurrence from the last frame to the first.
     Returns (o [B,F,N,H,D] in the q dtype, S_final [B,H,D,D] fp32 or None).
     """
     B, F, N, H, D = q.shape
@@ -98,7 +102,7 @@ def frame_scan_fwd(q, k, v, beta, alpha, S0=None, *, gates_are_logits: bool = Fa
     if S0 is not None:
         _check(S0, "S0", torch.float32, (B, H, D, D))
     desc = make_desc(B, H, F, N, D, q.dtype, gates_are_logits=gates_are_logits, eps=eps,
-                     normalize_keys=normalize_keys)
+                     normalize_keys=normalize_keys, reverse=reverse)
     if o is not None:
         _check(o, "o", q.dtype, (B, F, N, H, D))
     if S_final is not None:
@@ -119,7 +123,8 @@ def frame_scan_fwd(q, k, v, beta, alpha, S0=None, *, gates_are_logits: bool = Fa
 
 
 def frame_scan_fwd_static(q, k, v, beta, alpha, S0=None, *, gates_are_logits: bool = False,
-                          eps: float = 1e-6, normalize_keys: bool = True, o=None, S_final=None,
+                          eps: float = 1e-6, normalize_keys: bool = True, reverse: bool = False,
+                          o=None, S_final=None,
                           return_state: bool = True, stream=None):
     """frame_scan_fwd through gdn_frame_scan_fwd_static: the library's own static
     scratch instead of a workspace.  The C entry point allocates nothing; pass
@@ -137,7 +142,7 @@ def frame_scan_fwd_static(q, k, v, beta, alpha, S0=None, *, gates_are_logits: bo
     if S_final is not None:
         _check(S_final, "S_final", torch.float32, (B, H, D, D))
     desc = make_desc(B, H, F, N, D, q.dtype, gates_are_logits=gates_are_logits, eps=eps,
-                     normalize_keys=normalize_keys)
+                     normalize_keys=normalize_keys, reverse=reverse)
     stream = _launch_stream(stream, q.device)
     with torch.cuda.stream(stream):
         if o is None:

@@ -128,7 +128,8 @@ gdn_status check_desc(const gdn_desc* d, bool step, Plan* p, int fc_cap = gdn::k
     if (!d) return GDN_ERR_INVALID_ARG;
     if (d->B < 0 || d->H < 0 || d->F < 0 || d->N < 0) return GDN_ERR_INVALID_ARG;
     if (d->io_dtype != GDN_BF16 && d->io_dtype != GDN_F32) return GDN_ERR_INVALID_ARG;
-    if ((d->flags & ~(GDN_FLAG_GATES_ARE_LOGITS | GDN_FLAG_NO_KEY_NORM)) != 0) return GDN_ERR_INVALID_ARG;
+    if ((d->flags & ~(GDN_FLAG_GATES_ARE_LOGITS | GDN_FLAG_NO_KEY_NORM | GDN_FLAG_REVERSE)) != 0)
+        return GDN_ERR_INVALID_ARG;
     if (!(d->eps > 0.0f) || !isfinite(d->eps)) return GDN_ERR_INVALID_ARG;
     if (step && d->F != 1) return GDN_ERR_INVALID_ARG;
     if (d->Dk < 1 || d->Dv < 1) return GDN_ERR_INVALID_ARG;
@@ -206,16 +207,20 @@ gdn_status launch_output(ScanArgs a, hipStream_t stream, int cus) {
     return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 
-// Launch order, per chunk of up to kMaxChunkFrames frames, all on the caller's
-// stream: frame_gram, then the recurrence (whose state is carried in `carry`:
-// S_final, or the workspace's carry region), then the output pass.
+// Launch order, per chunk of up to p.Fc frames, all on the caller's stream:
+// frame_gram, then the recurrence (whose state is carried in `carry`:
+// S_final, or the workspace's carry region), then the output pass.  The
+// reverse direction visits the chunks from the last to the first.
 // (Running the recurrence on a second stream in sub-chunks, overlapped with
-// the output pass, measured slower.)
+// the output pass, measured slower: the two passes slow each other down
+// where they share compute units.)
 template <typename T, int D>
 gdn_status launch_all(const Plan& p, ScanArgs a, hipStream_t stream, int cus, float* carry) {
     const int units = (int)p.units;
     gdn_status st = GDN_OK;
-    for (int f0 = 0; f0 < a.F; f0 += p.Fc) {
+    const int nchunks = (a.F + p.Fc - 1) / p.Fc;
+    for (int ci = 0; ci < nchunks; ++ci) {
+        const int f0 = (a.reverse ? nchunks - 1 - ci : ci) * p.Fc;
         a.f0 = f0;
         a.Fc = a.F - f0 < p.Fc ? a.F - f0 : p.Fc;
         const int items = units * a.Fc;
@@ -452,6 +457,7 @@ gdn_status run(const gdn_desc* d, bool step, const void* q, const void* k, const
     a.N = d->N;
     a.logits = (d->flags & GDN_FLAG_GATES_ARE_LOGITS) ? 1 : 0;
     a.raw_keys = (d->flags & GDN_FLAG_NO_KEY_NORM) ? 1 : 0;
+    a.reverse = (d->flags & GDN_FLAG_REVERSE) ? 1 : 0;
     a.eps = d->eps;
     a.tsplit = 1;
     a.tchunk = 16;

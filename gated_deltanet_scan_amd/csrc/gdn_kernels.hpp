@@ -266,6 +266,7 @@ struct ScanArgs {
                           // as two workgroups of half the tokens each
     int logits;
     int raw_keys;         // keys used as given (no L2 normalisation)
+    int reverse;          // the recurrence walks the frames from last to first
     float eps;
     // One-frame path (see frame_step_kernel): frame_gram splits each (b, h)
     // into `parts` token ranges of `tpart` tokens (a multiple of its stage)
@@ -867,8 +868,12 @@ __global__ __launch_bounds__(256, 1) void state_scan_kernel(ScanArgs a) {   // N
     const int row = 16 * at + r;
     const uint32_t lo16 = (uint32_t)(lane * 16);
 
+    // step fl of the recurrence takes local frame phys(fl): the frames in
+    // order, or from the last to the first in the reverse direction
+    const int rev = a.reverse;
+    auto phys = [&](int fl) { return rev ? Fc - 1 - fl : fl; };
     for (int i = tid; i < Fc; i += C::NTH) {
-        const float x = a.alpha[((size_t)b * a.F + a.f0 + i) * a.H + h];
+        const float x = a.alpha[((size_t)b * a.F + a.f0 + phys(i)) * a.H + h];
         sAlpha[i] = a.logits ? sigmoid_f(x) : x;
     }
     // this unit's workspace items through one buffer resource
@@ -899,8 +904,8 @@ __global__ __launch_bounds__(256, 1) void state_scan_kernel(ScanArgs a) {   // N
         frag gm[C::KS][C::BPW];
         f32x4 u[C::BPW];
     };
-    auto load_ops = [&](int fl, Ops& o) {             // fl is always a valid frame
-        const uint32_t base = (uint32_t)fl * (uint32_t)W::item_bytes;
+    auto load_ops = [&](int fl, Ops& o) {             // fl is always a valid step
+        const uint32_t base = (uint32_t)phys(fl) * (uint32_t)W::item_bytes;
 #pragma unroll
         for (int kk = 0; kk < C::KS; ++kk)
 #pragma unroll
@@ -929,7 +934,7 @@ __global__ __launch_bounds__(256, 1) void state_scan_kernel(ScanArgs a) {   // N
     // Frame -1 maps past the resource (at most 256 frames of at most 192 KiB)
     // and is dropped, so the first call needs no branch.
     auto store_state = [&](int fl, const frag& hi) {
-        const uint32_t base = fl >= 0 ? (uint32_t)fl * (uint32_t)W::item_bytes + (uint32_t)W::sp_off : 0x80000000u;
+        const uint32_t base = fl >= 0 ? (uint32_t)phys(fl) * (uint32_t)W::item_bytes + (uint32_t)W::sp_off : 0x80000000u;
         const f32x4 y = C::BPW > 1 ? S[C::BPW - 1] : f32x4{0, 0, 0, 0};
         if constexpr (C::B16) {
             __builtin_amdgcn_raw_buffer_store_b128(hi, rws, lo16, base + (uint32_t)((at * C::KS + c) * 1024), kStreamStore);

@@ -74,6 +74,13 @@ typedef enum gdn_dtype { GDN_BF16 = 0, GDN_F32 = 1 } gdn_dtype;
  * Key normalisation is on by default (flag clear), which is the operator above;
  * a caller whose keys already have unit norm may skip it with this flag. */
 #define GDN_FLAG_NO_KEY_NORM 0x2u
+/* Reverse direction: the recurrence walks the frames from the last to the
+ * first, S0 entering before frame F and S_final leaving after frame 1:
+ *     S_f = alpha_f * S_{f+1} (I - G_f) + U_f,   o_i = S_f q_i.
+ * The WorldFoundry "SANA-WM" page (sections "What it is for" and "Running in
+ * WorldFoundry") names bidirectional weights; each direction is its own scan
+ * and the caller combines the two outputs as its model requires. */
+#define GDN_FLAG_REVERSE 0x4u
 
 /* Determinism.  Every call is bitwise reproducible: the same inputs on the same
  * device give the same bits, whatever ran before (no atomics, no data-dependent

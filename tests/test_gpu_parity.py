@@ -44,7 +44,7 @@ def check(got, ref, dtype, what):
         assert rel <= TOL_F32_REL, (what, mx, rel)
 
 
-def run_gpu(w, *, logits=False, S0="auto", beta=None, alpha=None, raw_keys=False):
+def run_gpu(w, *, logits=False, S0="auto", beta=None, alpha=None, raw_keys=False, reverse=False):
     q, k, v, b, a, s0 = inputs.to_torch(w, "cuda")
     if beta is not None:
         b = torch.from_numpy(np.ascontiguousarray(beta, dtype=np.float32)).cuda()
@@ -53,18 +53,19 @@ def run_gpu(w, *, logits=False, S0="auto", beta=None, alpha=None, raw_keys=False
     if S0 is not None and not isinstance(S0, str):
         s0 = torch.from_numpy(np.ascontiguousarray(S0, dtype=np.float32)).cuda()
     o, S = api.frame_scan_fwd(q, k, v, b, a, s0, gates_are_logits=logits,
-                              normalize_keys=not raw_keys)
+                              normalize_keys=not raw_keys, reverse=reverse)
     torch.cuda.synchronize()
     return o.float().cpu().numpy(), S.cpu().numpy()
 
 
-def oracle_ref(w, *, logits=False, units=None, beta=None, alpha=None, S0="auto", raw_keys=False):
+def oracle_ref(w, *, logits=False, units=None, beta=None, alpha=None, S0="auto", raw_keys=False,
+               reverse=False):
     beta = w.beta if beta is None else beta
     alpha = w.alpha if alpha is None else alpha
     S0 = w.S0 if isinstance(S0, str) else S0
     if units is None:
         return oracle.scan(w.q, w.k, w.v, beta, alpha, S0, gates_are_logits=logits,
-                           normalize_keys=not raw_keys)
+                           normalize_keys=not raw_keys, reverse=reverse)
     outs = []
     for b, h in units:
         sl = (slice(b, b + 1), slice(None), slice(None), slice(h, h + 1))
@@ -215,6 +216,47 @@ def test_raw_keys(dtype, D):
     ro, rS = oracle_ref(w, raw_keys=True)
     check(o, ro, dtype, "O")
     check(S, rS, dtype, "S_F")
+
+
+# ------------------------------------------------------------------ reverse direction
+@pytest.mark.parametrize("B,H,F,N,D,dtype", [
+    (1, 2, 7, 33, 16, "bf16"), (2, 3, 5, 130, 64, "bf16"), (1, 2, 6, 257, 128, "bf16"),
+    (1, 2, 4, 50, 32, "f32"), (2, 2, 3, 70, 128, "f32")])
+def test_reverse_scan(B, H, F, N, D, dtype):
+    w = inputs.make(B, H, F, N, D, dtype=dtype, seed=71 + F + D, s0_std=0.05)
+    o, S = run_gpu(w, reverse=True)
+    ro, rS = oracle_ref(w, reverse=True)
+    check(o, ro, dtype, "O")
+    check(S, rS, dtype, "S_F")
+
+
+def test_reverse_scan_over_launch_chunks_and_in_place():
+    """300 frames in reverse: two launch chunks visited last-first, the state
+    carried between them, also in place (S_final is S0)."""
+    w = inputs.make(1, 2, 300, 24, 32, dtype="bf16", seed=73, s0_std=0.05)
+    o, S = run_gpu(w, reverse=True)
+    ro, rS = oracle_ref(w, reverse=True)
+    check(o, ro, "bf16", "O")
+    check(S, rS, "bf16", "S_F")
+    q, k, v, b, a, s0 = inputs.to_torch(w, "cuda")
+    carry = s0.clone()
+    o2, _ = api.frame_scan_fwd(q, k, v, b, a, carry, S_final=carry, reverse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o2.float().cpu(), torch.from_numpy(o)) and np.array_equal(carry.cpu().numpy(), S)
+
+
+def test_reverse_short_clip_every_unit():
+    w = inputs.make_config("short_clip", seed=0)
+    o, S = run_gpu(w, reverse=True)
+    ro, rS = oracle_ref(w, reverse=True)
+    check_every_unit(w, o, S, ro, rS)
+
+
+def test_reverse_of_one_frame_is_the_forward_step():
+    w = inputs.make(2, 3, 1, 100, 64, dtype="bf16", seed=74, s0_std=0.05)
+    o1, S1 = run_gpu(w)
+    o2, S2 = run_gpu(w, reverse=True)
+    assert np.array_equal(o1, o2) and np.array_equal(S1, S2)
 
 
 # ------------------------------------------------------------------ full-size workloads
