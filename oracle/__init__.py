@@ -48,6 +48,9 @@ def _load():
         lib.gdn_oracle_scan.argtypes = [ctypes.c_int] * 6 + [dp] * 6 + [
             ctypes.c_double, ctypes.c_int, ctypes.c_int, ctypes.c_int, dp, dp]
         lib.gdn_oracle_scan.restype = ctypes.c_int
+        lib.gdn_oracle_scan_bwd.argtypes = [ctypes.c_int] * 6 + [dp] * 6 + [
+            ctypes.c_double, ctypes.c_int, ctypes.c_int, ctypes.c_int] + [dp] * 8
+        lib.gdn_oracle_scan_bwd.restype = ctypes.c_int
         lib.gdn_oracle_max_threads.argtypes = []
         lib.gdn_oracle_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -96,6 +99,30 @@ def scan(q, k, v, beta, alpha, S0=None, *, eps: float = 1e-6,
     if rc != 0:
         raise RuntimeError("gdn_oracle_scan failed with code %d" % rc)
     return o, S_final
+
+
+def scan_bwd(q, k, v, beta, alpha, S0, dO, dS_final=None, *, eps: float = 1e-6,
+             gates_are_logits: bool = False, normalize_keys: bool = True, reverse: bool = False):
+    """Gradients of the scan in fp64: given dO = dL/dO and dS_final = dL/dS_final
+    (None: zeros), returns (dq, dk, dv, dbeta, dalpha, dS0), each in the
+    layout of its input (dbeta, dalpha are logit gradients with
+    gates_are_logits; dS0 is returned even when S0 is None)."""
+    q, k, v, beta, alpha, dO = (_f64(x) for x in (q, k, v, beta, alpha, dO))
+    B, F, N, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if dO.shape != (B, F, N, H, Dv):
+        raise ValueError("dO shape disagrees")
+    S0 = None if S0 is None else _f64(S0)
+    dS_final = None if dS_final is None else _f64(dS_final)
+    outs = [np.zeros_like(q), np.zeros_like(k), np.zeros_like(v), np.zeros_like(beta),
+            np.zeros_like(alpha), np.zeros((B, H, Dv, Dk))]
+    rc = _load().gdn_oracle_scan_bwd(B, H, F, N, Dk, Dv, _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+                                     _ptr(alpha), _ptr(S0), float(eps), int(bool(gates_are_logits)),
+                                     int(bool(normalize_keys)), int(bool(reverse)), _ptr(dO),
+                                     _ptr(dS_final), *[_ptr(x) for x in outs])
+    if rc != 0:
+        raise RuntimeError("gdn_oracle_scan_bwd failed with code %d" % rc)
+    return tuple(outs)
 
 
 if __name__ == "__main__":  # pragma: no cover - manual rebuild helper

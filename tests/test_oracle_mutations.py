@@ -1,5 +1,8 @@
 """Each plausible slip, planted in a private copy of the oracle (on the CPU),
-must make at least one pin in test_oracle_pins.py fail."""
+must make at least one pin fail: slips in the forward scan (gdn_oracle_scan)
+against test_oracle_pins.py, slips in the backward pass (gdn_oracle_scan_bwd)
+against test_oracle_bwd.py.  Each anchor must occur exactly once inside the
+function it targets."""
 import os
 import subprocess
 import sys
@@ -34,13 +37,38 @@ MUTATIONS = {
 }
 
 
-@pytest.mark.slow
-@pytest.mark.parametrize("name", sorted(MUTATIONS))
-def test_pins_catch_planted_mistake(name, tmp_path):
+BWD_MUTATIONS = {
+    "bwd_state_gradient_not_decayed": [("Dn[(size_t)a * Dk + c] = al * t;", "Dn[(size_t)a * Dk + c] = t;")],
+    "bwd_state_gradient_no_correction": [
+        ("for (int e = 0; e < Dk; ++e) t -= Dm[(size_t)a * Dk + e] * G[(size_t)c * Dk + e];", "")],
+    "bwd_dG_sign": [("dG[(size_t)c * Dk + e] = -al * acc;", "dG[(size_t)c * Dk + e] = al * acc;")],
+    "bwd_dG_not_symmetrised": [("(dG[(size_t)c * Dk + e] + dG[(size_t)e * Dk + c])", "2.0 * dG[(size_t)c * Dk + e]")],
+    "bwd_no_normalisation_projection": [("dki[c] = (dkh[c] - khi[c] * proj) / nrm[i];", "dki[c] = dkh[c] / nrm[i];")],
+    "bwd_dq_from_previous_state": [("acc += Sc[(size_t)a * Dk + e] * doi[a];", "acc += Sp[(size_t)a * Dk + e] * doi[a];")],
+    "bwd_dalpha_without_correction": [
+        ("for (int c = 0; c < Dk; ++c) t -= Sp[(size_t)a * Dk + c] * G[(size_t)c * Dk + e];\n"
+         "                        T[(size_t)a * Dk + e] = t;",
+         "T[(size_t)a * Dk + e] = t;")],
+    "bwd_dbeta_missing_value_term": [("db += vi[a] * uk;", "db += 0.0 * uk;")],
+    "bwd_dv_missing_beta": [("dv[ti * Dv + a] = bt[i] * uk;", "dv[ti * Dv + a] = uk;")],
+    "bwd_logit_beta_not_divided": [("db = db * sg * (1.0 - sg) / (double)N;", "db = db * sg * (1.0 - sg);")],
+}
+
+
+def _function_span(src, name):
+    start = src.index("int %s(" % name)
+    nxt = src.find("\nint ", start + 1)
+    return start, (len(src) if nxt < 0 else nxt)
+
+
+def _plant(name, tmp_path, edits, scope, pins):
     src = open(SRC).read()
-    for old, new in MUTATIONS[name]:
-        assert src.count(old) == 1, "mutation anchor not found: %r" % old
-        src = src.replace(old, new)
+    lo, hi = _function_span(src, scope)
+    body = src[lo:hi]
+    for old, new in edits:
+        assert body.count(old) == 1, "mutation anchor not found once in %s: %r" % (scope, old)
+        body = body.replace(old, new)
+    src = src[:lo] + body + src[hi:]
     c = tmp_path / "mut.c"
     so = tmp_path / "libmut.so"
     c.write_text(src)
@@ -48,6 +76,18 @@ def test_pins_catch_planted_mistake(name, tmp_path):
                     str(so), "-lm"], check=True)
     env = dict(os.environ, GDN_ORACLE_LIB=str(so), OMP_NUM_THREADS="2")
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                        os.path.join(ROOT, "tests", pins)],
                        env=env, cwd=ROOT, capture_output=True, text=True)
     assert r.returncode != 0, "no pin caught mutation %s:\n%s" % (name, r.stdout[-2000:])
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    _plant(name, tmp_path, MUTATIONS[name], "gdn_oracle_scan", "test_oracle_pins.py")
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", sorted(BWD_MUTATIONS))
+def test_backward_pins_catch_planted_mistake(name, tmp_path):
+    _plant(name, tmp_path, BWD_MUTATIONS[name], "gdn_oracle_scan_bwd", "test_oracle_bwd.py")
