@@ -17,7 +17,7 @@ GDN_F32 = 1
 GDN_FLAG_GATES_ARE_LOGITS = 0x1
 GDN_FLAG_NO_KEY_NORM = 0x2
 GDN_FLAG_REVERSE = 0x4
-GDN_NUM_KERNELS = 5
+GDN_NUM_KERNELS = 9
 
 STATUS = {0: "GDN_OK", 1: "GDN_ERR_INVALID_ARG", 2: "GDN_ERR_UNSUPPORTED", 3: "GDN_ERR_ALIGNMENT",
           4: "GDN_ERR_ALIAS", 5: "GDN_ERR_WORKSPACE", 6: "GDN_ERR_LAUNCH", 7: "GDN_ERR_NO_DEVICE"}
@@ -64,6 +64,10 @@ def load():
         fn = getattr(lib, name)
         fn.argtypes = [dp, vp, vp, vp, fp, fp, fp, vp, fp, vp, sz, vp]
         fn.restype = ctypes.c_int
+    lib.gdn_workspace_size_bwd.argtypes = [dp]
+    lib.gdn_workspace_size_bwd.restype = sz
+    lib.gdn_frame_scan_bwd.argtypes = [dp, vp, vp, vp, fp, fp, fp, vp, fp, vp, vp, vp, fp, fp, fp, vp, sz, vp]
+    lib.gdn_frame_scan_bwd.restype = ctypes.c_int
     lib.gdn_frame_scan_fwd_static.argtypes = [dp, vp, vp, vp, fp, fp, fp, vp, fp, vp]
     lib.gdn_frame_scan_fwd_static.restype = ctypes.c_int
     lib.gdn_static_scratch_bytes.argtypes = []

@@ -200,6 +200,53 @@ def frame_step(q, k, v, beta, alpha, S_in=None, *, gates_are_logits: bool = Fals
     return (o.squeeze(1) if squeeze else o), S_out
 
 
+def workspace_size_bwd(desc: GdnDesc) -> int:
+    return int(_lib.load().gdn_workspace_size_bwd(ctypes.byref(desc)))
+
+
+def frame_scan_bwd(q, k, v, beta, alpha, dO, S0=None, dS_final=None, *, gates_are_logits: bool = False,
+                   eps: float = 1e-6, normalize_keys: bool = True, reverse: bool = False,
+                   workspace=None, return_dS0: bool = True, stream=None):
+    """Gradients of frame_scan_fwd with respect to its inputs.
+
+    q, k, v, beta, alpha, S0 and the flags as for frame_scan_fwd; dO: [B,F,N,H,D]
+    in the q dtype (the loss gradient of o); dS_final: [B,H,D,D] fp32 or None
+    (zeros).  Returns (dq, dk, dv, dbeta, dalpha, dS0): dq, dk, dv in the q
+    dtype, the rest fp32 (dbeta and dalpha are logit gradients with
+    gates_are_logits; dS0 is None when return_dS0 is False).
+    """
+    B, F, N, H, D = q.shape
+    _check(q, "q", q.dtype, (B, F, N, H, D))
+    _check(k, "k", q.dtype, (B, F, N, H, D))
+    _check(v, "v", q.dtype, (B, F, N, H, D))
+    _check(beta, "beta", torch.float32, (B, F, N, H))
+    _check(alpha, "alpha", torch.float32, (B, F, H))
+    _check(dO, "dO", q.dtype, (B, F, N, H, D))
+    if S0 is not None:
+        _check(S0, "S0", torch.float32, (B, H, D, D))
+    if dS_final is not None:
+        _check(dS_final, "dS_final", torch.float32, (B, H, D, D))
+    _check_workspace(workspace, q.device)
+    desc = make_desc(B, H, F, N, D, q.dtype, gates_are_logits=gates_are_logits, eps=eps,
+                     normalize_keys=normalize_keys, reverse=reverse)
+    stream = _launch_stream(stream, q.device)
+    with torch.cuda.stream(stream):   # allocations belong to the launch stream
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        dbeta, dalpha = torch.empty_like(beta), torch.empty_like(alpha)
+        dS0 = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device) if return_dS0 else None
+        if workspace is None:
+            n = workspace_size_bwd(desc)
+            workspace = torch.empty(n, dtype=torch.uint8, device=q.device) if n > 0 else None
+        ws_bytes = 0 if workspace is None else workspace.numel()
+        st = _lib.load().gdn_frame_scan_bwd(
+            ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha), _ptr(S0), _ptr(dO),
+            _ptr(dS_final), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbeta), _ptr(dalpha), _ptr(dS0),
+            _ptr(workspace), ctypes.c_size_t(ws_bytes), ctypes.c_void_p(stream.cuda_stream))
+    if st != 0:
+        raise GdnError(st, "gdn_frame_scan_bwd")
+    return dq, dk, dv, dbeta, dalpha, dS0
+
+
 def profile_begin() -> None:
     st = _lib.load().gdn_profile_begin()
     if st != 0:

@@ -1,5 +1,6 @@
-// C ABI of the frame-wise GDN forward scan: argument checks, launch planning
-// and kernel launches.  Declarations and the contract are in include/gdn.h.
+// C ABI of the frame-wise GDN scan (forward and backward): argument checks,
+// launch planning and kernel launches.  Declarations and the contract are in
+// include/gdn.h.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -12,6 +13,7 @@
 
 #include "../../include/gdn.h"
 #include "gdn_kernels.hpp"
+#include "gdn_bwd.hpp"
 
 namespace {
 
@@ -19,9 +21,13 @@ using gdn::ScanArgs;
 
 constexpr int kVersion = 10000;  // 1.0.0
 
-enum KernelKind { K_GRAM = 0, K_STATE = 1, K_OUTPUT = 2, K_COPY = 3, K_STEP = 4 };
-const char* const kKernelNames[GDN_NUM_KERNELS] = {"frame_gram", "state_scan", "frame_output",
-                                                   "state_copy", "frame_step"};
+enum KernelKind {
+    K_GRAM = 0, K_STATE = 1, K_OUTPUT = 2, K_COPY = 3, K_STEP = 4,
+    K_WGRAM = 5, K_ADJOINT = 6, K_DQ = 7, K_DKV = 8
+};
+const char* const kKernelNames[GDN_NUM_KERNELS] = {"frame_gram", "state_scan", "frame_output", "state_copy",
+                                                   "frame_step", "w_gram",     "adjoint_scan", "frame_dq",
+                                                   "frame_dkv"};
 
 // The one-frame path sizes its workspace for this many CUs (MI355X has 256;
 // a device with fewer uses fewer token ranges).
@@ -170,18 +176,18 @@ Range rng(const void* ptr, size_t bytes) {
 bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
 bool aligned(const void* p, uintptr_t al) { return ((uintptr_t)p & (al - 1)) == 0; }
 
-template <typename T, int D>
+template <typename T, int D, bool BWD = false>
 gdn_status launch_state(ScanArgs a, hipStream_t stream) {
     using SC = gdn::StateCfg<T, D>;
     const int units = a.B * a.H;
     // one workgroup per (b, h, row slab); the slabs of a unit share an XCD
     const int grid = 8 * ((units + 7) / 8) * SC::ET;
-    ProfScope ps(K_STATE, stream);
-    hipLaunchKernelGGL((gdn::state_scan_kernel<T, D>), dim3(grid), dim3(SC::NTH), 0, stream, a);
+    ProfScope ps(BWD ? K_ADJOINT : K_STATE, stream);
+    hipLaunchKernelGGL((gdn::state_scan_kernel<T, D, BWD>), dim3(grid), dim3(SC::NTH), 0, stream, a);
     return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 
-template <typename T, int D>
+template <typename T, int D, bool TRS = false>
 gdn_status launch_output(ScanArgs a, hipStream_t stream, int cus) {
     if (a.N <= 0 || a.Fc <= 0) return GDN_OK;
     const int items = a.B * a.H * a.Fc;
@@ -202,8 +208,8 @@ gdn_status launch_output(ScanArgs a, hipStream_t stream, int cus) {
     // the last quarter of the workgroups, at most one per CU, run as halves
     const int units = items * tsplit, c = cus > 0 ? cus : 256;
     a.ntail = units / 4 < c ? units / 4 : c;
-    ProfScope ps(K_OUTPUT, stream);
-    hipLaunchKernelGGL((gdn::frame_output_kernel<T, D>), dim3(units + a.ntail), dim3(256), 0, stream, a);
+    ProfScope ps(TRS ? K_DQ : K_OUTPUT, stream);
+    hipLaunchKernelGGL((gdn::frame_output_kernel<T, D, TRS>), dim3(units + a.ntail), dim3(256), 0, stream, a);
     return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 
@@ -475,6 +481,222 @@ gdn_status run(const gdn_desc* d, bool step, const void* q, const void* k, const
                                    : dispatch_d<float>(p, a, stream, cus, carry);
 }
 
+// ---------------------------------------------------------------- backward pass
+// Workspace of gdn_frame_scan_bwd, per chunk of up to Fc frames: the forward
+// items (Gm, U, S planes), the backward items (W, X planes), the states
+// entering chunks 1.. of the forward walk, and the state gradient carried
+// between chunks.
+struct BwdPlan {
+    Plan p;
+    int nchunks = 0;
+    size_t ws2_off = 0, enter_off = 0, state_bytes = 0, dcarry_off = 0, ws_bytes = 0;
+};
+
+size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+gdn_status check_bwd(const gdn_desc* d, BwdPlan* bp) {
+    Plan& p = bp->p;
+    gdn_status st = check_desc(d, false, &p);
+    if (st != GDN_OK) return st;
+    bp->nchunks = d->F > 0 ? (d->F + p.Fc - 1) / p.Fc : 0;
+    const size_t set = round256((size_t)p.units * p.Fc * p.item_bytes);
+    bp->state_bytes = round256((size_t)p.units * p.D * p.D * sizeof(float));
+    bp->ws2_off = set;
+    bp->enter_off = 2 * set;
+    bp->dcarry_off = bp->enter_off + (size_t)(bp->nchunks > 1 ? bp->nchunks - 1 : 0) * bp->state_bytes;
+    bp->ws_bytes = (p.units > 0 && d->F > 0) ? bp->dcarry_off + bp->state_bytes : 0;
+    return GDN_OK;
+}
+
+struct BwdIO {
+    const void* dO;
+    const float* dS_final;
+    void* dq;
+    void* dk;
+    void* dv;
+    float* dbeta;
+    float* dalpha;
+    float* dS0;
+};
+
+// Launch order, all on the caller's stream.  With more than one chunk, a first
+// forward walk (frame_gram, state_scan) leaves the state entering every chunk.
+// Then per chunk, from the last visited to the first: frame_gram and
+// state_scan recompute the chunk's Gm, U and S planes; frame_gram's W pass
+// forms W_f = dO_f^T Q_f; the adjoint state_scan walks the frames the other
+// way and leaves X_f (the state gradient carried in dS0 or the workspace);
+// frame_output in its transposed role forms dq; frame_dkv forms dk, dv, dbeta
+// and dalpha.
+template <typename T, int D>
+gdn_status launch_bwd(const BwdPlan& bp, ScanArgs a, const BwdIO& g, hipStream_t stream, int cus) {
+    const Plan& p = bp.p;
+    const int units = (int)p.units;
+    unsigned char* ws = a.ws;
+    unsigned char* ws2 = ws + bp.ws2_off;
+    float* dcarry = reinterpret_cast<float*>(ws + bp.dcarry_off);
+    const float* S0 = a.S_in;
+    auto enter = [&](int v) -> float* {
+        return v == 0 ? const_cast<float*>(S0) : reinterpret_cast<float*>(ws + bp.enter_off + (size_t)(v - 1) * bp.state_bytes);
+    };
+    auto chunk = [&](int v, ScanArgs& s) {
+        const int ci = a.reverse ? bp.nchunks - 1 - v : v;
+        s.f0 = ci * p.Fc;
+        s.Fc = a.F - s.f0 < p.Fc ? a.F - s.f0 : p.Fc;
+    };
+    auto gram = [&](const ScanArgs& s, bool wpass) {
+        const int items = units * s.Fc;
+        const int grid = items < cus ? items : (cus > 0 ? cus : 256);
+        ProfScope ps(wpass ? K_WGRAM : K_GRAM, stream);
+        if (wpass)
+            hipLaunchKernelGGL((gdn::frame_gram_kernel<T, D, false, true>), dim3(grid), dim3(1024), 0, stream, s);
+        else
+            hipLaunchKernelGGL((gdn::frame_gram_kernel<T, D, false>), dim3(grid), dim3(1024), 0, stream, s);
+        return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+    };
+    gdn_status st = GDN_OK;
+    for (int v = 0; v + 1 < bp.nchunks; ++v) {      // states entering chunks 1..
+        ScanArgs s = a;
+        chunk(v, s);
+        s.S_in = enter(v);
+        s.S_out = enter(v + 1);
+        if ((st = gram(s, false)) != GDN_OK) return st;
+        if ((st = launch_state<T, D>(s, stream)) != GDN_OK) return st;
+    }
+    for (int v = bp.nchunks - 1; v >= 0; --v) {
+        ScanArgs s = a;
+        chunk(v, s);
+        s.S_in = enter(v);
+        s.S_out = nullptr;
+        if ((st = gram(s, false)) != GDN_OK) return st;
+        if ((st = launch_state<T, D>(s, stream)) != GDN_OK) return st;
+        ScanArgs w = s;                              // W_f = dO_f^T Q_f into the backward items
+        w.k = a.q;
+        w.v = g.dO;
+        w.ws = ws2;
+        if ((st = gram(w, true)) != GDN_OK) return st;
+        ScanArgs adj = s;                            // X_f, and the gradient entering the chunk
+        adj.ws2 = ws2;
+        adj.reverse = !a.reverse;
+        adj.S_in = v == bp.nchunks - 1 ? g.dS_final : dcarry;
+        adj.S_out = v == 0 ? g.dS0 : dcarry;
+        if ((st = launch_state<T, D, true>(adj, stream)) != GDN_OK) return st;
+        ScanArgs dqa = s;                            // dq = S_f^T do
+        dqa.q = g.dO;
+        dqa.o = g.dq;
+        if ((st = launch_output<T, D, true>(dqa, stream, cus)) != GDN_OK) return st;
+        {
+            // dk, dv, dbeta, dalpha (with no tokens only dalpha = <X_f, S_{f-1}>)
+            gdn::DkvArgs da;
+            da.s = s;
+            da.s.ws2 = ws2;
+            da.dk = g.dk;
+            da.dv = g.dv;
+            da.dbeta = g.dbeta;
+            da.dalpha = g.dalpha;
+            ProfScope ps(K_DKV, stream);
+            hipLaunchKernelGGL((gdn::frame_dkv_kernel<T, D>), dim3(units * s.Fc), dim3(gdn::DkvCfg<T, D>::NTH), 0,
+                               stream, da);
+            if (hipGetLastError() != hipSuccess) return GDN_ERR_LAUNCH;
+        }
+    }
+    return GDN_OK;
+}
+
+template <typename T>
+gdn_status dispatch_bwd(const BwdPlan& bp, const ScanArgs& a, const BwdIO& g, hipStream_t s, int cus) {
+    switch (bp.p.D) {
+        case 16: return launch_bwd<T, 16>(bp, a, g, s, cus);
+        case 32: return launch_bwd<T, 32>(bp, a, g, s, cus);
+        case 64: return launch_bwd<T, 64>(bp, a, g, s, cus);
+        case 128: return launch_bwd<T, 128>(bp, a, g, s, cus);
+        default: return GDN_ERR_UNSUPPORTED;
+    }
+}
+
+gdn_status run_bwd(const gdn_desc* d, const void* q, const void* k, const void* v, const float* beta,
+                   const float* alpha, const float* S0, const BwdIO& g, void* workspace, size_t workspace_bytes,
+                   void* stream_v) {
+    BwdPlan bp;
+    gdn_status st = check_bwd(d, &bp);
+    if (st != GDN_OK) return st;
+    const Plan& p = bp.p;
+    const size_t ntok = (size_t)d->B * d->F * d->N * d->H;
+    const size_t tok_bytes = ntok * (size_t)p.D * p.esz;
+    const size_t beta_bytes = ntok * sizeof(float);
+    const size_t alpha_bytes = (size_t)d->B * d->F * d->H * sizeof(float);
+    const size_t state_bytes = (size_t)p.units * p.D * p.D * sizeof(float);
+
+    if (ntok > 0 && (!q || !k || !v || !beta || !g.dO || !g.dq || !g.dk || !g.dv || !g.dbeta))
+        return GDN_ERR_INVALID_ARG;
+    if (alpha_bytes > 0 && (!alpha || !g.dalpha)) return GDN_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(g.dO, 16) || !aligned(g.dq, 16) ||
+        !aligned(g.dk, 16) || !aligned(g.dv, 16))
+        return GDN_ERR_ALIGNMENT;
+    if (!aligned(beta, 4) || !aligned(alpha, 4) || !aligned(g.dbeta, 4) || !aligned(g.dalpha, 4))
+        return GDN_ERR_ALIGNMENT;
+    if (!aligned(S0, 16) || !aligned(g.dS_final, 16) || !aligned(g.dS0, 16)) return GDN_ERR_ALIGNMENT;
+    if (bp.ws_bytes > 0) {
+        if (!workspace || workspace_bytes < bp.ws_bytes) return GDN_ERR_WORKSPACE;
+        if (!aligned(workspace, 256)) return GDN_ERR_ALIGNMENT;
+    }
+    // aliasing: outputs overlap no input, no other output and not the workspace
+    // (dS0 == dS_final exactly is allowed)
+    auto R = [](const void* ptr, size_t n) { return rng(ptr, ptr ? n : 0); };
+    const Range ins[] = {R(q, tok_bytes), R(k, tok_bytes),     R(v, tok_bytes),   R(beta, beta_bytes),
+                         R(alpha, alpha_bytes), R(S0, state_bytes), R(g.dO, tok_bytes), R(g.dS_final, state_bytes)};
+    const Range outs[] = {R(g.dq, tok_bytes),        R(g.dk, tok_bytes),         R(g.dv, tok_bytes),
+                          R(g.dbeta, beta_bytes),    R(g.dalpha, alpha_bytes),   R(g.dS0, state_bytes),
+                          R(workspace, workspace ? bp.ws_bytes : 0)};
+    const int nout = sizeof(outs) / sizeof(outs[0]), nin = sizeof(ins) / sizeof(ins[0]);
+    for (int i = 0; i < nout; ++i) {
+        for (int j = 0; j < nin; ++j) {
+            const bool inplace = i == 5 && j == 7 && g.dS0 == g.dS_final;
+            if (!inplace && overlap(outs[i], ins[j])) return GDN_ERR_ALIAS;
+        }
+        for (int j = i + 1; j < nout; ++j)
+            if (overlap(outs[i], outs[j])) return GDN_ERR_ALIAS;
+    }
+
+    if (p.units == 0) return GDN_OK;
+    if (d->F == 0 && !g.dS0) return GDN_OK;
+    int cus = 0;
+    st = check_device(&cus);
+    if (st != GDN_OK) return st;
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_v);
+    if (d->F == 0) {  // dS0 <- dS_final (or zeros)
+        if (g.dS0 == g.dS_final) return GDN_OK;
+        const size_t n = (size_t)p.units * p.D * p.D;
+        ProfScope ps(K_COPY, stream);
+        hipLaunchKernelGGL(gdn::state_copy_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, g.dS_final,
+                           g.dS0, n);
+        return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+    }
+
+    ScanArgs a;
+    memset(&a, 0, sizeof(a));
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.beta = beta;
+    a.alpha = alpha;
+    a.S_in = S0;
+    a.ws = static_cast<unsigned char*>(workspace);
+    a.B = d->B;
+    a.H = d->H;
+    a.F = d->F;
+    a.N = d->N;
+    a.logits = (d->flags & GDN_FLAG_GATES_ARE_LOGITS) ? 1 : 0;
+    a.raw_keys = (d->flags & GDN_FLAG_NO_KEY_NORM) ? 1 : 0;
+    a.reverse = (d->flags & GDN_FLAG_REVERSE) ? 1 : 0;
+    a.eps = d->eps;
+    a.tsplit = 1;
+    a.tchunk = 16;
+    a.parts = 1;
+    a.tpart = d->N;
+    return d->io_dtype == GDN_BF16 ? dispatch_bwd<uint16_t>(bp, a, g, stream, cus)
+                                   : dispatch_bwd<float>(bp, a, g, stream, cus);
+}
+
 }  // namespace
 
 extern "C" {
@@ -504,6 +726,21 @@ gdn_status gdn_frame_step(const gdn_desc* d, const void* q, const void* k, const
                           float* S_out, void* workspace, size_t workspace_bytes, void* stream) {
     if (!S_out) return GDN_ERR_INVALID_ARG;
     return run(d, true, q, k, v, beta, alpha, S_in, o, S_out, workspace, workspace_bytes, stream);
+}
+
+size_t gdn_workspace_size_bwd(const gdn_desc* d) {
+    BwdPlan bp;
+    if (check_bwd(d, &bp) != GDN_OK) return 0;
+    return bp.ws_bytes;
+}
+
+gdn_status gdn_frame_scan_bwd(const gdn_desc* d, const void* q, const void* k, const void* v,
+                              const float* beta, const float* alpha, const float* S0, const void* dO,
+                              const float* dS_final, void* dq, void* dk, void* dv, float* dbeta,
+                              float* dalpha, float* dS0, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+    const BwdIO g{dO, dS_final, dq, dk, dv, dbeta, dalpha, dS0};
+    return run_bwd(d, q, k, v, beta, alpha, S0, g, workspace, workspace_bytes, stream);
 }
 
 const char* gdn_status_string(gdn_status s) {

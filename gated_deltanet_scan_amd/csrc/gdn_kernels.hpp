@@ -257,6 +257,8 @@ struct ScanArgs {
     void* o;
     float* S_out;         // state after the last frame of the launch (may equal S_in)
     unsigned char* ws;
+    unsigned char* ws2;   // backward pass: the second item set (W_f and the adjoint
+                          // state planes), same layout as ws
     int B, H, F, N;
     int f0, Fc;           // frames [f0, f0 + Fc) of this launch; the workspace holds
                           // Fc frames per (b, h): item (b, h, fl) is (b*H + h)*Fc + fl
@@ -405,8 +407,10 @@ __device__ __forceinline__ float lane_group_sum(float x) {
 // waves of each role per SIMD let one issue while the other waits: a single
 // wave issues VALU work far below the SIMD's rate.
 // PART selects the one-frame path's variant (token ranges, fp32 partials,
-// state copy); the scan path's instantiation carries none of it.
-template <typename T, int D, bool PART>
+// state copy); the scan path's instantiation carries none of it.  WPASS is the
+// backward pass's use of the same product with unit betas and keys as given:
+// with k := Q and v := dO its U is W_f = dO_f^T Q_f, and only the U tiles run.
+template <typename T, int D, bool PART, bool WPASS = false>
 __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
     using C = GramCfg<T, D>;
     using io = IO<T>;
@@ -506,8 +510,10 @@ __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
             R.k[j] = Q::load(L.rk, L.kvo + (uint32_t)j * row_bytes);
             R.v[j] = Q::load(L.rv, L.kvo + (uint32_t)j * row_bytes);
         }
+        if constexpr (!WPASS) {
 #pragma unroll
-        for (int j = 0; j < C::TPT; ++j) R.bt[j] = bload4f(L.rb, L.bo + (uint32_t)(j * H * 4));
+            for (int j = 0; j < C::TPT; ++j) R.bt[j] = bload4f(L.rb, L.bo + (uint32_t)(j * H * 4));
+        }
         L.kvo += (uint32_t)C::TS * row_bytes;
         L.bo += (uint32_t)(C::TS * H * 4);
         if (++L.st == nst && L.kk + 1 < nmine) loader_item(L, L.kk + 1);
@@ -532,15 +538,15 @@ __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
 #pragma unroll
         for (int j = 0; j < C::TPT; ++j) ssa[j] = lane_group_sum<C::SL>(ssa[j] + ssb[j]);
 #pragma unroll
-        for (int j = 0; j < C::TPT; ++j) bt[j] = R.bt[j];
-        if (a.logits) {
+        for (int j = 0; j < C::TPT; ++j) bt[j] = WPASS ? 1.0f : R.bt[j];
+        if (!WPASS && a.logits) {
             const int t0 = (gs % nst) * C::TS + tl * C::TPT, nt = range_tokens(item_of(gs / nst));
 #pragma unroll
             for (int j = 0; j < C::TPT; ++j) bt[j] = (t0 + j < nt) ? sigmoid_f(bt[j]) * inv_n : 0.0f;
         }
 #pragma unroll
         for (int j = 0; j < C::TPT; ++j) {
-            rho[j] = a.raw_keys ? 1.0f : fminf(__builtin_amdgcn_rsqf(ssa[j]), inv_eps);   // 1 / max(|k|, eps)
+            rho[j] = (WPASS || a.raw_keys) ? 1.0f : fminf(__builtin_amdgcn_rsqf(ssa[j]), inv_eps);   // 1 / max(|k|, eps)
             xs[j] = bt[j] * rho[j];
         }
         unsigned char* sKH = buf;                   // rho k         (A of G)
@@ -550,11 +556,12 @@ __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
         for (int e = 0; e < C::FPT; ++e) {
             const float k0 = Q::get(R.k[0], e), k1 = Q::get(R.k[1], e);
             if constexpr (sizeof(T) == 2) {         // the two tokens' bf16 values in one dword
-                *reinterpret_cast<uint32_t*>(sKH + woff[e]) = pack_bf16x2(rho[0] * k0, rho[1] * k1);
+                if constexpr (!WPASS)
+                    *reinterpret_cast<uint32_t*>(sKH + woff[e]) = pack_bf16x2(rho[0] * k0, rho[1] * k1);
                 *reinterpret_cast<uint32_t*>(sXB + woff[e]) = pack_bf16x2(xs[0] * k0, xs[1] * k1);
                 *reinterpret_cast<uint32_t*>(sVT + woff[e]) = Q::bits(R.v[0], e) | (Q::bits(R.v[1], e) << 16);
             } else {
-                *reinterpret_cast<f32x2*>(sKH + woff[e]) = f32x2{rho[0] * k0, rho[1] * k1};
+                if constexpr (!WPASS) *reinterpret_cast<f32x2*>(sKH + woff[e]) = f32x2{rho[0] * k0, rho[1] * k1};
                 *reinterpret_cast<f32x2*>(sXB + woff[e]) = f32x2{xs[0] * k0, xs[1] * k1};
                 *reinterpret_cast<f32x2*>(sVT + woff[e]) = f32x2{Q::get(R.v[0], e), Q::get(R.v[1], e)};
             }
@@ -562,7 +569,6 @@ __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
     };
 
     // ---- consumer state: wave `wave` owns row blocks rt*TR.. and column blocks ct*TC..
-    const bool cbusy = wave < C::NT;
     const int rt = wave / C::NCT, ct = wave % C::NCT;
     f32x4 acc[C::TR][C::TC];
     auto zero_acc = [&]() {
@@ -580,6 +586,7 @@ __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
     // (wave-uniform) LDS bases and rows.
     static_assert(C::TR == C::TC, "square tiles");
     const bool utile = rt * C::TR >= C::RB;         // this wave's tile lies in the U rows
+    const bool cbusy = wave < C::NT && (!WPASS || utile);
     const int a_arr = utile ? 2 : (rt * C::TR < C::RB ? 0 : 1);      // LDS array of operand A
     const int b_arr = utile ? 1 : 2;                                   // LDS array of operand B
     const int a_row0 = utile ? ct * C::TC : (rt * C::TR) % C::RB;      // first block of A
@@ -845,7 +852,19 @@ template <typename T, int D> struct StateCfg {
 // than one frame.  Rows of S evolve independently, so the workgroups of a
 // state never communicate; the slabs of a head share an XCD (workgroup index
 // mod 8), so its Gm^T rows come from one L2.
-template <typename T, int D>
+//
+// BWD is the backward pass's adjoint recurrence, which has the same form.
+// With X_f the loss gradient of S_f (its direct part W_f = dO_f^T Q_f plus
+// what flows back from later frames) and the frames walked in the opposite
+// order, the state entering step f is X_f and the step makes
+//     alpha_f X_f + bf16(X_f) Gm_f + W_next,
+// W_next being W of the frame the walk visits next (none after the last):
+// that is X of the next frame, or after the last step the gradient of the
+// initial state.  Gm_f is read from the forward items (ws); W and the stored
+// planes of X_f live in the second item set (ws2): W_f where frame_gram's U
+// would be, the planes of X_f, stored at the step that enters with it, where
+// S_f would be.
+template <typename T, int D, bool BWD = false>
 __global__ __launch_bounds__(256, 1) void state_scan_kernel(ScanArgs a) {   // NTH <= 256 threads
     using C = StateCfg<T, D>;
     using io = IO<T>;
@@ -879,6 +898,8 @@ __global__ __launch_bounds__(256, 1) void state_scan_kernel(ScanArgs a) {   // N
     // this unit's workspace items through one buffer resource
     const size_t item0 = (size_t)bh * Fc;
     const rsrc_t rws = make_rsrc(a.ws + item0 * W::item_bytes, (uint32_t)(Fc * W::item_bytes));
+    // the item set holding U (W) and the stored planes
+    const rsrc_t rout = BWD ? make_rsrc(a.ws2 + item0 * W::item_bytes, (uint32_t)(Fc * W::item_bytes)) : rws;
 
     // this wave's blocks of S (fp32) and the fragment they form
     f32x4 S[C::BPW];
@@ -887,6 +908,11 @@ __global__ __launch_bounds__(256, 1) void state_scan_kernel(ScanArgs a) {   // N
     for (int q = 0; q < C::BPW; ++q) {
         const int jb = c * C::BPW + q;
         S[q] = sin ? *reinterpret_cast<const f32x4*>(sin + 16 * jb + 4 * g) : f32x4{0, 0, 0, 0};
+        if constexpr (BWD)      // X of the first frame: the carried gradient plus its W
+            S[q] += __builtin_bit_cast(
+                f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                           rout, lo16, (uint32_t)phys(0) * (uint32_t)W::item_bytes +
+                                           (uint32_t)(W::ut_off + (size_t)(jb * W::RT + at) * 1024), 0));
     }
     auto own_frag = [&]() {
         const f32x4 x = S[0];
@@ -920,12 +946,15 @@ __global__ __launch_bounds__(256, 1) void state_scan_kernel(ScanArgs a) {   // N
                     o.gm[kk][q] = f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                 }
             }
+        // BWD: W of the frame visited next; after the last frame an offset past
+        // the resource, which loads zeros
+        const uint32_t ubase = !BWD ? base : (fl + 1 < Fc ? (uint32_t)phys(fl + 1) * (uint32_t)W::item_bytes : 0x80000000u);
 #pragma unroll
         for (int q = 0; q < C::BPW; ++q) {
             const int jb = c * C::BPW + q;
             o.u[q] = __builtin_bit_cast(
                 f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                           rws, lo16, base + (uint32_t)(W::ut_off + (size_t)(jb * W::RT + at) * 1024), 0));
+                           rout, lo16, ubase + (uint32_t)(W::ut_off + (size_t)(jb * W::RT + at) * 1024), 0));
         }
     };
     // this wave's fragment (at, c) of S_fl for frame_output (zeros past the
@@ -937,14 +966,14 @@ __global__ __launch_bounds__(256, 1) void state_scan_kernel(ScanArgs a) {   // N
         const uint32_t base = fl >= 0 ? (uint32_t)phys(fl) * (uint32_t)W::item_bytes + (uint32_t)W::sp_off : 0x80000000u;
         const f32x4 y = C::BPW > 1 ? S[C::BPW - 1] : f32x4{0, 0, 0, 0};
         if constexpr (C::B16) {
-            __builtin_amdgcn_raw_buffer_store_b128(hi, rws, lo16, base + (uint32_t)((at * C::KS + c) * 1024), kStreamStore);
+            __builtin_amdgcn_raw_buffer_store_b128(hi, rout, lo16, base + (uint32_t)((at * C::KS + c) * 1024), kStreamStore);
             const u32x2 codes{codes4(S[0], hi[0], hi[1]), C::BPW > 1 ? codes4(y, hi[2], hi[3]) : 0u};
-            __builtin_amdgcn_raw_buffer_store_b64(codes, rws, (uint32_t)(lane * 8),
+            __builtin_amdgcn_raw_buffer_store_b64(codes, rout, (uint32_t)(lane * 8),
                                                   base + (uint32_t)(W::sc_rel + (at * C::KS + c) * 512), kStreamStore);
         } else {
             const uint32_t off = base + (uint32_t)((at * C::KS + c) * 2048);
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, S[0]), rws, lo16, off, kStreamStore);
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, y), rws, lo16, off + 1024, kStreamStore);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, S[0]), rout, lo16, off, kStreamStore);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, y), rout, lo16, off + 1024, kStreamStore);
         }
     };
     // One frame.  Every fragment of S_{fl-1}, this wave's own included, is read
@@ -957,7 +986,7 @@ __global__ __launch_bounds__(256, 1) void state_scan_kernel(ScanArgs a) {   // N
 #pragma unroll
         for (int kk = 0; kk < C::KS; ++kk) bs[kk] = get_x(xb, kk);
         if (reload) load_ops(nx, prev);                 // the slot frame fl-1 used
-        store_state(fl - 1, bs[c]);                     // S still holds S_{fl-1}
+        store_state(BWD ? fl : fl - 1, bs[c]);          // S still holds the state entering step fl
         const float al = sAlpha[fl];
         f32x4 acc[C::BPW];
 #pragma unroll
@@ -1009,13 +1038,115 @@ __global__ __launch_bounds__(256, 1) void state_scan_kernel(ScanArgs a) {   // N
             step(fl, ring[j], ring[(j + C::PD - 1) % C::PD], nx < Fc ? nx : Fc - 1, true);
         }
     }
-    store_state(Fc - 1, own_frag());
+    if constexpr (!BWD) store_state(Fc - 1, own_frag());
 
     // ---- final state (fp32, row-major [a][e])
     if (a.S_out) {
         float* so = a.S_out + (size_t)bh * D * D + (size_t)row * D;
 #pragma unroll
         for (int q = 0; q < C::BPW; ++q) *reinterpret_cast<f32x4*>(so + 16 * (c * C::BPW + q) + 4 * g) = S[q];
+    }
+}
+
+// ================================================================== transposed state
+// The backward products contract a state over its row index, which the
+// planes spread across lanes.  A state is staged transposed in LDS: row c of
+// the staged array holds column c of the matrix, bf16 mode as two bf16 arrays
+// (high parts, then low parts: value = hi + lo to about 2^-16 relative), fp32
+// mode as one fp32 array.
+template <typename T, int D> struct TState {
+    static constexpr bool B16 = sizeof(T) == 2;
+    static constexpr int SZ = IO<T>::bytes;
+    static constexpr int KS = (D + 31) / 32, RT = D / 16;
+    static constexpr int ROWB = D * SZ + 16;          // padded row
+    static constexpr int ARR = D * ROWB;              // one array
+    static constexpr int BYTES = (B16 ? 2 : 1) * ARR;
+};
+
+// Fragment (row tile t, step kk) of a state in the planes' layout (lane 16g+r:
+// row 16t + r, the split order's columns of step kk) as high and low parts
+// (fp32 mode: lo is not used).  The state comes from the planes at `sp` (an
+// item's S region), else from the fp32 row-major matrix `rm`, else it is zero.
+template <typename T, int D>
+__device__ __forceinline__ void state_frag(const unsigned char* sp, const float* rm, int t, int kk, int lane,
+                                           typename IO<T>::frag& hi, typename IO<T>::frag& lo) {
+    using W = WS<T, D>;
+    const int r = lane & 15, g = lane >> 4;
+    if constexpr (sizeof(T) == 2) {
+        if (sp) {
+            hi = *reinterpret_cast<const u32x4*>(sp + W::frag_off(t, kk, 0, lane));
+            lo = rem_frag(hi, *reinterpret_cast<const u32x2*>(sp + W::sc_rel + W::code_off(t, kk, lane)));
+            return;
+        }
+    } else {
+        if (sp) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(sp + W::frag_off(t, kk, 0, lane));
+            const f32x4 y = *reinterpret_cast<const f32x4*>(sp + W::frag_off(t, kk, 1, lane));
+            hi = f32x8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+            lo = IO<T>::zero();
+            return;
+        }
+    }
+    f32x4 x = f32x4{0, 0, 0, 0}, y = f32x4{0, 0, 0, 0};
+    if (rm) {
+        const float* row = rm + (size_t)(16 * t + r) * D + 32 * kk + 4 * g;
+        x = *reinterpret_cast<const f32x4*>(row);
+        if constexpr (D >= 32) y = *reinterpret_cast<const f32x4*>(row + 16);
+    }
+    if constexpr (sizeof(T) == 2) {
+        hi = u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+        lo = u32x4{pack_bf16x2(x[0] - IO<T>::get(hi, 0), x[1] - IO<T>::get(hi, 1)),
+                   pack_bf16x2(x[2] - IO<T>::get(hi, 2), x[3] - IO<T>::get(hi, 3)),
+                   pack_bf16x2(y[0] - IO<T>::get(hi, 4), y[1] - IO<T>::get(hi, 5)),
+                   pack_bf16x2(y[2] - IO<T>::get(hi, 6), y[3] - IO<T>::get(hi, 7))};
+    } else {
+        hi = f32x8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+        lo = IO<T>::zero();
+    }
+}
+
+// Writes fragment (t, kk) of lane `lane` transposed into the staged arrays at
+// `arr` (element (row, col) of the matrix goes to row col, position row).
+template <typename T, int D>
+__device__ __forceinline__ void put_transposed(unsigned char* arr, int t, int kk, int lane, const typename IO<T>::frag& hi,
+                                               const typename IO<T>::frag& lo) {
+    using TS = TState<T, D>;
+    const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int j = 0; j < (D >= 32 ? 8 : 4); ++j) {
+        const int col = 32 * kk + 16 * (j >> 2) + 4 * g + (j & 3);
+        unsigned char* p = arr + col * TS::ROWB + (16 * t + r) * TS::SZ;
+        if constexpr (sizeof(T) == 2) {
+            const uint32_t wh = hi[j >> 1], wl = lo[j >> 1];
+            *reinterpret_cast<uint16_t*>(p) = (uint16_t)((j & 1) ? (wh >> 16) : wh);
+            *reinterpret_cast<uint16_t*>(p + TS::ARR) = (uint16_t)((j & 1) ? (wl >> 16) : wl);
+        } else {
+            *reinterpret_cast<float*>(p) = hi[j];
+        }
+    }
+}
+
+// Operand fragment (row tile t, step kk) of the transposed matrix from the
+// staged arrays: lane 16g+r gets row 16t + r of M^T, i.e. column 16t + r of M,
+// in the split order of step kk.
+template <typename T, int D>
+__device__ __forceinline__ void get_transposed(const unsigned char* arr, int t, int kk, int lane,
+                                               typename IO<T>::frag& hi, typename IO<T>::frag& lo) {
+    using TS = TState<T, D>;
+    const int r = lane & 15, g = lane >> 4;
+    const unsigned char* p = arr + (16 * t + r) * TS::ROWB + (32 * kk + 4 * g) * TS::SZ;
+    if constexpr (sizeof(T) == 2) {
+        const u32x2 a0 = *reinterpret_cast<const u32x2*>(p);
+        const u32x2 a1 = D >= 32 ? *reinterpret_cast<const u32x2*>(p + 32) : u32x2{0u, 0u};
+        hi = u32x4{a0[0], a0[1], a1[0], a1[1]};
+        const u32x2 b0 = *reinterpret_cast<const u32x2*>(p + TS::ARR);
+        const u32x2 b1 = D >= 32 ? *reinterpret_cast<const u32x2*>(p + TS::ARR + 32) : u32x2{0u, 0u};
+        lo = u32x4{b0[0], b0[1], b1[0], b1[1]};
+    } else {
+        const f32x4 a0 = *reinterpret_cast<const f32x4*>(p);
+        const f32x4 a1 = D >= 32 ? *reinterpret_cast<const f32x4*>(p + 64) : f32x4{0, 0, 0, 0};
+        hi = f32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+        lo = IO<T>::zero();
     }
 }
 
@@ -1050,7 +1181,9 @@ template <typename T, int D> struct OutCfg {
 // workgroup: 64-token blocks stream from HBM PD blocks ahead into registers,
 // then into a double-buffered LDS tile from which every wave reads its B
 // fragments (a token row of Q is 8 contiguous features per lane).
-template <typename T, int D>
+// TRS is the backward pass's dq_i = S_f^T do_i: the same kernel with q := dO,
+// o := dQ and the transposed state, staged through LDS before the pipeline.
+template <typename T, int D, bool TRS = false>
 __global__ __launch_bounds__(256, 2) void frame_output_kernel(ScanArgs a) {
     using C = OutCfg<T, D>;
     using io = IO<T>;
@@ -1123,8 +1256,22 @@ __global__ __launch_bounds__(256, 2) void frame_output_kernel(ScanArgs a) {
     using W = WS<T, D>;
     const unsigned char* sp = a.ws + (size_t)item * W::item_bytes + W::sp_off;
     frag ah[C::RPW][C::KS], alw[C::RPW][C::KS];
+    if constexpr (TRS) {
+        static_assert(TState<T, D>::BYTES <= C::LDS, "the staged state fits in the Q and O tiles");
+        for (int fi = wave; fi < C::RT * C::KS; fi += 4) {
+            frag hi, lo;
+            state_frag<T, D>(sp, nullptr, fi / C::KS, fi % C::KS, lane, hi, lo);
+            put_transposed<T, D>(smem, fi / C::KS, fi % C::KS, lane, hi, lo);
+        }
+        __syncthreads();
 #pragma unroll
-    for (int i = 0; i < C::RPW; ++i) {
+        for (int i = 0; i < C::RPW; ++i)
+#pragma unroll
+            for (int ks = 0; ks < C::KS; ++ks) get_transposed<T, D>(smem, wr * C::RPW + i, ks, lane, ah[i][ks], alw[i][ks]);
+        __syncthreads();                                // before the Q tiles overwrite the staging
+    }
+#pragma unroll
+    for (int i = 0; i < C::RPW && !TRS; ++i) {
         const int rt = wr * C::RPW + i;
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {

@@ -117,6 +117,19 @@ def make(B: int, H: int, F: int, N: int, Dk: int, Dv: Optional[int] = None, *,
                     meta=dict(beta_logit=bl, alpha_logit=al))
 
 
+def make_grads(w: Workload, seed: int = 0, *, ds_std: float = 1.0):
+    """Seeded loss gradients for the backward pass: (dO [B,F,N,H,Dv], dS_final
+    [B,H,Dv,Dk]), float32 standard normals from ``default_rng((seed, 1))`` in
+    that order, dS_final scaled by ds_std (0: None); dO is rounded to bfloat16
+    for bf16 workloads."""
+    rng = np.random.default_rng((seed, 1))
+    dO = rng.standard_normal((w.B, w.F, w.N, w.H, w.Dv), dtype=np.float32)
+    dS = rng.standard_normal((w.B, w.H, w.Dv, w.Dk), dtype=np.float32) * np.float32(ds_std)
+    if w.dtype == "bf16":
+        dO = round_bf16(dO)
+    return dO, (dS.astype(np.float32) if ds_std > 0.0 else None)
+
+
 def make_config(name: str, seed: int = 0, **overrides) -> Workload:
     """Draw one of the named workloads in CONFIGS (fields may be overridden)."""
     c = dict(CONFIGS[name])

@@ -163,6 +163,41 @@ gdn_status gdn_frame_scan_fwd_static(const gdn_desc* d,
 /* Size in bytes of the static scratch array gdn_frame_scan_fwd_static uses. */
 size_t gdn_static_scratch_bytes(void);
 
+/* ------------------------------------------------------------------ backward
+ * Gradients of gdn_frame_scan_fwd, for training on minute-long sequences
+ * ("SANA-WM: democratizing Minute-Scale World Modeling with Hybrid Linear
+ * DiT", section "Problem & Motivation").  Given the forward call's inputs and
+ * flags, the output gradient dO = dL/do and dS_final = dL/dS_final (NULL means
+ * zeros), writes
+ *     dq, dk, dv  [B][F][N][H][D]  io dtype      dbeta [B][F][N][H]  float32
+ *     dalpha      [B][F][H]        float32       dS0   [B][H][Dv][Dk] float32
+ * the gradients of the loss with respect to q, k, v, beta, alpha and S0 (with
+ * GDN_FLAG_GATES_ARE_LOGITS, dbeta and dalpha are gradients of the logits).
+ * dS0 may be NULL (not written) and may be the same pointer as dS_final.  The
+ * chain rule of the recurrence in the header comment: walking the frames in
+ * the opposite order with X_f = dL/dS_f,
+ *     X_f   = sum_i do_i q_i^T + alpha_g X_g (I - G_g)     (g the frame after f)
+ *     dq_i  = S_f^T do_i          dv_i = beta_i X_f k^_i
+ *     dk^_i = beta_i (X_f^T v_i - alpha_f (M + M^T) k^_i),  M = S_{f-1}^T X_f
+ *     dbeta_i = v_i . X_f k^_i - alpha_f k^_i . M k^_i
+ *     dalpha_f = <X_f, S_{f-1} (I - G_f)>
+ * and dk from dk^ through the key normalisation.  The states S_f are
+ * recomputed, not taken from the forward call.  Results are bitwise
+ * reproducible.  Pointers, alignment (q,k,v,dO,dq,dk,dv,S0,dS_final,dS0: 16
+ * bytes; beta,alpha,dbeta,dalpha: 4), ownership, streams and errors are as for
+ * gdn_frame_scan_fwd; every output must be disjoint from every input, from
+ * the other outputs and from the workspace. */
+size_t gdn_workspace_size_bwd(const gdn_desc* d);
+gdn_status gdn_frame_scan_bwd(const gdn_desc* d,
+                              const void* q, const void* k, const void* v,
+                              const float* beta, const float* alpha,
+                              const float* S0,
+                              const void* dO, const float* dS_final,
+                              void* dq, void* dk, void* dv,
+                              float* dbeta, float* dalpha, float* dS0,
+                              void* workspace, size_t workspace_bytes,
+                              void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* gdn_status_string(gdn_status s);
 
@@ -176,12 +211,13 @@ int32_t gdn_version(void);
  * recorded event, then fills, per kernel kind k < GDN_NUM_KERNELS, the summed
  * duration in milliseconds and the number of launches.  Not thread-safe; at
  * most GDN_PROFILE_MAX_LAUNCHES launches are recorded per session. */
-#define GDN_NUM_KERNELS 5
+#define GDN_NUM_KERNELS 9
 #define GDN_PROFILE_MAX_LAUNCHES 65536
 gdn_status gdn_profile_begin(void);
 gdn_status gdn_profile_end(double* total_ms, int64_t* launches);
 /* Name of kernel kind k ("frame_gram", "state_scan", "frame_output",
- * "state_copy", "frame_step"), or NULL when k is out of range. */
+ * "state_copy", "frame_step", and for the backward pass "w_gram",
+ * "adjoint_scan", "frame_dq", "frame_dkv"), or NULL when k is out of range. */
 const char* gdn_kernel_name(int32_t k);
 
 #ifdef __cplusplus

@@ -46,10 +46,11 @@ def test_status_strings_and_version(lib):
         assert lib.gdn_status_string(s)
     assert lib.gdn_status_string(99) == b"unknown status"
     assert lib.gdn_version() >= 10000
-    assert [lib.gdn_kernel_name(i) for i in range(5)] == [b"frame_gram", b"state_scan",
+    assert [lib.gdn_kernel_name(i) for i in range(9)] == [b"frame_gram", b"state_scan",
                                                           b"frame_output", b"state_copy",
-                                                          b"frame_step"]
-    assert lib.gdn_kernel_name(5) is None and lib.gdn_kernel_name(-1) is None
+                                                          b"frame_step", b"w_gram", b"adjoint_scan",
+                                                          b"frame_dq", b"frame_dkv"]
+    assert lib.gdn_kernel_name(9) is None and lib.gdn_kernel_name(-1) is None
 
 
 def desc(B=1, H=2, F=3, N=5, D=16, io=_lib.GDN_BF16, flags=0, eps=1e-6, Dv=None):
@@ -156,10 +157,10 @@ def test_empty_calls_do_nothing(lib):
 
 def test_profile_session_without_launches(lib):
     assert lib.gdn_profile_begin() == OK
-    ms = (ctypes.c_double * 5)()
-    n = (ctypes.c_int64 * 5)()
+    ms = (ctypes.c_double * _lib.GDN_NUM_KERNELS)()
+    n = (ctypes.c_int64 * _lib.GDN_NUM_KERNELS)()
     assert lib.gdn_profile_end(ms, n) == OK
-    assert list(n) == [0] * 5 and list(ms) == [0.0] * 5
+    assert list(n) == [0] * _lib.GDN_NUM_KERNELS and list(ms) == [0.0] * _lib.GDN_NUM_KERNELS
 
 
 def test_static_scratch_rejects_what_does_not_fit(lib):
@@ -178,3 +179,66 @@ def test_static_scratch_rejects_what_does_not_fit(lib):
     d0 = desc(B=0)
     assert lib.gdn_frame_scan_fwd_static(ctypes.byref(d0), None, None, None, None, None, None,
                                          None, None, None) == OK
+
+
+# ---------------------------------------------------------------- backward entry point
+BWD_NAMES = ["q", "k", "v", "beta", "alpha", "S0", "dO", "dS_final", "dq", "dk", "dv", "dbeta", "dalpha",
+             "dS0", "ws"]
+PB = {n: BASE + i * (1 << 32) for i, n in enumerate(BWD_NAMES)}
+
+
+def call_bwd(lib, d, ws_bytes=1 << 40, **over):
+    p = dict(PB)
+    p.update(over)
+    return lib.gdn_frame_scan_bwd(None if d is None else ctypes.byref(d), *[p[n] for n in BWD_NAMES],
+                                  ctypes.c_size_t(ws_bytes), None)
+
+
+def test_bwd_workspace_size(lib):
+    # two item sets (forward: Gm, U, S planes; backward: W and the X planes),
+    # each rounded to 256 bytes, the states entering launch chunks 1.. and one
+    # carried gradient state, all per (b, h)
+    for io, per_entry in ((_lib.GDN_BF16, 10), (_lib.GDN_F32, 12)):
+        d = desc(B=2, H=3, F=5, N=7, D=64, io=io)
+        per_set = (2 * 3 * 5 * per_entry * 64 * 64 + 255) // 256 * 256
+        assert lib.gdn_workspace_size_bwd(ctypes.byref(d)) == 2 * per_set + 2 * 3 * 64 * 64 * 4
+    # D = 16: each plane's fragments are padded to a 32-wide contraction, so an
+    # item is 4 KiB (1 KiB each for Gm, the S plane and its codes, U); chunks
+    # of 256 and 44 frames
+    d = desc(B=1, H=2, F=300, N=5, D=16)
+    per_set = (2 * 256 * 4096 + 255) // 256 * 256
+    assert lib.gdn_workspace_size_bwd(ctypes.byref(d)) == 2 * per_set + 2 * (2 * 16 * 16 * 4)
+    assert lib.gdn_workspace_size_bwd(ctypes.byref(desc(D=48))) == 0
+    assert lib.gdn_workspace_size_bwd(None) == 0
+
+
+@pytest.mark.parametrize("d,expect", [
+    (None, INVALID), (desc(B=-1), INVALID), (desc(flags=0x80), INVALID), (desc(D=48), UNSUPPORTED),
+])
+def test_bwd_descriptor_errors(lib, d, expect):
+    assert call_bwd(lib, d) == expect
+
+
+def test_bwd_pointer_alignment_workspace(lib):
+    d = desc()
+    for n in ["q", "k", "v", "beta", "alpha", "dO", "dq", "dk", "dv", "dbeta", "dalpha"]:
+        assert call_bwd(lib, d, **{n: None}) == INVALID, n
+    for n in ["q", "k", "v", "dO", "dq", "dk", "dv", "S0", "dS_final", "dS0"]:
+        assert call_bwd(lib, d, **{n: PB[n] + 8}) == ALIGN, n
+    for n in ["beta", "alpha", "dbeta", "dalpha"]:
+        assert call_bwd(lib, d, **{n: PB[n] + 2}) == ALIGN, n
+    need = lib.gdn_workspace_size_bwd(ctypes.byref(d))
+    assert call_bwd(lib, d, ws_bytes=need - 1) == WORKSPACE
+    assert call_bwd(lib, d, ws=None) == WORKSPACE
+
+
+def test_bwd_aliasing(lib):
+    d = desc()
+    assert call_bwd(lib, d, dq=PB["q"]) == ALIAS
+    assert call_bwd(lib, d, dk=PB["dO"] + 64) == ALIAS
+    assert call_bwd(lib, d, dv=PB["dk"]) == ALIAS
+    assert call_bwd(lib, d, dalpha=PB["alpha"]) == ALIAS
+    assert call_bwd(lib, d, dbeta=PB["ws"]) == ALIAS
+    assert call_bwd(lib, d, dS0=PB["S0"]) == ALIAS
+    assert call_bwd(lib, d, dS0=PB["dS_final"] + 16) == ALIAS        # only exact in-place is allowed
+    assert call_bwd(lib, desc(B=0), **{n: None for n in BWD_NAMES}) == OK
