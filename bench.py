@@ -7,7 +7,8 @@ line: throughput in tokens/s from a clean timed region of K steps, the
 roofline of the dominant kernel (HIP events recorded by the library around
 every launch in a second timed region of K steps), and the fp64 CPU oracle
 timed on a bounded sample of the same workload; also the per-step GPU time of
-gdn_frame_step at the streaming workload's shape.
+gdn_frame_step at the streaming workload's shape and the backward pass
+(gdn_frame_scan_bwd) on the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload full_minute]
 """
@@ -27,7 +28,8 @@ sys.path.insert(0, ROOT)
 METRIC = "GDN scan tokens/s (121 frames×880 tok, 16h×d128, bf16) + % of roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 MFMA, published
-CSRC = ["gated_deltanet_scan_amd/csrc/gdn_kernels.hpp", "gated_deltanet_scan_amd/csrc/gdn_api.hip"]
+CSRC = ["gated_deltanet_scan_amd/csrc/gdn_kernels.hpp", "gated_deltanet_scan_amd/csrc/gdn_bwd.hpp",
+        "gated_deltanet_scan_amd/csrc/gdn_api.hip"]
 
 
 def kernel_source_hash() -> str:
@@ -242,6 +244,67 @@ def streaming_step(frames: int, reps: int = 40, warm: int = 10):
                       "alternating buffers (in place: one buffer)" % (frames, reps, warm)}
 
 
+def backward(w, q, k, v, beta, alpha, S0, steps: int, warmup: int, flush_buf):
+    """gdn_frame_scan_bwd on the workload: one step is one call (forward
+    states recomputed, all six gradients written), inputs resident in HBM.
+    Algorithmic bytes: read q, k, v, dO, beta, alpha, S0 and dS_final once,
+    write dq, dk, dv, dbeta, dalpha and dS0 once."""
+    import torch
+    from gated_deltanet_scan_amd import api, inputs
+    dO_np, dS_np = inputs.make_grads(w, seed=0)
+    io = q.dtype
+    dO = torch.from_numpy(dO_np).cuda().to(io)
+    dS = torch.from_numpy(dS_np).cuda()
+    desc = api.make_desc(w.B, w.H, w.F, w.N, w.Dk, io)
+    ws = torch.empty(api.workspace_size_bwd(desc), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        return api.frame_scan_bwd(q, k, v, beta, alpha, dO, S0, dS, workspace=ws, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+
+    def timed(profiled):
+        if profiled:
+            api.profile_begin()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps if flush_buf is not None else 1)]
+        torch.cuda.synchronize()
+        if flush_buf is not None:
+            for e0, e1 in ev:
+                flush_buf.fill_(1.0)
+                e0.record(stream)
+                step()
+                e1.record(stream)
+        else:
+            ev[0][0].record(stream)
+            for _ in range(steps):
+                step()
+            ev[0][1].record(stream)
+        torch.cuda.synchronize()
+        kern = api.profile_end() if profiled else None
+        return sum(e0.elapsed_time(e1) for e0, e1 in ev), kern
+
+    gpu_ms, _ = timed(False)
+    _, kern = timed(True)
+    ms = gpu_ms / steps
+    esz = 2 if w.dtype == "bf16" else 4
+    tok = w.B * w.F * w.N * w.H
+    state = w.B * w.H * w.Dv * w.Dk * 4
+    nbytes = 7 * tok * w.Dk * esz + 2 * tok * 4 + 2 * w.B * w.F * w.H * 4 + 3 * state
+    kernels = {name: {"avg_ms": round(t / n, 5), "launches_per_step": n / steps}
+               for name, (t, n) in kern.items() if n > 0}
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": "the same workload, gdn_frame_scan_bwd", "ms_per_step": round(ms, 5),
+            "tokens_per_s": round(w.B * w.F * w.N / (ms * 1e-3), 1),
+            "alg_bytes_per_step": nbytes, "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "kernels": kernels, "steps": steps, "warmup": warmup,
+            "timing": "HIP events around %d calls (per-kernel figures from a second region with "
+                      "per-launch events)" % steps}
+
+
 def copy_calibration(nbytes: int, steps: int):
     """A plain device copy of known size, for scaling rocprofv3 byte counters."""
     import torch
@@ -264,6 +327,8 @@ def main():
                     help="seconds of oracle work for the CPU baseline (0: skip)")
     ap.add_argument("--stream-frames", type=int, default=16,
                     help="frames of the streaming-step measurement (0: skip)")
+    ap.add_argument("--bwd-steps", type=int, default=20,
+                    help="timed calls of the backward pass (0: skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES bytes --steps times")
     ap.add_argument("--flush", choices=["auto", "on", "off"], default="auto",
@@ -397,6 +462,8 @@ def main():
                          "(%.5f ms per step with the events)" % (args.steps, prof_ms / args.steps),
         "kernel_src": src_hash,
     }
+    line["backward"] = (backward(w, q, k, v, beta, alpha, S0, args.bwd_steps, min(args.warmup, 5), junk)
+                        if args.bwd_steps > 0 else None)
     line["streaming_step"] = streaming_step(args.stream_frames) if args.stream_frames > 0 else None
     if args.cpu_budget > 0:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)

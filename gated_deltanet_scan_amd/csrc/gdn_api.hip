@@ -482,14 +482,14 @@ gdn_status run(const gdn_desc* d, bool step, const void* q, const void* k, const
 }
 
 // ---------------------------------------------------------------- backward pass
-// Workspace of gdn_frame_scan_bwd, per chunk of up to Fc frames: the forward
-// items (Gm, U, S planes), the backward items (W, X planes), the states
-// entering chunks 1.. of the forward walk, and the state gradient carried
-// between chunks.
+// Workspace of gdn_frame_scan_bwd: per chunk of up to Fc frames the forward
+// items (Gm, U, S planes) and the backward items (W, X planes); the states
+// entering chunks 1.. of the forward walk; the state gradient carried between
+// chunks; every token's key scale (fp32 [B][F][N][H]).
 struct BwdPlan {
     Plan p;
     int nchunks = 0;
-    size_t ws2_off = 0, enter_off = 0, state_bytes = 0, dcarry_off = 0, ws_bytes = 0;
+    size_t ws2_off = 0, enter_off = 0, state_bytes = 0, dcarry_off = 0, rho_off = 0, ws_bytes = 0;
 };
 
 size_t round256(size_t x) { return (x + 255) / 256 * 256; }
@@ -504,7 +504,9 @@ gdn_status check_bwd(const gdn_desc* d, BwdPlan* bp) {
     bp->ws2_off = set;
     bp->enter_off = 2 * set;
     bp->dcarry_off = bp->enter_off + (size_t)(bp->nchunks > 1 ? bp->nchunks - 1 : 0) * bp->state_bytes;
-    bp->ws_bytes = (p.units > 0 && d->F > 0) ? bp->dcarry_off + bp->state_bytes : 0;
+    bp->rho_off = bp->dcarry_off + bp->state_bytes;
+    const size_t rho_bytes = round256((size_t)d->B * d->F * d->N * d->H * sizeof(float));
+    bp->ws_bytes = (p.units > 0 && d->F > 0) ? bp->rho_off + rho_bytes : 0;
     return GDN_OK;
 }
 
@@ -543,12 +545,15 @@ gdn_status launch_bwd(const BwdPlan& bp, ScanArgs a, const BwdIO& g, hipStream_t
         s.f0 = ci * p.Fc;
         s.Fc = a.F - s.f0 < p.Fc ? a.F - s.f0 : p.Fc;
     };
-    auto gram = [&](const ScanArgs& s, bool wpass) {
+    // mode 0: G and U; 1: also every token's key scale; 2: the W pass
+    auto gram = [&](const ScanArgs& s, int mode) {
         const int items = units * s.Fc;
         const int grid = items < cus ? items : (cus > 0 ? cus : 256);
-        ProfScope ps(wpass ? K_WGRAM : K_GRAM, stream);
-        if (wpass)
+        ProfScope ps(mode == 2 ? K_WGRAM : K_GRAM, stream);
+        if (mode == 2)
             hipLaunchKernelGGL((gdn::frame_gram_kernel<T, D, false, true>), dim3(grid), dim3(1024), 0, stream, s);
+        else if (mode == 1)
+            hipLaunchKernelGGL((gdn::frame_gram_kernel<T, D, false, false, true>), dim3(grid), dim3(1024), 0, stream, s);
         else
             hipLaunchKernelGGL((gdn::frame_gram_kernel<T, D, false>), dim3(grid), dim3(1024), 0, stream, s);
         return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
@@ -559,7 +564,7 @@ gdn_status launch_bwd(const BwdPlan& bp, ScanArgs a, const BwdIO& g, hipStream_t
         chunk(v, s);
         s.S_in = enter(v);
         s.S_out = enter(v + 1);
-        if ((st = gram(s, false)) != GDN_OK) return st;
+        if ((st = gram(s, 0)) != GDN_OK) return st;
         if ((st = launch_state<T, D>(s, stream)) != GDN_OK) return st;
     }
     for (int v = bp.nchunks - 1; v >= 0; --v) {
@@ -567,13 +572,14 @@ gdn_status launch_bwd(const BwdPlan& bp, ScanArgs a, const BwdIO& g, hipStream_t
         chunk(v, s);
         s.S_in = enter(v);
         s.S_out = nullptr;
-        if ((st = gram(s, false)) != GDN_OK) return st;
+        s.rho = reinterpret_cast<float*>(ws + bp.rho_off);       // unused with keys as given
+        if ((st = gram(s, a.raw_keys ? 0 : 1)) != GDN_OK) return st;
         if ((st = launch_state<T, D>(s, stream)) != GDN_OK) return st;
         ScanArgs w = s;                              // W_f = dO_f^T Q_f into the backward items
         w.k = a.q;
         w.v = g.dO;
         w.ws = ws2;
-        if ((st = gram(w, true)) != GDN_OK) return st;
+        if ((st = gram(w, 2)) != GDN_OK) return st;
         ScanArgs adj = s;                            // X_f, and the gradient entering the chunk
         adj.ws2 = ws2;
         adj.reverse = !a.reverse;

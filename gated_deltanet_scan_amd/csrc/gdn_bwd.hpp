@@ -45,7 +45,7 @@ template <typename T, int D> struct DkvCfg {
     static constexpr int RT = D / 16;               // 16-feature tiles of the products
     static constexpr int TG = NW / RT;              // waves per tile: token groups
     static constexpr int KS = (D + 31) / 32;
-    static constexpr int ROWB = D * SZ + 16;        // padded LDS token row
+    static constexpr int ROWB = D * SZ;             // LDS token row (16-byte chunks swizzled)
     static constexpr int LPR = D * SZ / 16;         // 16-byte loads per token row
     static constexpr int RPP = NTH / LPR;           // token rows per load pass
     static constexpr int BT0 = B16 ? 64 : 32;       // (fp32: half the tokens, half the LDS)
@@ -63,9 +63,10 @@ template <typename T, int D> struct DkvCfg {
     static constexpr int KEEP = NW * MSB * 64 * (16 + KQB + 8);
     static constexpr int BIG = TOK + KEEP > PREP ? TOK + KEEP : PREP;
     static constexpr int RED = 2 * RT * BT * 8;     // per-token (s, p) partials, double-buffered
-    static constexpr int BETA = 2 * BT * 4;         // the blocks' betas
+    static constexpr int BETA = 2 * 2 * BT * 4;     // the blocks' betas and key scales
     static constexpr int LDS = BIG + RED + BETA + 2 * NW * 4;
-    static_assert(MSB >= 1 && NSB % TG == 0 && NLD >= 1 && BT % RPP == 0 && BT % 16 == 0 && PD % 2 == 0,
+    static_assert(MSB >= 1 && NSB % TG == 0 && NLD >= 1 && BT % RPP == 0 && BT % 16 == 0 && PD % 2 == 0 &&
+                      2 * BT <= NTH,
                   "block shape");
     static_assert(LDS <= 160 * 1024, "LDS");
 };
@@ -76,10 +77,15 @@ __device__ __forceinline__ float wave_sum(float x) {
     x += __shfl_xor(x, 16);
     return x + __shfl_xor(x, 32);
 }
-// Sum over the four lanes 16g + r (g = 0..3) that hold one token.
+// Sum over the four lanes 16g + r (g = 0..3) that hold one token: a swap of
+// rows 0,2 with rows 1,3, then of rows 0,1 with rows 2,3 (v_permlane16_swap
+// and v_permlane32_swap); after each swap the two registers hold a lane's own
+// value and its partner's, in some order, so their sum is the pair's sum.
 __device__ __forceinline__ float token_sum(float x) {
-    x += __shfl_xor(x, 16);
-    return x + __shfl_xor(x, 32);
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // acc += (ah + al)(bh + bl) without the al*bl term (bf16 mode); fp32 mode
@@ -152,6 +158,7 @@ __global__ __launch_bounds__(512, 1) void frame_dkv_kernel(DkvArgs da) {
     const rsrc_t rdv = make_rsrc(static_cast<T*>(da.dv) + tok0 * rowstride + (size_t)h * D, rbytes);
     const uint32_t bbytes = N > 0 ? (uint32_t)(((N - 1) * H + 1) * 4) : 0u;
     const rsrc_t rb = make_rsrc(a.beta + tok0 * H + h, bbytes);
+    const rsrc_t rrho = make_rsrc(raw ? nullptr : a.rho + tok0 * H + h, raw ? 0u : bbytes);   // raw: scale 1
     const rsrc_t rdb = make_rsrc(da.dbeta + tok0 * H + h, bbytes);
     const uint32_t row_bytes = (uint32_t)(H * D * C::SZ);
     const int nblk = (N + C::BT - 1) / C::BT;
@@ -159,15 +166,16 @@ __global__ __launch_bounds__(512, 1) void frame_dkv_kernel(DkvArgs da) {
     unsigned char* const tx = smem;                              // X^T staging
     unsigned char* const tsp = smem + TSt::BYTES;                // Sp^T staging
     float* const red = reinterpret_cast<float*>(smem + C::BIG);  // [2][RT][BT] x (s, p)
-    float* const sbeta = red + 2 * C::RT * C::BT * 2;            // [2][BT]
-    float* const wsum = sbeta + 2 * C::BT;                       // [2][NW]
+    float* const sbeta = red + 2 * C::RT * C::BT * 2;            // [2][BT] betas, then [2][BT] key scales
+    float* const wsum = sbeta + 4 * C::BT;                       // [2][NW]
 
     // ---- token blocks: loader role (row lr of each pass, 16-byte column lc)
     const int lc = tid % C::LPR, lr = tid / C::LPR;
     struct TStage {
         u32x4 k[C::NLD], v[C::NLD];
-        float bt;
+        float bt;           // threads < BT: beta of token tid; BT..2BT-1: its key scale
     };
+    const int sbt = tid % (2 * C::BT);
     auto load_blk = [&](int blk, TStage& R) {
         const uint32_t base = (uint32_t)(blk * C::BT + lr) * row_bytes + (uint32_t)(lc * 16);
 #pragma unroll
@@ -175,15 +183,17 @@ __global__ __launch_bounds__(512, 1) void frame_dkv_kernel(DkvArgs da) {
             R.k[i] = bload16_nt(rk, base + (uint32_t)(i * C::RPP) * row_bytes);
             R.v[i] = bload16_nt(rv, base + (uint32_t)(i * C::RPP) * row_bytes);
         }
-        R.bt = bload4f(rb, (uint32_t)((blk * C::BT + (tid % C::BT)) * H * 4));
+        const uint32_t boff = (uint32_t)((blk * C::BT + (sbt % C::BT)) * H * 4);
+        R.bt = sbt < C::BT ? bload4f(rb, boff) : bload4f(rrho, boff);
     };
     auto put_blk = [&](const TStage& R, unsigned char* buf, float* sb) {
 #pragma unroll
         for (int i = 0; i < C::NLD; ++i) {
-            *reinterpret_cast<u32x4*>(buf + (lr + i * C::RPP) * C::ROWB + lc * 16) = R.k[i];
-            *reinterpret_cast<u32x4*>(buf + C::TBUF + (lr + i * C::RPP) * C::ROWB + lc * 16) = R.v[i];
+            const int row = lr + i * C::RPP;
+            *reinterpret_cast<u32x4*>(buf + swz<C::ROWB>(row, lc * 16)) = R.k[i];
+            *reinterpret_cast<u32x4*>(buf + C::TBUF + swz<C::ROWB>(row, lc * 16)) = R.v[i];
         }
-        if (tid < C::BT) sb[tid] = R.bt;
+        if (tid < 2 * C::BT) sb[tid < C::BT ? tid : C::BT + tid] = R.bt;
     };
     TStage ring[C::PD];
 #pragma unroll
@@ -195,22 +205,31 @@ __global__ __launch_bounds__(512, 1) void frame_dkv_kernel(DkvArgs da) {
     const int flp = a.reverse ? fl + 1 : fl - 1;
     const unsigned char* spp = first ? nullptr : a.ws + ((size_t)bh * a.Fc + flp) * W::item_bytes + W::sp_off;
     const float* srm = (first && a.S_in) ? a.S_in + (size_t)bh * D * D : nullptr;
-    float dot = 0.0f;                                            // <X, Sp>, this thread's share
-    for (int fi = wave; fi < C::RT * C::KS; fi += C::NW) {
-        const int t = fi / C::KS, kk = fi % C::KS;
-        frag xh, xl, sh, sl;
-        state_frag<T, D>(xp, nullptr, t, kk, lane, xh, xl);
-        state_frag<T, D>(spp, srm, t, kk, lane, sh, sl);
-        put_transposed<T, D>(tx, t, kk, lane, xh, xl);
-        put_transposed<T, D>(tsp, t, kk, lane, sh, sl);
+    // Every global load of the prologue is issued before the first LDS write
+    // (a store between them would keep the compiler from hoisting the loads):
+    // this wave's rows of X (tile wr, every step), and of Sp the steps it
+    // stages.  Wave (wr, wt) stages the fragments (wr, kk) of X and Sp with
+    // kk = wt mod TG, so every fragment is staged exactly once.
+    frag xd_h[C::KS], xd_l[C::KS];                               // rows 16wr.. of X
+    frag sp_h[C::KS], sp_l[C::KS];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) dot += (io::get(xh, e) + io::get(xl, e)) * (io::get(sh, e) + io::get(sl, e));
+    for (int kk = 0; kk < C::KS; ++kk) state_frag<T, D>(xp, nullptr, wr, kk, lane, xd_h[kk], xd_l[kk]);
+#pragma unroll
+    for (int kk = 0; kk < C::KS; ++kk)
+        if (kk % C::TG == wt) state_frag<T, D>(spp, srm, wr, kk, lane, sp_h[kk], sp_l[kk]);
+    float dot = 0.0f;                                            // <X, Sp>, this thread's share
+#pragma unroll
+    for (int kk = 0; kk < C::KS; ++kk) {
+        if (kk % C::TG == wt) {
+            put_transposed<T, D>(tx, wr, kk, lane, xd_h[kk], xd_l[kk]);
+            put_transposed<T, D>(tsp, wr, kk, lane, sp_h[kk], sp_l[kk]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                dot += (io::get(xd_h[kk], e) + io::get(xd_l[kk], e)) * (io::get(sp_h[kk], e) + io::get(sp_l[kk], e));
+        }
     }
     dot = wave_sum(dot);
     if (lane == 0) wsum[wave] = dot;
-    frag xd_h[C::KS], xd_l[C::KS];                               // rows 16wr.. of X
-#pragma unroll
-    for (int kk = 0; kk < C::KS; ++kk) state_frag<T, D>(xp, nullptr, wr, kk, lane, xd_h[kk], xd_l[kk]);
     __syncthreads();
 
     frag xt_h[C::KS], xt_l[C::KS], ms_h[C::KS], ms_l[C::KS];
@@ -273,21 +292,25 @@ __global__ __launch_bounds__(512, 1) void frame_dkv_kernel(DkvArgs da) {
         return f32x4{__uint_as_float(w2[0] << 16), __uint_as_float(w2[0] & 0xffff0000u), __uint_as_float(w2[1] << 16),
                      __uint_as_float(w2[1] & 0xffff0000u)};
     };
-    auto own4 = [&](const unsigned char* row) {
+    // this lane's four features of token row `row` of a tile (raw bits in bf16 mode)
+    auto own_raw = [&](const unsigned char* tile, int row) {
         if constexpr (C::B16)
-            return unpack4(*reinterpret_cast<const u32x2*>(row + fcol));
+            return *reinterpret_cast<const u32x2*>(tile + swz<C::ROWB>(row, fcol));
         else
-            return *reinterpret_cast<const f32x4*>(row + fcol);
+            return *reinterpret_cast<const f32x4*>(tile + swz<C::ROWB>(row, fcol));
     };
-    auto split_frag = [&](const unsigned char* row, int kk) {
-        const unsigned char* src = row + (kk * 32 + 4 * g) * C::SZ;
+    // split-order fragment of step kk of token row `row`
+    auto split_frag = [&](const unsigned char* tile, int row, int kk) {
+        const int b0 = (kk * 32 + 4 * g) * C::SZ;
+        const unsigned char* p0 = tile + swz<C::ROWB>(row, b0);
+        const unsigned char* p1 = tile + swz<C::ROWB>(row, b0 + 16 * C::SZ);
         if constexpr (C::B16) {
-            const u32x2 lo = *reinterpret_cast<const u32x2*>(src);
-            const u32x2 hi = D >= 32 ? *reinterpret_cast<const u32x2*>(src + 32) : u32x2{0u, 0u};
+            const u32x2 lo = *reinterpret_cast<const u32x2*>(p0);
+            const u32x2 hi = D >= 32 ? *reinterpret_cast<const u32x2*>(p1) : u32x2{0u, 0u};
             return frag{lo[0], lo[1], hi[0], hi[1]};
         } else {
-            const f32x4 lo = *reinterpret_cast<const f32x4*>(src);
-            const f32x4 hi = D >= 32 ? *reinterpret_cast<const f32x4*>(src + 64) : f32x4{0, 0, 0, 0};
+            const f32x4 lo = *reinterpret_cast<const f32x4*>(p0);
+            const f32x4 hi = D >= 32 ? *reinterpret_cast<const f32x4*>(p1) : f32x4{0, 0, 0, 0};
             return frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         }
     };
@@ -304,37 +327,35 @@ __global__ __launch_bounds__(512, 1) void frame_dkv_kernel(DkvArgs da) {
         for (int m = 0; m < C::MSB; ++m) {
             const int tl = (wt + C::TG * m) * 16 + r;            // token of the block
             const int n = blk * C::BT + tl;
-            const unsigned char* krow = buf + tl * C::ROWB;
-            const unsigned char* vrow = krow + C::TBUF;
-            f32x4 y = f32x4{0, 0, 0, 0}, z = f32x4{0, 0, 0, 0}, w = f32x4{0, 0, 0, 0};
-            float ss = 0.0f;
+            const unsigned char* kt = buf;
+            const unsigned char* vt = buf + C::TBUF;
+            // high and low parts accumulate separately: six independent MFMA chains
+            f32x4 yh = f32x4{0, 0, 0, 0}, zh = yh, wh = yh, yl = yh, zl = yh, wl = yh;
 #pragma unroll
             for (int kk = 0; kk < C::KS; ++kk) {
-                const frag kb = split_frag(krow, kk), vb = split_frag(vrow, kk);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) ss = fmaf(io::get(kb, e), io::get(kb, e), ss);
-                io::mma(y, xd_h[kk], kb);
-                io::mma(z, ms_h[kk], kb);
-                io::mma(w, xt_h[kk], vb);
+                const frag kb = split_frag(kt, tl, kk), vb = split_frag(vt, tl, kk);
+                io::mma(yh, xd_h[kk], kb);
+                io::mma(zh, ms_h[kk], kb);
+                io::mma(wh, xt_h[kk], vb);
                 if constexpr (C::B16) {
-                    io::mma(y, xd_l[kk], kb);
-                    io::mma(z, ms_l[kk], kb);
-                    io::mma(w, xt_l[kk], vb);
+                    io::mma(yl, xd_l[kk], kb);
+                    io::mma(zl, ms_l[kk], kb);
+                    io::mma(wl, xt_l[kk], vb);
                 }
             }
-            ss = token_sum(ss);
-            const float rs = __builtin_amdgcn_rsqf(ss);
-            const float rho = raw ? 1.0f : fminf(rs, inv_eps);
-            const bool clamped = !raw && rs >= inv_eps;
+            const f32x4 y = yh + yl, z = zh + zl, w = wh + wl;
+            const float rho = raw ? 1.0f : sb[2 * C::BT + tl];   // 1 / max(|k|, eps), from the recomputation
+            const bool proj = !raw && rho < inv_eps;             // |k| > eps: dk has the projection term
             u32x2 kraw = u32x2{0u, 0u};
-            f32x4 kq;
+            f32x4 kq, vq;
             if constexpr (C::B16) {
-                kraw = *reinterpret_cast<const u32x2*>(krow + fcol);
+                kraw = own_raw(kt, tl);
                 kq = unpack4(kraw);
+                vq = unpack4(own_raw(vt, tl));
             } else {
-                kq = own4(krow);
+                kq = own_raw(kt, tl);
+                vq = own_raw(vt, tl);
             }
-            const f32x4 vq = own4(vrow);
             const f32x4 ys = y * rho, zs = z * rho;
             float sp = 0.0f, pp = 0.0f;
 #pragma unroll
@@ -354,7 +375,7 @@ __global__ __launch_bounds__(512, 1) void frame_dkv_kernel(DkvArgs da) {
                 *reinterpret_cast<u32x2*>(keep_kq(m)) = kraw;
             else
                 *reinterpret_cast<f32x4*>(keep_kq(m)) = kq;
-            *keep_rb(m) = f32x2{(raw || clamped) ? -rho : rho, bt};
+            *keep_rb(m) = f32x2{proj ? rho : -rho, bt};
         }
     };
     auto finish = [&](const float* rd, int blk) {

@@ -280,6 +280,9 @@ struct ScanArgs {
     float* spart;
     float* scopy;
     int ncopy;
+    // Backward pass: the recomputing frame_gram also writes every token's key
+    // scale rho = 1 / max(|k|, eps) here, fp32 [B][F][N][H].
+    float* rho;
 };
 
 // Partial G and U of one token range (one-frame path), both fp32: G in the
@@ -410,7 +413,9 @@ __device__ __forceinline__ float lane_group_sum(float x) {
 // state copy); the scan path's instantiation carries none of it.  WPASS is the
 // backward pass's use of the same product with unit betas and keys as given:
 // with k := Q and v := dO its U is W_f = dO_f^T Q_f, and only the U tiles run.
-template <typename T, int D, bool PART, bool WPASS = false>
+// RHO (the backward pass's recomputation) also writes each token's key scale
+// to a.rho.
+template <typename T, int D, bool PART, bool WPASS = false, bool RHO = false>
 __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
     using C = GramCfg<T, D>;
     using io = IO<T>;
@@ -548,6 +553,15 @@ __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
         for (int j = 0; j < C::TPT; ++j) {
             rho[j] = (WPASS || a.raw_keys) ? 1.0f : fminf(__builtin_amdgcn_rsqf(ssa[j]), inv_eps);   // 1 / max(|k|, eps)
             xs[j] = bt[j] * rho[j];
+        }
+        if constexpr (RHO) {
+            if (s == 0) {                           // one lane of each token
+                const Item it = item_of(gs / nst);
+                const int t0 = (gs % nst) * C::TS + tl * C::TPT, nt = range_tokens(it);
+#pragma unroll
+                for (int j = 0; j < C::TPT; ++j)
+                    if (t0 + j < nt) a.rho[(((size_t)it.b * a.F + it.f) * N + t0 + j) * H + it.h] = rho[j];
+            }
         }
         unsigned char* sKH = buf;                   // rho k         (A of G)
         unsigned char* sVT = buf + C::ARR;          // v             (A of U)
@@ -1058,10 +1072,21 @@ template <typename T, int D> struct TState {
     static constexpr bool B16 = sizeof(T) == 2;
     static constexpr int SZ = IO<T>::bytes;
     static constexpr int KS = (D + 31) / 32, RT = D / 16;
-    static constexpr int ROWB = D * SZ + 16;          // padded row
+    static constexpr int ROWB = D * SZ;               // one row
     static constexpr int ARR = D * ROWB;              // one array
     static constexpr int BYTES = (B16 ? 2 : 1) * ARR;
 };
+
+// Byte offset of byte `b` of row `row` in an LDS tile of ROWB-byte rows whose
+// 16-byte chunks are XOR-swizzled by the row: the split-order fragment reads
+// (16 consecutive rows, 8 or 16 bytes at the same column) then fall on
+// distinct banks.
+template <int ROWB>
+__device__ __forceinline__ int swz(int row, int b) {
+    constexpr int CPR = ROWB / 16;                    // chunks per row
+    constexpr int M = (CPR < 16 ? CPR : 16) - 1;
+    return row * ROWB + ((((b >> 4) ^ (row & M))) << 4) + (b & 15);
+}
 
 // Fragment (row tile t, step kk) of a state in the planes' layout (lane 16g+r:
 // row 16t + r, the split order's columns of step kk) as high and low parts
@@ -1115,7 +1140,7 @@ __device__ __forceinline__ void put_transposed(unsigned char* arr, int t, int kk
 #pragma unroll
     for (int j = 0; j < (D >= 32 ? 8 : 4); ++j) {
         const int col = 32 * kk + 16 * (j >> 2) + 4 * g + (j & 3);
-        unsigned char* p = arr + col * TS::ROWB + (16 * t + r) * TS::SZ;
+        unsigned char* p = arr + swz<TS::ROWB>(col, (16 * t + r) * TS::SZ);
         if constexpr (sizeof(T) == 2) {
             const uint32_t wh = hi[j >> 1], wl = lo[j >> 1];
             *reinterpret_cast<uint16_t*>(p) = (uint16_t)((j & 1) ? (wh >> 16) : wh);
@@ -1134,17 +1159,19 @@ __device__ __forceinline__ void get_transposed(const unsigned char* arr, int t, 
                                                typename IO<T>::frag& hi, typename IO<T>::frag& lo) {
     using TS = TState<T, D>;
     const int r = lane & 15, g = lane >> 4;
-    const unsigned char* p = arr + (16 * t + r) * TS::ROWB + (32 * kk + 4 * g) * TS::SZ;
+    const int row = 16 * t + r, b0 = (32 * kk + 4 * g) * TS::SZ;
+    const unsigned char* p0 = arr + swz<TS::ROWB>(row, b0);
+    const unsigned char* p1 = arr + swz<TS::ROWB>(row, b0 + 16 * TS::SZ);
     if constexpr (sizeof(T) == 2) {
-        const u32x2 a0 = *reinterpret_cast<const u32x2*>(p);
-        const u32x2 a1 = D >= 32 ? *reinterpret_cast<const u32x2*>(p + 32) : u32x2{0u, 0u};
+        const u32x2 a0 = *reinterpret_cast<const u32x2*>(p0);
+        const u32x2 a1 = D >= 32 ? *reinterpret_cast<const u32x2*>(p1) : u32x2{0u, 0u};
         hi = u32x4{a0[0], a0[1], a1[0], a1[1]};
-        const u32x2 b0 = *reinterpret_cast<const u32x2*>(p + TS::ARR);
-        const u32x2 b1 = D >= 32 ? *reinterpret_cast<const u32x2*>(p + TS::ARR + 32) : u32x2{0u, 0u};
-        lo = u32x4{b0[0], b0[1], b1[0], b1[1]};
+        const u32x2 c0 = *reinterpret_cast<const u32x2*>(p0 + TS::ARR);
+        const u32x2 c1 = D >= 32 ? *reinterpret_cast<const u32x2*>(p1 + TS::ARR) : u32x2{0u, 0u};
+        lo = u32x4{c0[0], c0[1], c1[0], c1[1]};
     } else {
-        const f32x4 a0 = *reinterpret_cast<const f32x4*>(p);
-        const f32x4 a1 = D >= 32 ? *reinterpret_cast<const f32x4*>(p + 64) : f32x4{0, 0, 0, 0};
+        const f32x4 a0 = *reinterpret_cast<const f32x4*>(p0);
+        const f32x4 a1 = D >= 32 ? *reinterpret_cast<const f32x4*>(p1) : f32x4{0, 0, 0, 0};
         hi = f32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
         lo = IO<T>::zero();
     }

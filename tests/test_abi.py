@@ -197,17 +197,20 @@ def call_bwd(lib, d, ws_bytes=1 << 40, **over):
 def test_bwd_workspace_size(lib):
     # two item sets (forward: Gm, U, S planes; backward: W and the X planes),
     # each rounded to 256 bytes, the states entering launch chunks 1.. and one
-    # carried gradient state, all per (b, h)
+    # carried gradient state, all per (b, h), then a key scale per token
+    # (rounded to 256 bytes)
+    r256 = lambda x: (x + 255) // 256 * 256
     for io, per_entry in ((_lib.GDN_BF16, 10), (_lib.GDN_F32, 12)):
         d = desc(B=2, H=3, F=5, N=7, D=64, io=io)
-        per_set = (2 * 3 * 5 * per_entry * 64 * 64 + 255) // 256 * 256
-        assert lib.gdn_workspace_size_bwd(ctypes.byref(d)) == 2 * per_set + 2 * 3 * 64 * 64 * 4
+        per_set = r256(2 * 3 * 5 * per_entry * 64 * 64)
+        assert lib.gdn_workspace_size_bwd(ctypes.byref(d)) == \
+            2 * per_set + 2 * 3 * 64 * 64 * 4 + r256(2 * 5 * 7 * 3 * 4)
     # D = 16: each plane's fragments are padded to a 32-wide contraction, so an
     # item is 4 KiB (1 KiB each for Gm, the S plane and its codes, U); chunks
     # of 256 and 44 frames
     d = desc(B=1, H=2, F=300, N=5, D=16)
-    per_set = (2 * 256 * 4096 + 255) // 256 * 256
-    assert lib.gdn_workspace_size_bwd(ctypes.byref(d)) == 2 * per_set + 2 * (2 * 16 * 16 * 4)
+    per_set = r256(2 * 256 * 4096)
+    assert lib.gdn_workspace_size_bwd(ctypes.byref(d)) == 2 * per_set + 2 * (2 * 16 * 16 * 4) + r256(300 * 5 * 2 * 4)
     assert lib.gdn_workspace_size_bwd(ctypes.byref(desc(D=48))) == 0
     assert lib.gdn_workspace_size_bwd(None) == 0
 
