@@ -45,7 +45,15 @@ template <typename T, int D> struct DkvCfg {
     static constexpr int RT = D / 16;               // 16-feature tiles of the products
     static constexpr int TG = NW / RT;              // waves per tile: token groups
     static constexpr int KS = (D + 31) / 32;
-    static constexpr int ROWB = D * SZ;             // LDS token row (16-byte chunks swizzled)
+    // LDS token row, padded by 16 bytes.  Within each 32-feature window the
+    // 4-feature pieces are stored in the order 0,4,1,5,2,6,3,7, so that the
+    // split-order fragment of lane group g (pieces g and 4+g) is contiguous
+    // (at D = 16 the window is 16 features and keeps its order).
+    static constexpr int ROWB = D * SZ + 16;
+    static constexpr int PIECE = 4 * SZ;            // bytes of 4 features
+    __device__ static constexpr int pos(int q) { return D >= 32 ? (q < 4 ? 2 * q : 2 * (q - 4) + 1) : q; }
+    // byte offset in a row of the piece holding features 4p .. 4p+3
+    __device__ static constexpr int piece_off(int p) { return (p >> 3) * 8 * PIECE + pos(p & 7) * PIECE; }
     static constexpr int LPR = D * SZ / 16;         // 16-byte loads per token row
     static constexpr int RPP = NTH / LPR;           // token rows per load pass
     static constexpr int BT0 = B16 ? 64 : 32;       // (fp32: half the tokens, half the LDS)
@@ -190,8 +198,17 @@ __global__ __launch_bounds__(512, 1) void frame_dkv_kernel(DkvArgs da) {
 #pragma unroll
         for (int i = 0; i < C::NLD; ++i) {
             const int row = lr + i * C::RPP;
-            *reinterpret_cast<u32x4*>(buf + swz<C::ROWB>(row, lc * 16)) = R.k[i];
-            *reinterpret_cast<u32x4*>(buf + C::TBUF + swz<C::ROWB>(row, lc * 16)) = R.v[i];
+            unsigned char* kr = buf + row * C::ROWB;
+            unsigned char* vr = kr + C::TBUF;
+            if constexpr (C::B16) {                              // a 16-byte chunk is pieces 2lc, 2lc+1
+                *reinterpret_cast<u32x2*>(kr + C::piece_off(2 * lc)) = u32x2{R.k[i][0], R.k[i][1]};
+                *reinterpret_cast<u32x2*>(kr + C::piece_off(2 * lc + 1)) = u32x2{R.k[i][2], R.k[i][3]};
+                *reinterpret_cast<u32x2*>(vr + C::piece_off(2 * lc)) = u32x2{R.v[i][0], R.v[i][1]};
+                *reinterpret_cast<u32x2*>(vr + C::piece_off(2 * lc + 1)) = u32x2{R.v[i][2], R.v[i][3]};
+            } else {                                             // a 16-byte chunk is piece lc
+                *reinterpret_cast<u32x4*>(kr + C::piece_off(lc)) = R.k[i];
+                *reinterpret_cast<u32x4*>(vr + C::piece_off(lc)) = R.v[i];
+            }
         }
         if (tid < 2 * C::BT) sb[tid < C::BT ? tid : C::BT + tid] = R.bt;
     };
@@ -210,17 +227,26 @@ __global__ __launch_bounds__(512, 1) void frame_dkv_kernel(DkvArgs da) {
     // this wave's rows of X (tile wr, every step), and of Sp the steps it
     // stages.  Wave (wr, wt) stages the fragments (wr, kk) of X and Sp with
     // kk = wt mod TG, so every fragment is staged exactly once.
+    // (The source of Sp is chosen once, outside the loops: a choice per load
+    // made the compiler wait for each load before issuing the next.)
+    auto staged = [&](int kk) { return C::TG == 1 || kk % C::TG == wt; };
     frag xd_h[C::KS], xd_l[C::KS];                               // rows 16wr.. of X
     frag sp_h[C::KS], sp_l[C::KS];
 #pragma unroll
     for (int kk = 0; kk < C::KS; ++kk) state_frag<T, D>(xp, nullptr, wr, kk, lane, xd_h[kk], xd_l[kk]);
+    if (spp) {
 #pragma unroll
-    for (int kk = 0; kk < C::KS; ++kk)
-        if (kk % C::TG == wt) state_frag<T, D>(spp, srm, wr, kk, lane, sp_h[kk], sp_l[kk]);
+        for (int kk = 0; kk < C::KS; ++kk)
+            if (staged(kk)) state_frag<T, D>(spp, nullptr, wr, kk, lane, sp_h[kk], sp_l[kk]);
+    } else {
+#pragma unroll
+        for (int kk = 0; kk < C::KS; ++kk)
+            if (staged(kk)) state_frag<T, D>(nullptr, srm, wr, kk, lane, sp_h[kk], sp_l[kk]);
+    }
     float dot = 0.0f;                                            // <X, Sp>, this thread's share
 #pragma unroll
     for (int kk = 0; kk < C::KS; ++kk) {
-        if (kk % C::TG == wt) {
+        if (staged(kk)) {
             put_transposed<T, D>(tx, wr, kk, lane, xd_h[kk], xd_l[kk]);
             put_transposed<T, D>(tsp, wr, kk, lane, sp_h[kk], sp_l[kk]);
 #pragma unroll
@@ -241,12 +267,14 @@ __global__ __launch_bounds__(512, 1) void frame_dkv_kernel(DkvArgs da) {
             get_transposed<T, D>(tsp, wr, kk, lane, st_h[kk], st_l[kk]);
         }
         // column block wr of Ms: block i = (Sp^T)_i X_wr + (X^T)_i Sp_wr, contracted over rows
+        // (steps outermost, so that consecutive products go to different blocks)
         f32x4 m[C::RT];
 #pragma unroll
-        for (int i = 0; i < C::RT; ++i) {
-            m[i] = f32x4{0, 0, 0, 0};
+        for (int i = 0; i < C::RT; ++i) m[i] = f32x4{0, 0, 0, 0};
 #pragma unroll
-            for (int kk = 0; kk < C::KS; ++kk) {
+        for (int kk = 0; kk < C::KS; ++kk) {
+#pragma unroll
+            for (int i = 0; i < C::RT; ++i) {
                 frag ah, alo;
                 get_transposed<T, D>(tsp, i, kk, lane, ah, alo);
                 mma_hl<T>(m[i], ah, alo, xt_h[kk], xt_l[kk]);
@@ -293,25 +321,33 @@ __global__ __launch_bounds__(512, 1) void frame_dkv_kernel(DkvArgs da) {
                      __uint_as_float(w2[1] & 0xffff0000u)};
     };
     // this lane's four features of token row `row` of a tile (raw bits in bf16 mode)
+    const int own_off = C::piece_off(4 * wr + g);                // piece of features 16wr + 4g ..
     auto own_raw = [&](const unsigned char* tile, int row) {
         if constexpr (C::B16)
-            return *reinterpret_cast<const u32x2*>(tile + swz<C::ROWB>(row, fcol));
+            return *reinterpret_cast<const u32x2*>(tile + row * C::ROWB + own_off);
         else
-            return *reinterpret_cast<const f32x4*>(tile + swz<C::ROWB>(row, fcol));
+            return *reinterpret_cast<const f32x4*>(tile + row * C::ROWB + own_off);
     };
     // split-order fragment of step kk of token row `row`
     auto split_frag = [&](const unsigned char* tile, int row, int kk) {
-        const int b0 = (kk * 32 + 4 * g) * C::SZ;
-        const unsigned char* p0 = tile + swz<C::ROWB>(row, b0);
-        const unsigned char* p1 = tile + swz<C::ROWB>(row, b0 + 16 * C::SZ);
+        // pieces g and 4+g of window kk: contiguous (D = 16: piece g, no second half)
+        const unsigned char* p0 = tile + row * C::ROWB + kk * 8 * C::PIECE + 2 * g * C::PIECE;
         if constexpr (C::B16) {
-            const u32x2 lo = *reinterpret_cast<const u32x2*>(p0);
-            const u32x2 hi = D >= 32 ? *reinterpret_cast<const u32x2*>(p1) : u32x2{0u, 0u};
-            return frag{lo[0], lo[1], hi[0], hi[1]};
+            if constexpr (D >= 32) {
+                return *reinterpret_cast<const frag*>(p0);
+            } else {
+                const u32x2 lo = *reinterpret_cast<const u32x2*>(tile + row * C::ROWB + g * C::PIECE);
+                return frag{lo[0], lo[1], 0u, 0u};
+            }
         } else {
-            const f32x4 lo = *reinterpret_cast<const f32x4*>(p0);
-            const f32x4 hi = D >= 32 ? *reinterpret_cast<const f32x4*>(p1) : f32x4{0, 0, 0, 0};
-            return frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            if constexpr (D >= 32) {
+                const f32x4 lo = *reinterpret_cast<const f32x4*>(p0);
+                const f32x4 hi = *reinterpret_cast<const f32x4*>(p0 + 16);
+                return frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            } else {
+                const f32x4 lo = *reinterpret_cast<const f32x4*>(tile + row * C::ROWB + g * C::PIECE);
+                return frag{lo[0], lo[1], lo[2], lo[3], 0.0f, 0.0f, 0.0f, 0.0f};
+            }
         }
     };
     auto store4 = [&](rsrc_t rs, int n, f32x4 val) {
@@ -356,21 +392,22 @@ __global__ __launch_bounds__(512, 1) void frame_dkv_kernel(DkvArgs da) {
                 kq = own_raw(kt, tl);
                 vq = own_raw(vt, tl);
             }
-            const f32x4 ys = y * rho, zs = z * rho;
+            // y and z here are X k and Ms k; the key scale enters as scalars
             float sp = 0.0f, pp = 0.0f;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                sp = fmaf(kq[j], zs[j], sp);
-                pp = fmaf(vq[j], ys[j], pp);
+                sp = fmaf(kq[j], z[j], sp);
+                pp = fmaf(vq[j], y[j], pp);
             }
-            sp = token_sum(sp * rho);                            // k^ . z over this tile's features
-            pp = token_sum(pp);
+            sp = token_sum(sp * (rho * rho));                    // k^ . Ms k^ over this tile's features
+            pp = token_sum(pp * rho);                            // v . X k^
             if (g == 0) *reinterpret_cast<f32x2*>(rd + 2 * (wr * C::BT + tl)) = f32x2{sp, pp};
             float bt = sb[tl];
             if (a.logits) bt = sigmoid_f(bt) * inv_n;
             if (n >= N) bt = 0.0f;
-            store4(rdv, n, ys * bt);
-            *keep_dkh(m) = (w - zs * al) * bt;
+            const float br = bt * rho;
+            store4(rdv, n, y * br);                              // dv = beta X k^
+            *keep_dkh(m) = w * bt - z * (al * br);               // dk^ = beta (X^T v - alpha Ms k^)
             if constexpr (C::B16)
                 *reinterpret_cast<u32x2*>(keep_kq(m)) = kraw;
             else
