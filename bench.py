@@ -8,7 +8,8 @@ roofline of the dominant kernel (HIP events recorded by the library around
 every launch in a second timed region of K steps), and the fp64 CPU oracle
 timed on a bounded sample of the same workload; also the per-step GPU time of
 gdn_frame_step at the streaming workload's shape and the backward pass
-(gdn_frame_scan_bwd) on the same workload.
+(gdn_frame_scan_bwd) and of the block-scaled FP8 input mode
+(gdn_frame_scan_fwd_fp8) on the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload full_minute]
 """
@@ -305,6 +306,65 @@ def backward(w, q, k, v, beta, alpha, S0, steps: int, warmup: int, flush_buf):
                       "per-launch events)" % steps}
 
 
+def fp8_inputs(w, q, k, v, beta, alpha, S0, steps: int, warmup: int, flush_buf, bf16_ms: float):
+    """gdn_frame_scan_fwd_fp8 on the workload with q, k and v encoded as MXFP8
+    on the device (E4M3 values, one E8M0 scale per 32 features); o in bf16.
+    Algorithmic bytes: q, k, v at one byte per value plus their scales, beta,
+    alpha and S0 read once, o (bf16) and S_final written once."""
+    import torch
+    from gated_deltanet_scan_amd import api, inputs
+    enc = [inputs.to_mxfp8_device(x) for x in (q, k, v)]
+    o = torch.empty((w.B, w.F, w.N, w.H, w.Dv), dtype=torch.bfloat16, device="cuda")
+    S_final = torch.empty((w.B, w.H, w.Dv, w.Dk), dtype=torch.float32, device="cuda")
+    desc = api.make_desc(w.B, w.H, w.F, w.N, w.Dk, torch.float8_e4m3fn)
+    ws = api.alloc_workspace(desc, q.device)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        api.frame_scan_fwd_fp8(enc[0][0], enc[0][1], enc[1][0], enc[1][1], enc[2][0], enc[2][1], beta, alpha, S0,
+                               o=o, S_final=S_final, workspace=ws, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+
+    def timed(profiled):
+        if profiled:
+            api.profile_begin()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps if flush_buf is not None else 1)]
+        torch.cuda.synchronize()
+        if flush_buf is not None:
+            for e0, e1 in ev:
+                flush_buf.fill_(1.0)
+                e0.record(stream)
+                step()
+                e1.record(stream)
+        else:
+            ev[0][0].record(stream)
+            for _ in range(steps):
+                step()
+            ev[0][1].record(stream)
+        torch.cuda.synchronize()
+        kern = api.profile_end() if profiled else None
+        return sum(e0.elapsed_time(e1) for e0, e1 in ev), kern
+
+    gpu_ms, _ = timed(False)
+    _, kern = timed(True)
+    ms = gpu_ms / steps
+    tok = w.B * w.F * w.N * w.H
+    state = w.B * w.H * w.Dv * w.Dk * 4
+    nbytes = 3 * tok * w.Dk + 3 * tok * (w.Dk // 32) + tok * w.Dv * 2 + tok * 4 + w.B * w.F * w.H * 4 + 2 * state
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    kernels = {name: {"avg_ms": round(t / n, 5), "launches_per_step": n / steps}
+               for name, (t, n) in kern.items() if n > 0}
+    return {"workload": "the same workload, q/k/v as MXFP8 (E4M3, E8M0 scale per 32 features), o bf16",
+            "ms_per_step": round(ms, 5), "tokens_per_s": round(w.B * w.F * w.N / (ms * 1e-3), 1),
+            "speedup_vs_bf16": round(bf16_ms / ms, 3), "alg_bytes_per_step": nbytes,
+            "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "kernels": kernels,
+            "steps": steps, "warmup": warmup}
+
+
 def copy_calibration(nbytes: int, steps: int):
     """A plain device copy of known size, for scaling rocprofv3 byte counters."""
     import torch
@@ -329,6 +389,8 @@ def main():
                     help="frames of the streaming-step measurement (0: skip)")
     ap.add_argument("--bwd-steps", type=int, default=20,
                     help="timed calls of the backward pass (0: skip)")
+    ap.add_argument("--fp8-steps", type=int, default=20,
+                    help="timed calls of the block-scaled FP8 input mode (0: skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES bytes --steps times")
     ap.add_argument("--flush", choices=["auto", "on", "off"], default="auto",
@@ -355,7 +417,6 @@ def main():
     torch.cuda.set_device(0)
     w = inputs.make_config(args.workload, seed=args.seed)
     q, k, v, beta, alpha, S0 = inputs.to_torch(w, "cuda")
-    peaks = measured_peaks()      # right before the warm-up: the clocks come up here
     o = torch.empty_like(q)
     S_final = torch.empty((w.B, w.H, w.Dv, w.Dk), dtype=torch.float32, device="cuda")
     desc = api.make_desc(w.B, w.H, w.F, w.N, w.Dk, q.dtype)
@@ -434,6 +495,9 @@ def main():
                 "scope": "the dominant kernel alone, on the bytes it must move; the whole "
                          "scan against the same peak is path_roofline"}
     path_gbs = total_bytes / (ms_per_step * 1e-3) / 1e9
+    # measured after the timed regions: the 8192^3 products draw enough power
+    # to slow the scan timed right after them
+    peaks = measured_peaks()
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
@@ -464,6 +528,9 @@ def main():
     }
     line["backward"] = (backward(w, q, k, v, beta, alpha, S0, args.bwd_steps, min(args.warmup, 5), junk)
                         if args.bwd_steps > 0 else None)
+    line["fp8_inputs"] = (fp8_inputs(w, q, k, v, beta, alpha, S0, args.fp8_steps, min(args.warmup, 5), junk,
+                                     ms_per_step)
+                          if args.fp8_steps > 0 and w.Dk % 32 == 0 and w.dtype == "bf16" else None)
     line["streaming_step"] = streaming_step(args.stream_frames) if args.stream_frames > 0 else None
     if args.cpu_budget > 0:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)

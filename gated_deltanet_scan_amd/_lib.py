@@ -14,6 +14,7 @@ LIB_PATH = os.path.join(_PKG, "libgdn.so")
 
 GDN_BF16 = 0
 GDN_F32 = 1
+GDN_FP8_E4M3 = 2
 GDN_FLAG_GATES_ARE_LOGITS = 0x1
 GDN_FLAG_NO_KEY_NORM = 0x2
 GDN_FLAG_REVERSE = 0x4
@@ -68,6 +69,8 @@ def load():
     lib.gdn_workspace_size_bwd.restype = sz
     lib.gdn_frame_scan_bwd.argtypes = [dp, vp, vp, vp, fp, fp, fp, vp, fp, vp, vp, vp, fp, fp, fp, vp, sz, vp]
     lib.gdn_frame_scan_bwd.restype = ctypes.c_int
+    lib.gdn_frame_scan_fwd_fp8.argtypes = [dp, vp, vp, vp, vp, vp, vp, fp, fp, fp, vp, fp, vp, sz, vp]
+    lib.gdn_frame_scan_fwd_fp8.restype = ctypes.c_int
     lib.gdn_frame_scan_fwd_static.argtypes = [dp, vp, vp, vp, fp, fp, fp, vp, fp, vp]
     lib.gdn_frame_scan_fwd_static.restype = ctypes.c_int
     lib.gdn_static_scratch_bytes.argtypes = []

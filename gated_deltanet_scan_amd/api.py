@@ -38,8 +38,10 @@ def make_desc(B, H, F, N, D, dtype: torch.dtype, *, gates_are_logits=False, eps=
         io = _lib.GDN_BF16
     elif dtype == torch.float32:
         io = _lib.GDN_F32
+    elif dtype == torch.float8_e4m3fn:
+        io = _lib.GDN_FP8_E4M3
     else:
-        raise TypeError("q/k/v must be bfloat16 or float32")
+        raise TypeError("q/k/v must be bfloat16, float32 or float8_e4m3fn")
     flags = _lib.GDN_FLAG_GATES_ARE_LOGITS if gates_are_logits else 0
     if not normalize_keys:
         flags |= _lib.GDN_FLAG_NO_KEY_NORM
@@ -154,6 +156,52 @@ def frame_scan_fwd_static(q, k, v, beta, alpha, S0=None, *, gates_are_logits: bo
             _ptr(o), _ptr(S_final), ctypes.c_void_p(stream.cuda_stream))
     if st != 0:
         raise GdnError(st, "gdn_frame_scan_fwd_static")
+    return o, S_final
+
+
+def frame_scan_fwd_fp8(q, q_scale, k, k_scale, v, v_scale, beta, alpha, S0=None, *,
+                       gates_are_logits: bool = False, eps: float = 1e-6, normalize_keys: bool = True,
+                       reverse: bool = False, o=None, S_final=None, workspace=None,
+                       return_state: bool = True, stream=None):
+    """frame_scan_fwd on block-scaled FP8 inputs (OCP MXFP8, E4M3 elements).
+
+    q, k, v: [B,F,N,H,D] torch.float8_e4m3fn; q_scale, k_scale, v_scale:
+    [B,F,N,H,D/32] torch.uint8 E8M0 exponents (value = e4m3 * 2^(s - 127));
+    D in {32, 64, 128}.  Returns (o [B,F,N,H,D] bfloat16, S_final fp32 or None).
+    """
+    B, F, N, H, D = q.shape
+    f8 = torch.float8_e4m3fn
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check(t, name, f8, (B, F, N, H, D))
+    nb = D // 32
+    for name, t in (("q_scale", q_scale), ("k_scale", k_scale), ("v_scale", v_scale)):
+        _check(t, name, torch.uint8, (B, F, N, H, nb))
+    _check(beta, "beta", torch.float32, (B, F, N, H))
+    _check(alpha, "alpha", torch.float32, (B, F, H))
+    if S0 is not None:
+        _check(S0, "S0", torch.float32, (B, H, D, D))
+    if o is not None:
+        _check(o, "o", torch.bfloat16, (B, F, N, H, D))
+    if S_final is not None:
+        _check(S_final, "S_final", torch.float32, (B, H, D, D))
+    _check_workspace(workspace, q.device)
+    desc = make_desc(B, H, F, N, D, f8, gates_are_logits=gates_are_logits, eps=eps,
+                     normalize_keys=normalize_keys, reverse=reverse)
+    stream = _launch_stream(stream, q.device)
+    with torch.cuda.stream(stream):   # allocations belong to the launch stream
+        if o is None:
+            o = torch.empty((B, F, N, H, D), dtype=torch.bfloat16, device=q.device)
+        if S_final is None and return_state:
+            S_final = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
+        if workspace is None:
+            workspace = alloc_workspace(desc, q.device)
+        ws_bytes = 0 if workspace is None else workspace.numel()
+        st = _lib.load().gdn_frame_scan_fwd_fp8(
+            ctypes.byref(desc), _ptr(q), _ptr(q_scale), _ptr(k), _ptr(k_scale), _ptr(v), _ptr(v_scale),
+            _ptr(beta), _ptr(alpha), _ptr(S0), _ptr(o), _ptr(S_final), _ptr(workspace),
+            ctypes.c_size_t(ws_bytes), ctypes.c_void_p(stream.cuda_stream))
+    if st != 0:
+        raise GdnError(st, "gdn_frame_scan_fwd_fp8")
     return o, S_final
 
 

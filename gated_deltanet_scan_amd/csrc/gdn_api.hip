@@ -133,26 +133,27 @@ bool dim_ok(int D) { return D == 16 || D == 32 || D == 64 || D == 128; }
 gdn_status check_desc(const gdn_desc* d, bool step, Plan* p, int fc_cap = gdn::kMaxChunkFrames) {
     if (!d) return GDN_ERR_INVALID_ARG;
     if (d->B < 0 || d->H < 0 || d->F < 0 || d->N < 0) return GDN_ERR_INVALID_ARG;
-    if (d->io_dtype != GDN_BF16 && d->io_dtype != GDN_F32) return GDN_ERR_INVALID_ARG;
+    if (d->io_dtype != GDN_BF16 && d->io_dtype != GDN_F32 && d->io_dtype != GDN_FP8_E4M3) return GDN_ERR_INVALID_ARG;
     if ((d->flags & ~(GDN_FLAG_GATES_ARE_LOGITS | GDN_FLAG_NO_KEY_NORM | GDN_FLAG_REVERSE)) != 0)
         return GDN_ERR_INVALID_ARG;
     if (!(d->eps > 0.0f) || !isfinite(d->eps)) return GDN_ERR_INVALID_ARG;
     if (step && d->F != 1) return GDN_ERR_INVALID_ARG;
     if (d->Dk < 1 || d->Dv < 1) return GDN_ERR_INVALID_ARG;
     if (d->Dk != d->Dv || !dim_ok(d->Dk)) return GDN_ERR_UNSUPPORTED;
+    if (d->io_dtype == GDN_FP8_E4M3 && d->Dk < gdn::kMxBlock) return GDN_ERR_UNSUPPORTED;   // one scale block
     // element counts must fit comfortably in 64-bit byte offsets, and one
     // frame of one tensor in the 32-bit offsets of a buffer resource
     const double tok = (double)d->B * d->F * d->N * d->H * d->Dk;
     if (tok > 1e15) return GDN_ERR_INVALID_ARG;
-    const double esz = d->io_dtype == GDN_BF16 ? 2.0 : 4.0;
+    const double esz = d->io_dtype == GDN_F32 ? 4.0 : 2.0;
     if (((double)d->N + 1024.0) * d->H * d->Dk * esz >= 2147483648.0) return GDN_ERR_UNSUPPORTED;
     p->D = d->Dk;
-    p->esz = d->io_dtype == GDN_BF16 ? 2 : 4;
+    p->esz = d->io_dtype == GDN_F32 ? 4 : 2;    // the block-scaled mode computes in bf16
     p->units = (int64_t)d->B * d->H;
     // frames per launch chunk (state_scan stages the chunk's gates in LDS)
     p->Fc = d->F < fc_cap ? d->F : fc_cap;
     p->item_bytes = gdn::ws_item_bytes(p->esz, p->D);
-    if (d->F == 1) {
+    if (d->F == 1 && d->io_dtype != GDN_FP8_E4M3) {   // (block-scaled inputs take the scan path)
         int tpart = 0;
         step_ranges(p->units, d->N, gram_stage_tokens(p->esz, p->D), kSizingCUs, &p->parts_max, &tpart);
         p->scopy_off = ((size_t)p->units * p->parts_max * gdn::part_bytes(p->D) + 255) / 256 * 256;
@@ -239,7 +240,7 @@ gdn_status launch_all(const Plan& p, ScanArgs a, hipStream_t stream, int cus, fl
         if (hipGetLastError() != hipSuccess) return GDN_ERR_LAUNCH;
         ScanArgs s = a;
         s.S_out = carry;
-        if ((st = launch_state<T, D>(s, stream)) != GDN_OK) return st;
+        if ((st = launch_state<typename gdn::Elem<T>::C, D>(s, stream)) != GDN_OK) return st;
         a.S_in = carry;
         if ((st = launch_output<T, D>(a, stream, cus)) != GDN_OK) return st;
     }
@@ -384,6 +385,7 @@ gdn_status run(const gdn_desc* d, bool step, const void* q, const void* k, const
     }
     gdn_status st = check_desc(d, step, &p, fc_cap);
     if (st != GDN_OK) return st;
+    if (d->io_dtype == GDN_FP8_E4M3) return GDN_ERR_INVALID_ARG;   // needs the scales: gdn_frame_scan_fwd_fp8
     if (static_ws) {
         if (p.ws_bytes > kScratchBytes) return GDN_ERR_WORKSPACE;
         workspace = nullptr;
@@ -481,6 +483,95 @@ gdn_status run(const gdn_desc* d, bool step, const void* q, const void* k, const
                                    : dispatch_d<float>(p, a, stream, cus, carry);
 }
 
+// ---------------------------------------------------------------- block-scaled inputs
+template <int D>
+gdn_status launch_fp8(const Plan& p, const ScanArgs& a, hipStream_t s, int cus, float* carry) {
+    return launch_all<gdn::fp8e4m3, D>(p, a, s, cus, carry);
+}
+
+gdn_status run_fp8(const gdn_desc* d, const void* q, const uint8_t* qs, const void* k, const uint8_t* ks,
+                   const void* v, const uint8_t* vs, const float* beta, const float* alpha, const float* S0, void* o,
+                   float* S_final, void* workspace, size_t workspace_bytes, void* stream_v) {
+    Plan p;
+    gdn_status st = check_desc(d, false, &p);
+    if (st != GDN_OK) return st;
+    if (d->io_dtype != GDN_FP8_E4M3) return GDN_ERR_INVALID_ARG;
+    const size_t ntok = (size_t)d->B * d->F * d->N * d->H;
+    const size_t in_bytes = ntok * (size_t)p.D;                       // one byte per value
+    const size_t sc_bytes = ntok * (size_t)(p.D / gdn::kMxBlock);     // one E8M0 byte per 32 values
+    const size_t o_bytes = ntok * (size_t)p.D * 2;                    // bf16
+    const size_t beta_bytes = ntok * sizeof(float);
+    const size_t alpha_bytes = (size_t)d->B * d->F * d->H * sizeof(float);
+    const size_t state_bytes = (size_t)p.units * p.D * p.D * sizeof(float);
+    if (ntok > 0 && (!q || !qs || !k || !ks || !v || !vs || !beta || !o)) return GDN_ERR_INVALID_ARG;
+    if (alpha_bytes > 0 && !alpha) return GDN_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return GDN_ERR_ALIGNMENT;
+    if (!aligned(beta, 4) || !aligned(alpha, 4)) return GDN_ERR_ALIGNMENT;
+    if (!aligned(S0, 16) || !aligned(S_final, 16)) return GDN_ERR_ALIGNMENT;
+    if (p.ws_bytes > 0) {
+        if (!workspace || workspace_bytes < p.ws_bytes) return GDN_ERR_WORKSPACE;
+        if (!aligned(workspace, 256)) return GDN_ERR_ALIGNMENT;
+    }
+    auto R = [](const void* ptr, size_t n) { return rng(ptr, ptr ? n : 0); };
+    const Range ins[] = {R(q, in_bytes), R(qs, sc_bytes), R(k, in_bytes), R(ks, sc_bytes), R(v, in_bytes),
+                         R(vs, sc_bytes), R(beta, beta_bytes), R(alpha, alpha_bytes), R(S0, state_bytes)};
+    const Range ro = R(o, o_bytes), rsf = R(S_final, state_bytes), rw = R(workspace, workspace ? p.ws_bytes : 0);
+    for (const Range& x : ins) {
+        if (overlap(ro, x) || overlap(rw, x)) return GDN_ERR_ALIAS;
+        if (overlap(rsf, x) && !(x.lo == rsf.lo && S_final == S0)) return GDN_ERR_ALIAS;
+    }
+    if (overlap(rsf, R(S0, state_bytes)) && S_final != S0) return GDN_ERR_ALIAS;
+    if (overlap(ro, rsf) || overlap(ro, rw) || overlap(rsf, rw)) return GDN_ERR_ALIAS;
+
+    if (p.units == 0) return GDN_OK;
+    if (d->F == 0 && !S_final) return GDN_OK;
+    int cus = 0;
+    st = check_device(&cus);
+    if (st != GDN_OK) return st;
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_v);
+    if (d->F == 0) {
+        if (S_final == S0) return GDN_OK;
+        const size_t n = (size_t)p.units * p.D * p.D;
+        ProfScope ps(K_COPY, stream);
+        hipLaunchKernelGGL(gdn::state_copy_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, S0,
+                           S_final, n);
+        return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+    }
+    ScanArgs a;
+    memset(&a, 0, sizeof(a));
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.qs = qs;
+    a.ks = ks;
+    a.vs = vs;
+    a.beta = beta;
+    a.alpha = alpha;
+    a.S_in = S0;
+    a.o = o;
+    a.S_out = S_final;
+    a.ws = static_cast<unsigned char*>(workspace);
+    a.B = d->B;
+    a.H = d->H;
+    a.F = d->F;
+    a.N = d->N;
+    a.logits = (d->flags & GDN_FLAG_GATES_ARE_LOGITS) ? 1 : 0;
+    a.raw_keys = (d->flags & GDN_FLAG_NO_KEY_NORM) ? 1 : 0;
+    a.reverse = (d->flags & GDN_FLAG_REVERSE) ? 1 : 0;
+    a.eps = d->eps;
+    a.tsplit = 1;
+    a.tchunk = 16;
+    a.parts = 1;
+    a.tpart = d->N;
+    float* carry = S_final ? S_final : reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + p.carry_off);
+    switch (p.D) {
+        case 32: return launch_fp8<32>(p, a, stream, cus, carry);
+        case 64: return launch_fp8<64>(p, a, stream, cus, carry);
+        case 128: return launch_fp8<128>(p, a, stream, cus, carry);
+        default: return GDN_ERR_UNSUPPORTED;
+    }
+}
+
 // ---------------------------------------------------------------- backward pass
 // Workspace of gdn_frame_scan_bwd: per chunk of up to Fc frames the forward
 // items (Gm, U, S planes) and the backward items (W, X planes); the states
@@ -498,6 +589,7 @@ gdn_status check_bwd(const gdn_desc* d, BwdPlan* bp) {
     Plan& p = bp->p;
     gdn_status st = check_desc(d, false, &p);
     if (st != GDN_OK) return st;
+    if (d->io_dtype == GDN_FP8_E4M3) return GDN_ERR_UNSUPPORTED;
     bp->nchunks = d->F > 0 ? (d->F + p.Fc - 1) / p.Fc : 0;
     const size_t set = round256((size_t)p.units * p.Fc * p.item_bytes);
     bp->state_bytes = round256((size_t)p.units * p.D * p.D * sizeof(float));
@@ -726,6 +818,14 @@ gdn_status gdn_frame_scan_fwd_static(const gdn_desc* d, const void* q, const voi
 }
 
 size_t gdn_static_scratch_bytes(void) { return kScratchBytes; }
+
+gdn_status gdn_frame_scan_fwd_fp8(const gdn_desc* d, const void* q, const uint8_t* q_scale, const void* k,
+                                  const uint8_t* k_scale, const void* v, const uint8_t* v_scale, const float* beta,
+                                  const float* alpha, const float* S0, void* o, float* S_final, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+    return run_fp8(d, q, q_scale, k, k_scale, v, v_scale, beta, alpha, S0, o, S_final, workspace, workspace_bytes,
+                   stream);
+}
 
 gdn_status gdn_frame_step(const gdn_desc* d, const void* q, const void* k, const void* v,
                           const float* beta, const float* alpha, const float* S_in, void* o,

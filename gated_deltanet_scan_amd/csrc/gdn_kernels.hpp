@@ -152,6 +152,32 @@ __device__ __forceinline__ void bstore16(rsrc_t r, uint32_t off, u32x4 v) {
 
 // ---------------------------------------------------------------- I/O type traits
 // Storage type of q/k/v/o: uint16_t holds bfloat16 bits; float is the fp32 mode.
+// fp8e4m3 is the block-scaled input mode: q, k and v hold OCP FP8 E4M3 bytes,
+// each run of 32 consecutive features of a token row shares an E8M0 scale
+// 2^(e - 127) (the OCP microscaling "MXFP8" layout), and the kernels turn
+// them into bf16 on load (exact: an E4M3 value times a power of two fits
+// bf16), so everything after the load, the output included, is the bf16 mode.
+struct fp8e4m3 {
+    uint8_t bits;
+};
+template <typename T> struct Elem {
+    using C = T;                                       // compute (and output) type
+    static constexpr int GB = sizeof(T);               // bytes per input element in HBM
+};
+template <> struct Elem<fp8e4m3> {
+    using C = uint16_t;
+    static constexpr int GB = 1;
+};
+constexpr int kMxBlock = 32;                           // features per E8M0 scale
+// Eight E4M3 values (two dwords) times 2^(e - 127), as eight bf16 values.
+__device__ __forceinline__ u32x4 mx_to_bf16(u32x2 raw, uint32_t e) {
+    const float sc = __builtin_amdgcn_ldexpf(1.0f, (int)e - 127);
+    return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[0], sc, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[0], sc, true)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[1], sc, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[1], sc, true))};
+}
+
 template <typename T> struct IO;
 
 template <> struct IO<uint16_t> {
@@ -283,6 +309,10 @@ struct ScanArgs {
     // Backward pass: the recomputing frame_gram also writes every token's key
     // scale rho = 1 / max(|k|, eps) here, fp32 [B][F][N][H].
     float* rho;
+    // Block-scaled inputs: the E8M0 scales of q, k and v, [B][F][N][H][D/32].
+    const uint8_t* qs;
+    const uint8_t* ks;
+    const uint8_t* vs;
 };
 
 // Partial G and U of one token range (one-frame path), both fp32: G in the
@@ -375,6 +405,12 @@ template <> struct Quad<uint16_t> {
         return (e & 1) ? (x[e >> 1] >> 16) : (x[e >> 1] & 0xffffu);
     }
 };
+template <> struct Quad<fp8e4m3> {                     // the same eight features as one byte each
+    using type = u32x2;
+    __device__ static __forceinline__ type load(rsrc_t r, uint32_t off) {
+        return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kNonTemporal);
+    }
+};
 template <> struct Quad<float> {
     using type = u32x4;
     __device__ static __forceinline__ type load(rsrc_t r, uint32_t off) { return bload16_nt(r, off); }
@@ -414,13 +450,19 @@ __device__ __forceinline__ float lane_group_sum(float x) {
 // backward pass's use of the same product with unit betas and keys as given:
 // with k := Q and v := dO its U is W_f = dO_f^T Q_f, and only the U tiles run.
 // RHO (the backward pass's recomputation) also writes each token's key scale
-// to a.rho.
-template <typename T, int D, bool PART, bool WPASS = false, bool RHO = false>
+// to a.rho.  TIN is the input element type (fp8e4m3: block-scaled bytes,
+// turned into bf16 as each stage is written to LDS; everything else is the
+// bf16 mode).
+template <typename TIN, int D, bool PART, bool WPASS = false, bool RHO = false>
 __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
+    using T = typename Elem<TIN>::C;
+    constexpr bool MX = !__is_same(T, TIN);
+    constexpr int GB = Elem<TIN>::GB;               // input bytes per element
     using C = GramCfg<T, D>;
     using io = IO<T>;
     using frag = typename io::frag;
-    using Q = Quad<T>;
+    using Q = Quad<T>;                              // the stage's values (bf16 bits or fp32)
+    using QL = Quad<TIN>;                           // what the loads return
     __shared__ __attribute__((aligned(16))) unsigned char smem[C::LDS];
 
     const int N = a.N, H = a.H;
@@ -466,8 +508,13 @@ __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
     const int s = ptid % C::SL;                     // features s*FPT .. s*FPT+3
     const int tl = ptid / C::SL;                    // tokens tl*TPT .. tl*TPT+TPT-1
     const size_t rowstride = (size_t)H * D;         // elements between tokens
-    const uint32_t row_bytes = (uint32_t)(H * D * C::SZ);
-    const uint32_t kv_off0 = (uint32_t)(tl * C::TPT) * row_bytes + (uint32_t)(s * C::FPT * C::SZ);
+    const uint32_t row_bytes = (uint32_t)(H * D * GB);
+    const uint32_t kv_off0 = (uint32_t)(tl * C::TPT) * row_bytes + (uint32_t)(s * C::FPT * GB);
+    // block-scaled inputs: each token row has D/32 scale bytes; this thread's
+    // eight features lie in block s*FPT/32
+    constexpr int NB = D / kMxBlock;
+    const uint32_t srow = (uint32_t)(H * NB);
+    const uint32_t sc_off0 = (uint32_t)(tl * C::TPT) * srow + (uint32_t)(s * C::FPT / kMxBlock);
     // betas of this thread's tokens (the lanes of a token load the same value:
     // an exchange through ds_bpermute instead waited on LDS latency)
     const uint32_t b_off0 = (uint32_t)(tl * C::TPT * H * 4);
@@ -482,8 +529,9 @@ __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
     }
 
     struct Stage {
-        typename Q::type k[C::TPT], v[C::TPT];
+        typename QL::type k[C::TPT], v[C::TPT];
         float bt[C::TPT];
+        uint32_t ks[C::TPT], vs[C::TPT];            // E8M0 scales (block-scaled inputs)
     };
     // The producers' load stream walks this workgroup's stages in order, one
     // per call; the item's buffer resources are rebuilt only when an item
@@ -491,18 +539,24 @@ __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
     // the end stay on the last item past its last token: the buffer range
     // check returns zeros for them.
     struct Loader {
-        rsrc_t rk, rv, rb;
-        uint32_t kvo, bo;                           // offsets of the next stage
+        rsrc_t rk, rv, rb, rks, rvs;
+        uint32_t kvo, bo, so;                       // offsets of the next stage
         int kk, st;                                 // its item and stage within the item
     };
     auto loader_item = [&](Loader& L, int kk) {
         const Item it = item_of(kk);
         const size_t tok0 = ((size_t)it.b * a.F + it.f) * (size_t)N + (size_t)it.p * tpart;
         const int nt = range_tokens(it);
-        const uint32_t kv_bytes = nt > 0 ? (uint32_t)(((size_t)(nt - 1) * H * D + D) * C::SZ) : 0u;
+        const uint32_t kv_bytes = nt > 0 ? (uint32_t)(((size_t)(nt - 1) * H * D + D) * GB) : 0u;
         const uint32_t beta_bytes = nt > 0 ? (uint32_t)(((nt - 1) * H + 1) * 4) : 0u;
-        L.rk = make_rsrc(static_cast<const T*>(a.k) + tok0 * rowstride + (size_t)it.h * D, kv_bytes);
-        L.rv = make_rsrc(static_cast<const T*>(a.v) + tok0 * rowstride + (size_t)it.h * D, kv_bytes);
+        L.rk = make_rsrc(static_cast<const TIN*>(a.k) + tok0 * rowstride + (size_t)it.h * D, kv_bytes);
+        L.rv = make_rsrc(static_cast<const TIN*>(a.v) + tok0 * rowstride + (size_t)it.h * D, kv_bytes);
+        if constexpr (MX) {
+            const uint32_t sc_bytes = nt > 0 ? (uint32_t)((nt - 1) * H * NB + NB) : 0u;
+            L.rks = make_rsrc(a.ks + tok0 * H * NB + (size_t)it.h * NB, sc_bytes);
+            L.rvs = make_rsrc(a.vs + tok0 * H * NB + (size_t)it.h * NB, sc_bytes);
+            L.so = sc_off0;
+        }
         L.rb = make_rsrc(a.beta + tok0 * H + it.h, beta_bytes);
         L.kvo = kv_off0;
         L.bo = b_off0;
@@ -512,8 +566,16 @@ __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
     auto load_stage = [&](Loader& L, Stage& R) {
 #pragma unroll
         for (int j = 0; j < C::TPT; ++j) {
-            R.k[j] = Q::load(L.rk, L.kvo + (uint32_t)j * row_bytes);
-            R.v[j] = Q::load(L.rv, L.kvo + (uint32_t)j * row_bytes);
+            R.k[j] = QL::load(L.rk, L.kvo + (uint32_t)j * row_bytes);
+            R.v[j] = QL::load(L.rv, L.kvo + (uint32_t)j * row_bytes);
+        }
+        if constexpr (MX) {
+#pragma unroll
+            for (int j = 0; j < C::TPT; ++j) {
+                R.ks[j] = __builtin_amdgcn_raw_buffer_load_b8(L.rks, L.so + (uint32_t)j * srow, 0, 0);
+                R.vs[j] = __builtin_amdgcn_raw_buffer_load_b8(L.rvs, L.so + (uint32_t)j * srow, 0, 0);
+            }
+            L.so += (uint32_t)C::TS * srow;
         }
         if constexpr (!WPASS) {
 #pragma unroll
@@ -525,6 +587,18 @@ __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
     };
     // Norms, scales and the transposed LDS write of stage gs.
     auto write_stage = [&](int gs, const Stage& R, unsigned char* buf) {
+        // the stage's values (block-scaled inputs: converted to bf16 here)
+        typename Q::type Rk[C::TPT], Rv[C::TPT];
+#pragma unroll
+        for (int j = 0; j < C::TPT; ++j) {
+            if constexpr (MX) {
+                Rk[j] = mx_to_bf16(R.k[j], R.ks[j]);
+                Rv[j] = mx_to_bf16(R.v[j], R.vs[j]);
+            } else {
+                Rk[j] = R.k[j];
+                Rv[j] = R.v[j];
+            }
+        }
         // the tokens' sums of squares as independent chains (two per token),
         // then their lane reductions side by side, then the gates: a branch
         // inside the per-token loop kept the compiler from interleaving them
@@ -535,7 +609,7 @@ __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
             ssb[j] = 0.0f;
 #pragma unroll
             for (int e = 0; e < C::FPT; e += 2) {
-                const float k0 = Q::get(R.k[j], e), k1 = Q::get(R.k[j], e + 1);
+                const float k0 = Q::get(Rk[j], e), k1 = Q::get(Rk[j], e + 1);
                 ssa[j] = fmaf(k0, k0, ssa[j]);
                 ssb[j] = fmaf(k1, k1, ssb[j]);
             }
@@ -568,16 +642,16 @@ __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
         unsigned char* sXB = buf + 2 * C::ARR;      // beta rho k    (B of both)
 #pragma unroll
         for (int e = 0; e < C::FPT; ++e) {
-            const float k0 = Q::get(R.k[0], e), k1 = Q::get(R.k[1], e);
+            const float k0 = Q::get(Rk[0], e), k1 = Q::get(Rk[1], e);
             if constexpr (sizeof(T) == 2) {         // the two tokens' bf16 values in one dword
                 if constexpr (!WPASS)
                     *reinterpret_cast<uint32_t*>(sKH + woff[e]) = pack_bf16x2(rho[0] * k0, rho[1] * k1);
                 *reinterpret_cast<uint32_t*>(sXB + woff[e]) = pack_bf16x2(xs[0] * k0, xs[1] * k1);
-                *reinterpret_cast<uint32_t*>(sVT + woff[e]) = Q::bits(R.v[0], e) | (Q::bits(R.v[1], e) << 16);
+                *reinterpret_cast<uint32_t*>(sVT + woff[e]) = Q::bits(Rv[0], e) | (Q::bits(Rv[1], e) << 16);
             } else {
                 if constexpr (!WPASS) *reinterpret_cast<f32x2*>(sKH + woff[e]) = f32x2{rho[0] * k0, rho[1] * k1};
                 *reinterpret_cast<f32x2*>(sXB + woff[e]) = f32x2{xs[0] * k0, xs[1] * k1};
-                *reinterpret_cast<f32x2*>(sVT + woff[e]) = f32x2{Q::get(R.v[0], e), Q::get(R.v[1], e)};
+                *reinterpret_cast<f32x2*>(sVT + woff[e]) = f32x2{Q::get(Rv[0], e), Q::get(Rv[1], e)};
             }
         }
     };
@@ -1210,8 +1284,13 @@ template <typename T, int D> struct OutCfg {
 // fragments (a token row of Q is 8 contiguous features per lane).
 // TRS is the backward pass's dq_i = S_f^T do_i: the same kernel with q := dO,
 // o := dQ and the transposed state, staged through LDS before the pipeline.
-template <typename T, int D, bool TRS = false>
+// TIN is q's element type (fp8e4m3: block-scaled bytes, turned into bf16 as
+// each block is written to LDS; o is then bf16).
+template <typename TIN, int D, bool TRS = false>
 __global__ __launch_bounds__(256, 2) void frame_output_kernel(ScanArgs a) {
+    using T = typename Elem<TIN>::C;
+    constexpr bool MX = !__is_same(T, TIN);
+    constexpr int GB = Elem<TIN>::GB;
     using C = OutCfg<T, D>;
     using io = IO<T>;
     using frag = typename io::frag;
@@ -1257,26 +1336,48 @@ __global__ __launch_bounds__(256, 2) void frame_output_kernel(ScanArgs a) {
     const size_t rowstride = (size_t)H * D;
     const size_t tok0 = ((size_t)b * a.F + f) * (size_t)N + nbeg;
     const uint32_t rbytes = (uint32_t)(((size_t)(nend - nbeg - 1) * rowstride + D) * C::SZ);
-    const rsrc_t rq = make_rsrc(static_cast<const T*>(a.q) + tok0 * rowstride + (size_t)h * D, rbytes);
+    const uint32_t qbytes = (uint32_t)(((size_t)(nend - nbeg - 1) * rowstride + D) * GB);
+    const rsrc_t rq = make_rsrc(static_cast<const TIN*>(a.q) + tok0 * rowstride + (size_t)h * D, qbytes);
     const rsrc_t ro = make_rsrc(static_cast<T*>(a.o) + tok0 * rowstride + (size_t)h * D, rbytes);
-    const uint32_t row_bytes = (uint32_t)(H * D * C::SZ);
+    const uint32_t row_bytes = (uint32_t)(H * D * C::SZ);     // o (and q unless block-scaled)
+    const uint32_t qrow_bytes = (uint32_t)(H * D * GB);
     const int nloc = nend - nbeg;
     const int nblk = (nloc + C::BT - 1) / C::BT;
+    // block-scaled q: D/32 scale bytes per token row
+    constexpr int NB = D / kMxBlock;
+    rsrc_t rqs;
+    if constexpr (MX)
+        rqs = make_rsrc(a.qs + tok0 * H * NB + (size_t)h * NB, (uint32_t)((nend - nbeg - 1) * H * NB + NB));
 
-    // loader role: row lr of each pass, 16-byte column lc
+    // loader role: row lr of each pass, 16-byte column lc (of the bf16 row:
+    // eight features; block-scaled q loads their eight bytes and their scale)
     const int lc = tid % C::LPR, lr = tid / C::LPR;
     struct QStage {
-        u32x4 v[C::NLD];
+        typename Quad<TIN>::type v[C::NLD];
+        uint32_t e[MX ? C::NLD : 1];
     };
     auto load_blk = [&](int blk, QStage& R) {
-        const uint32_t base = (uint32_t)(blk * C::BT + lr) * row_bytes + (uint32_t)(lc * 16);
+        constexpr int FPC = 16 / C::SZ;             // features per 16-byte chunk of the LDS row
+        const uint32_t base = (uint32_t)(blk * C::BT + lr) * qrow_bytes + (uint32_t)(lc * FPC * GB);
 #pragma unroll
-        for (int i = 0; i < C::NLD; ++i) R.v[i] = bload16_nt(rq, base + (uint32_t)(i * C::RPP) * row_bytes);
+        for (int i = 0; i < C::NLD; ++i) R.v[i] = Quad<TIN>::load(rq, base + (uint32_t)(i * C::RPP) * qrow_bytes);
+        if constexpr (MX) {
+            const uint32_t sb = (uint32_t)(blk * C::BT + lr) * (uint32_t)(H * NB) + (uint32_t)(lc * FPC / kMxBlock);
+#pragma unroll
+            for (int i = 0; i < C::NLD; ++i)
+                R.e[i] = __builtin_amdgcn_raw_buffer_load_b8(rqs, sb + (uint32_t)(i * C::RPP * H * NB), 0, 0);
+        }
     };
     auto put_blk = [&](const QStage& R, unsigned char* buf) {
 #pragma unroll
-        for (int i = 0; i < C::NLD; ++i)
-            *reinterpret_cast<u32x4*>(buf + (lr + i * C::RPP) * C::ROWB + lc * 16) = R.v[i];
+        for (int i = 0; i < C::NLD; ++i) {
+            u32x4 val;
+            if constexpr (MX)
+                val = mx_to_bf16(R.v[i], R.e[i]);
+            else
+                val = R.v[i];
+            *reinterpret_cast<u32x4*>(buf + (lr + i * C::RPP) * C::ROWB + lc * 16) = val;
+        }
     };
 
     // ---- S_f rows of this wave as A fragments (fragment-major workspace)

@@ -130,6 +130,53 @@ def make_grads(w: Workload, seed: int = 0, *, ds_std: float = 1.0):
     return dO, (dS.astype(np.float32) if ds_std > 0.0 else None)
 
 
+def to_mxfp8(x: np.ndarray):
+    """Encode x ([..., D], D a multiple of 32) in the OCP microscaling MXFP8
+    layout: per block of 32 consecutive values of the last axis one E8M0 scale
+    2^e with e = floor(log2(max |x|)) - 8 (8 is the largest exponent of an
+    E4M3 value; all-zero blocks take e = 0), and per value the E4M3 code of
+    x / 2^e rounded to nearest even, clamped to +-448.  Returns (codes uint8
+    [..., D], scale bytes e + 127 uint8 [..., D/32], the dequantised values
+    code * 2^e as float32)."""
+    import torch
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    lead, D = x.shape[:-1], x.shape[-1]
+    if D % 32:
+        raise ValueError("the last axis must be a multiple of 32")
+    blk = x.reshape(lead + (D // 32, 32)).astype(np.float64)
+    amax = np.abs(blk).max(axis=-1)
+    e = np.floor(np.log2(np.where(amax > 0, amax, 256.0))) - 8
+    e = np.clip(e, -127, 127)
+    scaled = np.clip(blk / np.exp2(e)[..., None], -448.0, 448.0).astype(np.float32)
+    codes = torch.from_numpy(scaled).to(torch.float8_e4m3fn)
+    deq = codes.to(torch.float64).numpy() * np.exp2(e)[..., None]
+    return (codes.view(torch.uint8).numpy().reshape(x.shape), (e + 127).astype(np.uint8),
+            deq.reshape(x.shape).astype(np.float32))
+
+
+def to_mxfp8_device(x):
+    """to_mxfp8 on a device tensor (the same recipe, in torch): returns (codes
+    torch.float8_e4m3fn, scale bytes torch.uint8) on x's device."""
+    import torch
+    lead, D = x.shape[:-1], x.shape[-1]
+    blk = x.float().reshape(*lead, D // 32, 32)
+    amax = blk.abs().amax(dim=-1)
+    e = torch.floor(torch.log2(torch.where(amax > 0, amax, torch.full_like(amax, 256.0)))) - 8
+    e = e.clamp(-127, 127)
+    scaled = (blk / torch.exp2(e).unsqueeze(-1)).clamp(-448.0, 448.0)
+    return scaled.to(torch.float8_e4m3fn).reshape(x.shape), (e + 127).to(torch.uint8)
+
+
+def make_fp8(w: Workload):
+    """MXFP8 encodings of a workload's q, k and v, and a copy of the workload
+    holding their dequantised values (what the scan computes on).  Returns
+    (((q codes, q scales), (k ...), (v ...)), dequantised workload)."""
+    from dataclasses import replace
+    enc = [to_mxfp8(x) for x in (w.q, w.k, w.v)]
+    deq = replace(w, q=enc[0][2], k=enc[1][2], v=enc[2][2], dtype="bf16")
+    return tuple((c, s) for c, s, _ in enc), deq
+
+
 def make_config(name: str, seed: int = 0, **overrides) -> Workload:
     """Draw one of the named workloads in CONFIGS (fields may be overridden)."""
     c = dict(CONFIGS[name])

@@ -66,7 +66,7 @@ typedef enum gdn_status {
     GDN_ERR_NO_DEVICE = 7     /* no current HIP device could be queried            */
 } gdn_status;
 
-typedef enum gdn_dtype { GDN_BF16 = 0, GDN_F32 = 1 } gdn_dtype;
+typedef enum gdn_dtype { GDN_BF16 = 0, GDN_F32 = 1, GDN_FP8_E4M3 = 2 } gdn_dtype;
 
 /* beta and alpha hold logits; the library applies sigmoid(.)/N and sigmoid(.). */
 #define GDN_FLAG_GATES_ARE_LOGITS 0x1u
@@ -162,6 +162,35 @@ gdn_status gdn_frame_scan_fwd_static(const gdn_desc* d,
 
 /* Size in bytes of the static scratch array gdn_frame_scan_fwd_static uses. */
 size_t gdn_static_scratch_bytes(void);
+
+/* Block-scaled FP8 inputs (io_dtype GDN_FP8_E4M3, Dk = Dv in {32, 64, 128}):
+ * the same operation on the dequantised values, for callers whose Q, K and V
+ * arrive in low precision (the 4-step distilled model of "NVIDIA's New 2.6B
+ * World Model Generates Minute-Scale 720p Video on a Single GPU", section
+ * "SANA-WM: One Image, One Minute, One GPU", runs with 4-bit quantization;
+ * the scan is bound by HBM bytes, and FP8 halves the bytes of its three
+ * input streams).  q, k, v: [B][F][N][H][D] OCP FP8 E4M3 bytes (sign, 4
+ * exponent bits with bias 7, 3 mantissa bits; no infinities; 0x7F and 0xFF
+ * are NaN); q_scale, k_scale, v_scale: [B][F][N][H][D/32] E8M0 bytes, one per
+ * 32 consecutive features of a row: the value of element i is
+ * e4m3(x_i) * 2^(s - 127), s its block's scale byte (255 is not a valid
+ * scale).  This is the OCP microscaling MXFP8 (E4M3) layout.  o is bfloat16
+ * [B][F][N][H][D]; beta, alpha, S0, S_final, the flags, the workspace
+ * (gdn_workspace_size of the same descriptor) and every error are as for
+ * gdn_frame_scan_fwd.  The kernels turn each loaded value into bf16 exactly,
+ * so the result equals gdn_frame_scan_fwd's on bf16 inputs holding the
+ * dequantised values.  gdn_frame_scan_fwd and gdn_frame_step refuse this
+ * dtype (GDN_ERR_INVALID_ARG), and so does the backward pass
+ * (GDN_ERR_UNSUPPORTED). */
+gdn_status gdn_frame_scan_fwd_fp8(const gdn_desc* d,
+                                  const void* q, const uint8_t* q_scale,
+                                  const void* k, const uint8_t* k_scale,
+                                  const void* v, const uint8_t* v_scale,
+                                  const float* beta, const float* alpha,
+                                  const float* S0,
+                                  void* o, float* S_final,
+                                  void* workspace, size_t workspace_bytes,
+                                  void* stream);
 
 /* ------------------------------------------------------------------ backward
  * Gradients of gdn_frame_scan_fwd, for training on minute-long sequences

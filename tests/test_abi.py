@@ -245,3 +245,32 @@ def test_bwd_aliasing(lib):
     assert call_bwd(lib, d, dS0=PB["S0"]) == ALIAS
     assert call_bwd(lib, d, dS0=PB["dS_final"] + 16) == ALIAS        # only exact in-place is allowed
     assert call_bwd(lib, desc(B=0), **{n: None for n in BWD_NAMES}) == OK
+
+
+# ---------------------------------------------------------------- block-scaled FP8 entry point
+FP8_NAMES = ["q", "qs", "k", "ks", "v", "vs", "beta", "alpha", "S0", "o", "S_final", "ws"]
+P8 = {n: BASE + i * (1 << 32) for i, n in enumerate(FP8_NAMES)}
+
+
+def call_fp8(lib, d, ws_bytes=1 << 40, **over):
+    p = dict(P8)
+    p.update(over)
+    return lib.gdn_frame_scan_fwd_fp8(None if d is None else ctypes.byref(d), *[p[n] for n in FP8_NAMES[:-1]],
+                                      p["ws"], ctypes.c_size_t(ws_bytes), None)
+
+
+def test_fp8_entry_point_checks(lib):
+    f8 = _lib.GDN_FP8_E4M3
+    assert call_fp8(lib, desc(D=16, io=f8)) == UNSUPPORTED           # one 32-feature scale block at least
+    assert call_fp8(lib, desc(D=64, io=_lib.GDN_BF16)) == INVALID      # this entry point takes FP8 only
+    for n in ["q", "qs", "k", "ks", "v", "vs", "beta", "alpha", "o"]:
+        assert call_fp8(lib, desc(D=64, io=f8), **{n: None}) == INVALID, n
+    assert call_fp8(lib, desc(D=64, io=f8), o=P8["q"]) == ALIAS
+    assert call_fp8(lib, desc(D=64, io=f8), o=P8["ks"]) == ALIAS
+    assert call_fp8(lib, desc(D=64, io=f8), ws=P8["vs"]) == ALIAS
+    need = lib.gdn_workspace_size(ctypes.byref(desc(D=64, io=f8)))
+    assert need == lib.gdn_workspace_size(ctypes.byref(desc(D=64, io=_lib.GDN_BF16)))
+    assert call_fp8(lib, desc(D=64, io=f8), ws_bytes=need - 1) == WORKSPACE
+    # the other entry points refuse the FP8 dtype (they have no scales)
+    assert call(lib, desc(D=64, io=f8)) == INVALID
+    assert call_bwd(lib, desc(D=64, io=f8)) == UNSUPPORTED

@@ -33,3 +33,53 @@ def test_named_configs():
                                                  s0_std=0.0)
     assert inputs.CONFIGS["guidance"]["B"] == 2 and inputs.CONFIGS["guidance"]["s0_std"] == 0.02
     assert inputs.CONFIGS["streaming"]["D"] == 64 and inputs.CONFIGS["streaming"]["H"] == 32
+
+
+# ---------------------------------------------------------------- MXFP8 encoding
+def _e4m3_value(code):
+    """OCP FP8 E4M3 from its bit fields: sign, 4 exponent bits (bias 7), 3
+    mantissa bits; exponent 0 is subnormal; 0x7F and 0xFF are NaN."""
+    s, e, m = code >> 7, (code >> 3) & 0xF, code & 7
+    if e == 15 and m == 7:
+        return float("nan")
+    mag = (m / 8.0) * 2.0 ** -6 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return -mag if s else mag
+
+
+def test_e4m3_decoding_matches_the_format_definition():
+    import torch
+    codes = torch.arange(256, dtype=torch.uint8)
+    dec = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    want = np.array([_e4m3_value(c) for c in range(256)])
+    assert np.array_equal(np.isnan(dec), np.isnan(want))
+    fin = ~np.isnan(want)
+    assert np.array_equal(dec[fin], want[fin])
+    assert want[0x7E] == 448.0 and want[0x01] == 2.0 ** -9 and want[0x38] == 1.0
+
+
+def test_mxfp8_blocks_scales_and_rounding():
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal((3, 7, 128)) * np.exp2(rng.integers(-20, 20, (3, 7, 1)))).astype(np.float32)
+    x[0, 0, :32] = 0.0                                  # an all-zero block
+    codes, scales, deq = inputs.to_mxfp8(x)
+    assert codes.shape == x.shape and scales.shape == (3, 7, 4) and codes.dtype == np.uint8
+    vals = np.array([_e4m3_value(c) for c in range(256)])[codes]
+    e = scales.astype(np.int64) - 127
+    np.testing.assert_array_equal(deq, (vals * np.exp2(np.repeat(e, 32, axis=-1))).astype(np.float32))
+    blk = np.abs(x.reshape(3, 7, 4, 32)).max(-1)
+    nz = blk > 0
+    np.testing.assert_array_equal(e[nz], np.floor(np.log2(blk[nz])) - 8)
+    vmax = np.abs(vals.reshape(3, 7, 4, 32)).max(-1)
+    assert np.all(vmax[nz] >= 256) and np.all(vmax[nz] <= 448)
+    assert np.all(deq[0, 0, :32] == 0)
+    # round to nearest: within half a step of the E4M3 grid at each value's
+    # binade, except above 464 (half a step past 448), which saturates to 448
+    sc = np.exp2(np.repeat(e, 32, axis=-1))
+    t = np.abs(x / sc)
+    step = np.exp2(np.maximum(np.floor(np.log2(np.maximum(t, 2.0 ** -6))), -6) - 3)
+    err = np.abs(x / sc - deq / sc)
+    assert np.all(err[t <= 464] <= step[t <= 464] / 2 + 1e-12)
+    assert np.all(np.abs(deq / sc)[t > 464] == 448)
+    # values already on the grid come back exactly
+    c2, s2, d2 = inputs.to_mxfp8(deq)
+    np.testing.assert_array_equal(d2, deq)
