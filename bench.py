@@ -366,6 +366,69 @@ def fp8_inputs(w, q, k, v, beta, alpha, S0, steps: int, warmup: int, flush_buf, 
             "steps": steps, "warmup": warmup}
 
 
+def block_projections(w, steps: int, warmup: int, C: int, seed: int):
+    """The GDN block around the scan on the same (B, F, N, H, D): input
+    projections from hidden states of width C (gdn_block_in_proj), the scan on
+    the gate logits they produce, and the output projection
+    (gdn_block_out_proj).  Hidden states and weights are seeded device
+    Gaussians (weights scaled by 1/sqrt(fan-in)) rounded to bf16.  Each part is
+    timed by its own HIP events over `steps` calls; the GEMM rates are the
+    algorithmic 2*M*N*K flops over those times."""
+    import torch
+    from gated_deltanet_scan_amd import api
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    B, F, N, H, D = w.B, w.F, w.N, w.H, w.Dk
+    dev = dict(device="cuda", dtype=torch.float32, generator=g)
+    x = (torch.randn((B, F, 1, C), **dev) + torch.randn((B, F, N, C), **dev)).to(torch.bfloat16)
+    w_qkv = (torch.randn((C, 3, H, D), **dev) / C ** 0.5).to(torch.bfloat16)
+    w_gate = (torch.randn((C, 2, H), **dev) / C ** 0.5).to(torch.bfloat16)
+    w_out = (torch.randn((H * D, C), **dev) / (H * D) ** 0.5).to(torch.bfloat16)
+    q, k, v = [torch.empty((B, F, N, H, D), dtype=torch.bfloat16, device="cuda") for _ in range(3)]
+    bl = torch.empty((B, F, N, H), dtype=torch.float32, device="cuda")
+    al = torch.empty((B, F, H), dtype=torch.float32, device="cuda")
+    o = torch.empty_like(q)
+    y = torch.empty((B, F, N, C), dtype=torch.bfloat16, device="cuda")
+    bws = torch.empty(api.block_workspace_size(B, H, F, N, D, C), dtype=torch.uint8, device="cuda")
+    desc = api.make_desc(B, H, F, N, D, torch.bfloat16, gates_are_logits=True)
+    sws = api.alloc_workspace(desc, q.device)
+    stream = torch.cuda.current_stream()
+    parts = {
+        "in_proj": lambda: api.block_in_proj(x, w_qkv, w_gate, H=H, D=D, q=q, k=k, v=v, beta_logit=bl,
+                                             alpha_logit=al, workspace=bws, stream=stream),
+        "scan": lambda: api.frame_scan_fwd(q, k, v, bl, al, None, gates_are_logits=True, o=o, workspace=sws,
+                                           return_state=False, stream=stream),
+        "out_proj": lambda: api.block_out_proj(o, w_out, y=y, workspace=bws, stream=stream),
+    }
+    for _ in range(warmup):
+        for fn in parts.values():
+            fn()
+    torch.cuda.synchronize()
+    ev = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+          for n in parts}
+    for i in range(steps):
+        for n, fn in parts.items():
+            ev[n][i][0].record(stream)
+            fn()
+            ev[n][i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = {n: sum(a.elapsed_time(b) for a, b in ev[n]) / steps for n in parts}
+    M = B * F * N
+    flops = {"in_proj": 2 * M * C * (3 * H * D + 2 * H), "out_proj": 2 * M * H * D * C}
+    total = sum(ms.values())
+    out = {"workload": "the same (B, F, N, H, D) at model width C = %d, bf16 GEMMs with fp32 accumulation "
+                       "(hipBLASLt), scan on the gate logits" % C,
+           "C": C, "ms_per_step": round(total, 5), "tokens_per_s": round(M / (total * 1e-3), 1),
+           "steps": steps, "warmup": warmup}
+    for n in parts:
+        out[n] = {"ms": round(ms[n], 5)}
+        if n in flops:
+            tfs = flops[n] / (ms[n] * 1e-3) / 1e12
+            out[n].update({"alg_flops": flops[n], "tflops": round(tfs, 1),
+                           "mfma_frac": round(tfs / MFMA_BF16_PEAK_TFS, 4)})
+    del x, q, k, v, o, y, bws, sws
+    return out
+
+
 def copy_calibration(nbytes: int, steps: int):
     """A plain device copy of known size, for scaling rocprofv3 byte counters."""
     import torch
@@ -392,6 +455,10 @@ def main():
                     help="timed calls of the backward pass (0: skip)")
     ap.add_argument("--fp8-steps", type=int, default=20,
                     help="timed calls of the block-scaled FP8 input mode (0: skip)")
+    ap.add_argument("--block-steps", type=int, default=10,
+                    help="timed calls of the block around the scan: projections at model width "
+                         "--block-width, the scan, the output projection (0: skip)")
+    ap.add_argument("--block-width", type=int, default=2048)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES bytes --steps times")
     ap.add_argument("--flush", choices=["auto", "on", "off"], default="auto",
@@ -532,6 +599,8 @@ def main():
     line["fp8_inputs"] = (fp8_inputs(w, q, k, v, beta, alpha, S0, args.fp8_steps, min(args.warmup, 5), junk,
                                      ms_per_step)
                           if args.fp8_steps > 0 and w.Dk % 32 == 0 and w.dtype == "bf16" else None)
+    line["block"] = (block_projections(w, args.block_steps, min(args.warmup, 3), args.block_width, args.seed)
+                     if args.block_steps > 0 and w.dtype == "bf16" else None)
     line["streaming_step"] = streaming_step(args.stream_frames) if args.stream_frames > 0 else None
     if args.cpu_budget > 0:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)

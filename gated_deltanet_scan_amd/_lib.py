@@ -71,6 +71,12 @@ def load():
     lib.gdn_frame_scan_bwd.restype = ctypes.c_int
     lib.gdn_frame_scan_fwd_fp8.argtypes = [dp, vp, vp, vp, vp, vp, vp, fp, fp, fp, vp, fp, vp, sz, vp]
     lib.gdn_frame_scan_fwd_fp8.restype = ctypes.c_int
+    lib.gdn_block_workspace_size.argtypes = [dp, ctypes.c_int32]
+    lib.gdn_block_workspace_size.restype = sz
+    lib.gdn_block_in_proj.argtypes = [dp, ctypes.c_int32, vp, vp, vp, vp, vp, vp, fp, fp, vp, sz, vp]
+    lib.gdn_block_in_proj.restype = ctypes.c_int
+    lib.gdn_block_out_proj.argtypes = [dp, ctypes.c_int32, vp, vp, vp, vp, sz, vp]
+    lib.gdn_block_out_proj.restype = ctypes.c_int
     lib.gdn_frame_scan_fwd_static.argtypes = [dp, vp, vp, vp, fp, fp, fp, vp, fp, vp]
     lib.gdn_frame_scan_fwd_static.restype = ctypes.c_int
     lib.gdn_static_scratch_bytes.argtypes = []

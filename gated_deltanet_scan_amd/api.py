@@ -310,3 +310,78 @@ def profile_end() -> dict:
     if st != 0:
         raise GdnError(st, "gdn_profile_end")
     return {lib.gdn_kernel_name(i).decode(): (ms[i], int(n[i])) for i in range(_lib.GDN_NUM_KERNELS)}
+
+
+def block_workspace_size(B, H, F, N, D, C) -> int:
+    desc = make_desc(B, H, F, N, D, torch.bfloat16)
+    return int(_lib.load().gdn_block_workspace_size(ctypes.byref(desc), int(C)))
+
+
+def block_in_proj(x, w_qkv, w_gate, *, H: int, D: int, q=None, k=None, v=None, beta_logit=None,
+                  alpha_logit=None, workspace=None, stream=None):
+    """Input projections of a GDN block: hidden states to the scan's inputs.
+
+    x: [B,F,N,C] bf16; w_qkv: [C,3,H,D] bf16; w_gate: [C,2,H] bf16.  Returns
+    (q, k, v, beta_logit, alpha_logit): q, k, v [B,F,N,H,D] bf16,
+    beta_logit [B,F,N,H] fp32 (one per token) and alpha_logit [B,F,H] fp32
+    (the frame mean of the per-token alpha terms); the logits feed
+    frame_scan_fwd(..., gates_are_logits=True).
+    """
+    B, F, N, C = x.shape
+    _check(x, "x", torch.bfloat16, (B, F, N, C))
+    _check(w_qkv, "w_qkv", torch.bfloat16, (C, 3, H, D))
+    _check(w_gate, "w_gate", torch.bfloat16, (C, 2, H))
+    outs = {"q": q, "k": k, "v": v}
+    for name, t in outs.items():
+        if t is not None:
+            _check(t, name, torch.bfloat16, (B, F, N, H, D))
+    if beta_logit is not None:
+        _check(beta_logit, "beta_logit", torch.float32, (B, F, N, H))
+    if alpha_logit is not None:
+        _check(alpha_logit, "alpha_logit", torch.float32, (B, F, H))
+    _check_workspace(workspace, x.device)
+    desc = make_desc(B, H, F, N, D, torch.bfloat16)
+    lib = _lib.load()
+    stream = _launch_stream(stream, x.device)
+    with torch.cuda.stream(stream):   # allocations belong to the launch stream
+        q, k, v = [t if t is not None else torch.empty((B, F, N, H, D), dtype=torch.bfloat16, device=x.device)
+                   for t in (q, k, v)]
+        if beta_logit is None:
+            beta_logit = torch.empty((B, F, N, H), dtype=torch.float32, device=x.device)
+        if alpha_logit is None:
+            alpha_logit = torch.empty((B, F, H), dtype=torch.float32, device=x.device)
+        if workspace is None:
+            n = int(lib.gdn_block_workspace_size(ctypes.byref(desc), int(C)))
+            workspace = torch.empty(n, dtype=torch.uint8, device=x.device)
+        st = lib.gdn_block_in_proj(ctypes.byref(desc), int(C), _ptr(x), _ptr(w_qkv), _ptr(w_gate), _ptr(q),
+                                   _ptr(k), _ptr(v), _ptr(beta_logit), _ptr(alpha_logit), _ptr(workspace),
+                                   ctypes.c_size_t(workspace.numel()), ctypes.c_void_p(stream.cuda_stream))
+    if st != 0:
+        raise GdnError(st, "gdn_block_in_proj")
+    return q, k, v, beta_logit, alpha_logit
+
+
+def block_out_proj(o, w_out, *, y=None, workspace=None, stream=None):
+    """Output projection of a GDN block: o [B,F,N,H,D] bf16 times w_out
+    [H*D, C] bf16 gives y [B,F,N,C] bf16."""
+    B, F, N, H, D = o.shape
+    C = w_out.shape[-1]
+    _check(o, "o", torch.bfloat16, (B, F, N, H, D))
+    _check(w_out, "w_out", torch.bfloat16, (H * D, C))
+    if y is not None:
+        _check(y, "y", torch.bfloat16, (B, F, N, C))
+    _check_workspace(workspace, o.device)
+    desc = make_desc(B, H, F, N, D, torch.bfloat16)
+    lib = _lib.load()
+    stream = _launch_stream(stream, o.device)
+    with torch.cuda.stream(stream):
+        if y is None:
+            y = torch.empty((B, F, N, C), dtype=torch.bfloat16, device=o.device)
+        if workspace is None:
+            n = int(lib.gdn_block_workspace_size(ctypes.byref(desc), int(C)))
+            workspace = torch.empty(n, dtype=torch.uint8, device=o.device)
+        st = lib.gdn_block_out_proj(ctypes.byref(desc), int(C), _ptr(o), _ptr(w_out), _ptr(y), _ptr(workspace),
+                                    ctypes.c_size_t(workspace.numel()), ctypes.c_void_p(stream.cuda_stream))
+    if st != 0:
+        raise GdnError(st, "gdn_block_out_proj")
+    return y

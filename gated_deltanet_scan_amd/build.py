@@ -7,7 +7,9 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "gdn_api.hip")
+SRCS = [os.path.join(PKG, "csrc", "gdn_api.hip"),    # scan kernels and their C ABI
+        os.path.join(PKG, "csrc", "gdn_block.hip")]  # block projections (hipBLASLt GEMMs)
+LIBS = ["-L/opt/rocm/lib", "-lhipblaslt", "-Wl,-rpath,/opt/rocm/lib"]
 SO = os.path.join(PKG, "libgdn.so")
 
 HIPCC_FLAGS = [
@@ -21,7 +23,7 @@ HIPCC_FLAGS = [
 def build(verbose: bool = False) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     tmp = SO + ".tmp%d" % os.getpid()
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), SRC, "-o", tmp]
+    cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), *SRCS, *LIBS, "-o", tmp]
     if verbose:
         print(" ".join(cmd), file=sys.stderr)
     r = subprocess.run(cmd, capture_output=True, text=True)

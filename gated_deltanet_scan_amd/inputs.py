@@ -196,3 +196,41 @@ def to_torch(w: Workload, device="cuda", *, with_s0: bool = True):
     S0 = dev(w.S0, torch.float32) if (with_s0 and w.S0 is not None) else None
     return (dev(w.q, io), dev(w.k, io), dev(w.v, io), dev(w.beta, torch.float32),
             dev(w.alpha, torch.float32), S0)
+
+
+@dataclass
+class BlockWorkload:
+    """Hidden states and projection weights of one GDN block (all float32
+    arrays holding bfloat16 values exactly)."""
+    B: int
+    F: int
+    N: int
+    C: int
+    H: int
+    D: int
+    x: np.ndarray        # [B,F,N,C]
+    w_qkv: np.ndarray    # [C,3,H,D]
+    w_gate: np.ndarray   # [C,2,H]  (beta columns, then alpha columns)
+    w_out: np.ndarray    # [H*D,C]
+
+
+def make_block(B: int, F: int, N: int, C: int, H: int, D: int, *, seed: int = 0,
+               frame_share: float = 1.0) -> BlockWorkload:
+    """Seeded hidden states and weights for the block projections.
+
+    Recipe (``default_rng((seed, 3))``, float32 standard normals in C order,
+    drawn in this order): a per-frame component s [B,F,1,C], token noise
+    [B,F,N,C], w_qkv [C,3,H,D], w_gate [C,2,H], w_out [H*D,C].
+    x = frame_share * s + noise (tokens of one latent frame share content, so
+    the frame-mean decay logits are not all near zero); the weights are scaled
+    by 1/sqrt(fan-in) (C, or H*D for w_out).  Everything is rounded to bf16.
+    """
+    rng = np.random.default_rng((seed, 3))
+    s = rng.standard_normal((B, F, 1, C), dtype=np.float32)
+    noise = rng.standard_normal((B, F, N, C), dtype=np.float32)
+    x = noise + np.float32(frame_share) * s
+    w_qkv = rng.standard_normal((C, 3, H, D), dtype=np.float32) * np.float32(1.0 / np.sqrt(C))
+    w_gate = rng.standard_normal((C, 2, H), dtype=np.float32) * np.float32(1.0 / np.sqrt(C))
+    w_out = rng.standard_normal((H * D, C), dtype=np.float32) * np.float32(1.0 / np.sqrt(H * D))
+    return BlockWorkload(B, F, N, C, H, D, round_bf16(x), round_bf16(w_qkv), round_bf16(w_gate),
+                         round_bf16(w_out))

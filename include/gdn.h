@@ -30,8 +30,9 @@
  * float32.  Supported: Dk == Dv in {16, 32, 64, 128}.
  *
  * Ownership and execution.  Every pointer is a device pointer owned by the
- * caller; the library keeps none after a call returns and allocates no device
- * memory.  Calls are asynchronous on `stream` (a hipStream_t; NULL is the
+ * caller; the library keeps none after a call returns, and the scan calls
+ * allocate no device memory (the block projections' GEMM library handle is the
+ * one exception, see gdn_block_in_proj).  Calls are asynchronous on `stream` (a hipStream_t; NULL is the
  * default stream) and never synchronise it.  Scratch memory comes from the
  * caller's workspace (see gdn_workspace_size); calls that share a workspace
  * must be ordered on one stream.
@@ -224,6 +225,51 @@ gdn_status gdn_frame_scan_bwd(const gdn_desc* d,
                               const void* dO, const float* dS_final,
                               void* dq, void* dk, void* dv,
                               float* dbeta, float* dalpha, float* dS0,
+                              void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/* ---------------------------------------------------------- block projections
+ * The steps either side of the scan inside a GDN block ("NVIDIA's New 2.6B
+ * World Model Generates Minute-Scale 720p Video on a Single GPU", section "The
+ * Architecture: Replacing Softmax Attention at Scale": the GDN layer sits in
+ * transformer blocks of a hybrid backbone).  The pages do not give the
+ * block's projections; these calls take the plain reading of a linear
+ * attention block: linear maps, without bias, from the hidden states
+ * x [B][F][N][C] (bf16, C the model width) to the scan's inputs, and from the
+ * scan's output back to width C.
+ *
+ * gdn_block_in_proj, with w_qkv [C][3][H][D] and w_gate [C][2][H] (bf16),
+ *     q[b,f,n,h,:] = x[b,f,n,:] w_qkv[:,0,h,:]   (likewise k with 1, v with 2)
+ *     beta_logit[b,f,n,h] = x[b,f,n,:] w_gate[:,0,h]
+ *     alpha_logit[b,f,h]  = (1/N) sum_n x[b,f,n,:] w_gate[:,1,h]
+ * so the decay gate is one per frame, taken from the frame's mean hidden
+ * state.  q, k, v [B][F][N][H][D] are bf16; the logits are float32 and feed
+ * the scan with GDN_FLAG_GATES_ARE_LOGITS.  N == 0 gives alpha_logit = 0.
+ * gdn_block_out_proj, with w_out [H*D][C] (bf16),
+ *     y[b,f,n,:] = o[b,f,n,:,:] (flattened to H*D) w_out          (bf16)
+ * Products accumulate in float32 and round once to the output type.
+ *
+ * d gives B, H, F, N and D = Dk (== Dv); io_dtype must be GDN_BF16 and the
+ * flags are ignored.  B, F and N may be 0; H, D and C must be at least 1
+ * (GDN_ERR_INVALID_ARG), and C and H*D multiples of 8 for 16-byte rows
+ * (GDN_ERR_UNSUPPORTED, as are io_dtype != GDN_BF16 and Dk != Dv).  Pointers
+ * are device pointers owned by the caller: bf16 tensors 16-byte aligned,
+ * float32 tensors 4-byte aligned, workspace 256-byte aligned and at least
+ * gdn_block_workspace_size bytes (both calls use the same size).  Outputs must
+ * be disjoint from the inputs, from each other and from the workspace.  Errors
+ * as for the scan; the calls are asynchronous on `stream`.  The GEMMs run in
+ * hipBLASLt, whose handle (with whatever device memory hipBLASLt keeps for it)
+ * the library creates on a device's first call and keeps until the process
+ * ends; the first call on a device may therefore allocate. */
+size_t gdn_block_workspace_size(const gdn_desc* d, int32_t C);
+gdn_status gdn_block_in_proj(const gdn_desc* d, int32_t C,
+                             const void* x, const void* w_qkv, const void* w_gate,
+                             void* q, void* k, void* v,
+                             float* beta_logit, float* alpha_logit,
+                             void* workspace, size_t workspace_bytes,
+                             void* stream);
+gdn_status gdn_block_out_proj(const gdn_desc* d, int32_t C,
+                              const void* o, const void* w_out, void* y,
                               void* workspace, size_t workspace_bytes,
                               void* stream);
 

@@ -274,3 +274,68 @@ def test_fp8_entry_point_checks(lib):
     # the other entry points refuse the FP8 dtype (they have no scales)
     assert call(lib, desc(D=64, io=f8)) == INVALID
     assert call_bwd(lib, desc(D=64, io=f8)) == UNSUPPORTED
+
+
+# ----------------------------------------------------------- block projections
+BP = {n: BASE + i * (1 << 32) for i, n in enumerate(["x", "w_qkv", "w_gate", "q", "k", "v", "bl", "al", "ws",
+                                                       "o", "w_out", "y"])}
+
+
+def call_in(lib, d, C=64, ws_bytes=1 << 40, **over):
+    p = dict(BP)
+    p.update(over)
+    return lib.gdn_block_in_proj(None if d is None else ctypes.byref(d), C,
+                                 *[p[n] for n in ["x", "w_qkv", "w_gate", "q", "k", "v", "bl", "al", "ws"]],
+                                 ctypes.c_size_t(ws_bytes), None)
+
+
+def call_out(lib, d, C=64, ws_bytes=1 << 40, **over):
+    p = dict(BP)
+    p.update(over)
+    return lib.gdn_block_out_proj(None if d is None else ctypes.byref(d), C, p["o"], p["w_out"], p["y"], p["ws"],
+                                  ctypes.c_size_t(ws_bytes), None)
+
+
+def test_block_workspace_size(lib):
+    d = desc(B=2, H=3, F=5, N=7, D=16)
+    # 32 MiB for the GEMM library plus the fp32 gate product [tokens][2H], rounded to 256 bytes
+    assert lib.gdn_block_workspace_size(ctypes.byref(d), 64) == (32 << 20) + (2 * 5 * 7 * 6 * 4 + 255) // 256 * 256
+    assert lib.gdn_block_workspace_size(ctypes.byref(d), 12) == 0          # C not a multiple of 8
+    assert lib.gdn_block_workspace_size(None, 64) == 0
+
+
+@pytest.mark.parametrize("d,C,expect", [
+    (None, 64, INVALID),
+    (desc(B=-1), 64, INVALID),
+    (desc(H=0), 64, INVALID),
+    (desc(), 0, INVALID),
+    (desc(io=_lib.GDN_F32), 64, UNSUPPORTED),
+    (desc(D=64, Dv=32), 64, UNSUPPORTED),
+    (desc(), 60, UNSUPPORTED),                  # C not a multiple of 8
+    (desc(H=1, D=12), 64, UNSUPPORTED),         # H*D not a multiple of 8
+])
+def test_block_descriptor_errors(lib, d, C, expect):
+    assert call_in(lib, d, C) == expect
+    assert call_out(lib, d, C) == expect
+
+
+def test_block_pointer_checks(lib):
+    d = desc()
+    for n in ["x", "w_qkv", "w_gate", "q", "k", "v", "bl", "al"]:
+        assert call_in(lib, d, **{n: None}) == INVALID, n
+    for n in ["x", "w_qkv", "w_gate", "q", "k", "v"]:
+        assert call_in(lib, d, **{n: BP[n] + 8}) == ALIGN, n
+    assert call_in(lib, d, bl=BP["bl"] + 2) == ALIGN
+    assert call_in(lib, d, ws=BP["ws"] + 16) == ALIGN
+    assert call_in(lib, d, ws=None) == WORKSPACE
+    need = lib.gdn_block_workspace_size(ctypes.byref(d), 64)
+    assert call_in(lib, d, ws_bytes=need - 1) == WORKSPACE
+    assert call_in(lib, d, q=BP["x"]) == ALIAS
+    assert call_in(lib, d, k=BP["q"] + 16) == ALIAS
+    assert call_in(lib, d, al=BP["ws"] + 1024) == ALIAS
+    for n in ["o", "w_out", "y"]:
+        assert call_out(lib, d, **{n: None}) == INVALID, n
+        assert call_out(lib, d, **{n: BP[n] + 8}) == ALIGN, n
+    assert call_out(lib, d, y=BP["o"]) == ALIAS
+    assert call_out(lib, d, y=BP["ws"] + 4096) == ALIAS
+    assert call_out(lib, d, ws_bytes=need - 1) == WORKSPACE
