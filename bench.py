@@ -380,9 +380,9 @@ def block_projections(w, steps: int, warmup: int, C: int, seed: int):
     B, F, N, H, D = w.B, w.F, w.N, w.H, w.Dk
     dev = dict(device="cuda", dtype=torch.float32, generator=g)
     x = (torch.randn((B, F, 1, C), **dev) + torch.randn((B, F, N, C), **dev)).to(torch.bfloat16)
-    w_qkv = (torch.randn((C, 3, H, D), **dev) / C ** 0.5).to(torch.bfloat16)
-    w_gate = (torch.randn((C, 2, H), **dev) / C ** 0.5).to(torch.bfloat16)
-    w_out = (torch.randn((H * D, C), **dev) / (H * D) ** 0.5).to(torch.bfloat16)
+    w_qkv = (torch.randn((3, H, D, C), **dev) / C ** 0.5).to(torch.bfloat16)
+    w_gate = (torch.randn((2, H, C), **dev) / C ** 0.5).to(torch.bfloat16)
+    w_out = (torch.randn((C, H * D), **dev) / (H * D) ** 0.5).to(torch.bfloat16)
     q, k, v = [torch.empty((B, F, N, H, D), dtype=torch.bfloat16, device="cuda") for _ in range(3)]
     bl = torch.empty((B, F, N, H), dtype=torch.float32, device="cuda")
     al = torch.empty((B, F, H), dtype=torch.float32, device="cuda")
@@ -415,8 +415,9 @@ def block_projections(w, steps: int, warmup: int, C: int, seed: int):
     M = B * F * N
     flops = {"in_proj": 2 * M * C * (3 * H * D + 2 * H), "out_proj": 2 * M * H * D * C}
     total = sum(ms.values())
-    out = {"workload": "the same (B, F, N, H, D) at model width C = %d, bf16 GEMMs with fp32 accumulation "
-                       "(hipBLASLt), scan on the gate logits" % C,
+    out = {"workload": "the same (B, F, N, H, D) at model width C = %d: q/k/v and output projections as bf16 "
+                       "GEMMs with fp32 accumulation (hipBLASLt), gate logits and frame means in the library's "
+                       "own kernels, the scan on the gate logits" % C,
            "C": C, "ms_per_step": round(total, 5), "tokens_per_s": round(M / (total * 1e-3), 1),
            "steps": steps, "warmup": warmup}
     for n in parts:

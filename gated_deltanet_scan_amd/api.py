@@ -321,7 +321,8 @@ def block_in_proj(x, w_qkv, w_gate, *, H: int, D: int, q=None, k=None, v=None, b
                   alpha_logit=None, workspace=None, stream=None):
     """Input projections of a GDN block: hidden states to the scan's inputs.
 
-    x: [B,F,N,C] bf16; w_qkv: [C,3,H,D] bf16; w_gate: [C,2,H] bf16.  Returns
+    x: [B,F,N,C] bf16; w_qkv: [3,H,D,C] bf16; w_gate: [2,H,C] bf16 (weights
+    output-major, as torch.nn.Linear stores them).  Returns
     (q, k, v, beta_logit, alpha_logit): q, k, v [B,F,N,H,D] bf16,
     beta_logit [B,F,N,H] fp32 (one per token) and alpha_logit [B,F,H] fp32
     (the frame mean of the per-token alpha terms); the logits feed
@@ -329,8 +330,8 @@ def block_in_proj(x, w_qkv, w_gate, *, H: int, D: int, q=None, k=None, v=None, b
     """
     B, F, N, C = x.shape
     _check(x, "x", torch.bfloat16, (B, F, N, C))
-    _check(w_qkv, "w_qkv", torch.bfloat16, (C, 3, H, D))
-    _check(w_gate, "w_gate", torch.bfloat16, (C, 2, H))
+    _check(w_qkv, "w_qkv", torch.bfloat16, (3, H, D, C))
+    _check(w_gate, "w_gate", torch.bfloat16, (2, H, C))
     outs = {"q": q, "k": k, "v": v}
     for name, t in outs.items():
         if t is not None:
@@ -362,12 +363,12 @@ def block_in_proj(x, w_qkv, w_gate, *, H: int, D: int, q=None, k=None, v=None, b
 
 
 def block_out_proj(o, w_out, *, y=None, workspace=None, stream=None):
-    """Output projection of a GDN block: o [B,F,N,H,D] bf16 times w_out
-    [H*D, C] bf16 gives y [B,F,N,C] bf16."""
+    """Output projection of a GDN block: y [B,F,N,C] bf16 = o [B,F,N,H,D] bf16
+    (flattened to H*D) times the transpose of w_out [C, H*D] bf16."""
     B, F, N, H, D = o.shape
-    C = w_out.shape[-1]
+    C = w_out.shape[0]
     _check(o, "o", torch.bfloat16, (B, F, N, H, D))
-    _check(w_out, "w_out", torch.bfloat16, (H * D, C))
+    _check(w_out, "w_out", torch.bfloat16, (C, H * D))
     if y is not None:
         _check(y, "y", torch.bfloat16, (B, F, N, C))
     _check_workspace(workspace, o.device)

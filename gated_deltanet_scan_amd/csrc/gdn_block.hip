@@ -1,11 +1,12 @@
 // Projections either side of the scan inside a GDN block: the C ABI of
 // gdn_block_in_proj / gdn_block_out_proj (declared in include/gdn.h).
 //
-// The GEMMs are plain bf16 products with fp32 accumulation and go to
-// hipBLASLt; the two steps that are not GEMMs (splitting the gate logits and
-// averaging the decay logits over a frame's tokens) are kernels of this file.
-// Row-major products Y[M][N] = X[M][K] W[K][N] are issued as their
-// column-major transposes Y^T = W^T X^T, which read the same memory.
+// The q, k, v and output products are plain bf16 GEMMs with fp32 accumulation
+// and go to hipBLASLt; the gate logits (2H outputs per token, with a mean over
+// each frame's tokens) are kernels of this file.  Weights are stored
+// output-major, one row of inputs per output.  Row-major products
+// Y[M][N] = X[M][K] W^T are issued as their column-major transposes
+// Y^T = W X^T, which read the same memory.
 #include <hip/hip_runtime.h>
 #include <hipblaslt/hipblaslt.h>
 
@@ -19,6 +20,7 @@
 namespace {
 
 constexpr size_t kLtWorkspace = (size_t)32 << 20;   // hipBLASLt's share of the workspace
+constexpr int kMaxWidth = 1 << 20;                   // C and H*D (32-bit offsets within 64 rows)
 
 std::mutex g_lt_mu;
 hipblasLtHandle_t g_lt[64];
@@ -36,8 +38,9 @@ gdn_status lt_handle(hipblasLtHandle_t* out) {
     return GDN_OK;
 }
 
-// Y[M][N] (row stride ldy, type yt) = X[M][K] (row stride ldx) W[K][N] (row
-// stride ldw), X and W bf16, fp32 accumulation.
+// Y[M][N] (row stride ldy, type yt) = X[M][K] (row stride ldx) W^T, with the
+// weights W stored output-major ([N][K], row stride ldw); X and W bf16, fp32
+// accumulation.
 gdn_status gemm(hipblasLtHandle_t h, int64_t M, int64_t N, int64_t K, const void* X, int64_t ldx, const void* W,
                 int64_t ldw, void* Y, int64_t ldy, hipDataType yt, void* lt_ws, hipStream_t stream) {
     if (M == 0 || N == 0) return GDN_OK;
@@ -47,11 +50,12 @@ gdn_status gemm(hipblasLtHandle_t h, int64_t M, int64_t N, int64_t K, const void
     gdn_status st = GDN_ERR_LAUNCH;
     do {
         if (hipblasLtMatmulDescCreate(&op, HIPBLAS_COMPUTE_32F, HIP_R_32F) != HIPBLAS_STATUS_SUCCESS) break;
-        const hipblasOperation_t nt = HIPBLAS_OP_N;
-        hipblasLtMatmulDescSetAttribute(op, HIPBLASLT_MATMUL_DESC_TRANSA, &nt, sizeof(nt));
+        const hipblasOperation_t tr = HIPBLAS_OP_T, nt = HIPBLAS_OP_N;
+        hipblasLtMatmulDescSetAttribute(op, HIPBLASLT_MATMUL_DESC_TRANSA, &tr, sizeof(tr));
         hipblasLtMatmulDescSetAttribute(op, HIPBLASLT_MATMUL_DESC_TRANSB, &nt, sizeof(nt));
-        // column-major: A = W^T (N x K, ld ldw), B = X^T (K x M, ld ldx), D = Y^T (N x M, ld ldy)
-        if (hipblasLtMatrixLayoutCreate(&la, HIP_R_16BF, N, K, ldw) != HIPBLAS_STATUS_SUCCESS) break;
+        // column-major view: Y^T (N x M) = op(A) B with A = W^T stored K x N (ld ldw)
+        // and transposed, B = X^T stored K x M (ld ldx)
+        if (hipblasLtMatrixLayoutCreate(&la, HIP_R_16BF, K, N, ldw) != HIPBLAS_STATUS_SUCCESS) break;
         if (hipblasLtMatrixLayoutCreate(&lb, HIP_R_16BF, K, M, ldx) != HIPBLAS_STATUS_SUCCESS) break;
         if (hipblasLtMatrixLayoutCreate(&lc, yt, N, M, ldy) != HIPBLAS_STATUS_SUCCESS) break;
         if (hipblasLtMatmulPreferenceCreate(&pref) != HIPBLAS_STATUS_SUCCESS) break;
@@ -76,22 +80,146 @@ gdn_status gemm(hipblasLtHandle_t h, int64_t M, int64_t N, int64_t K, const void
     return st;
 }
 
-// Gate logits from the fused gate product Z[token][2H] (columns 0..H-1: the
-// beta logits, H..2H-1: per-token alpha terms): beta_logit[token][h] = Z[token][h],
-// alpha_logit[b][f][h] = the mean over the frame's N tokens of Z[token][H + h].
-// One workgroup per (b, f); thread h sums its column in token order.
-__global__ void gate_split_kernel(const float* __restrict__ Z, float* __restrict__ beta_logit,
-                                  float* __restrict__ alpha_logit, int N, int H) {
-    const int bf = blockIdx.x;
-    const size_t tok0 = (size_t)bf * N;
-    const float inv_n = N > 0 ? 1.0f / (float)N : 0.0f;
-    for (int h = threadIdx.x; h < H; h += blockDim.x) {
-        float s = 0.0f;
-        for (int n = 0; n < N; ++n) {
-            const float* z = Z + (tok0 + n) * 2 * H;
-            beta_logit[(tok0 + n) * H + h] = z[h];
-            s += z[H + h];
+// ------------------------------------------------------------------ gate logits
+// The gate rows of the input projection have only 2H outputs per token, so a
+// library GEMM would stream the hidden states at a fraction of HBM speed and
+// leave the frame mean to another pass.  gate_proj_kernel reads each hidden
+// state once, forms the 2H logits of 64 tokens with MFMA, writes the beta
+// logits and one partial sum of the alpha terms per 64-token chunk;
+// alpha_mean_kernel adds the chunks of a frame in order and divides by N.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+constexpr int kGateTok = 64;    // tokens per workgroup: four 16-token MFMA tiles
+constexpr int kGateWaves = 4;   // waves per workgroup; they split the contraction
+constexpr int kGateThreads = 64 * kGateWaves;
+
+// Raw buffer resource over [p, p + bytes): loads past the end return zeros,
+// which masks the rows past the last token and the outputs past 2H.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload16(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma(const u32x4& a, const u32x4& b, f32x4 acc) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), acc,
+                                                   0, 0, 0);
+}
+
+// Grid (B*F*ceil(N/64) chunks, the chunk index fastest; 1; slabs of 16*OT gate rows).  MFMA operands: A = gate
+// weights (16 rows = outputs), B = hidden states (16 columns = tokens); lane
+// l = 16g + r holds row/column r and eight contraction indices.  In 128-wide
+// steps lane group g reads 32 consecutive inputs at 128s + 32g (64 bytes per
+// row, so four lanes cover 256 contiguous bytes), and the j-th MFMA of the
+// step takes the eight at offset 8j: both operands use this same order, so the
+// sum covers every input exactly once.  Waves take every fourth step; their
+// partial tiles are added in wave order through LDS.
+template <int OT>
+__global__ __launch_bounds__(kGateThreads) void gate_proj_kernel(const uint16_t* __restrict__ x,
+                                                                 const uint16_t* __restrict__ wg,
+                                                                 float* __restrict__ beta_logit,
+                                                                 float* __restrict__ part, int N, int C, int H,
+                                                                 int nchunk) {
+    constexpr int MW = 16 * OT;     // gate rows per workgroup
+    constexpr int ZS = MW + 4;      // padded row stride of the logit tile in LDS (floats)
+    __shared__ f32x4 red[kGateWaves][OT * 4][64];
+    __shared__ float zt[kGateTok * ZS];
+    const int c = (int)(blockIdx.x % (unsigned)nchunk), bf = (int)(blockIdx.x / (unsigned)nchunk);
+    const int m0 = blockIdx.z * MW;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, r = lane & 15;
+    const int n0 = c * kGateTok;
+    const int rows = min(kGateTok, N - n0);
+    const int mrows = min(MW, 2 * H - m0);
+    const uint32_t rowb = (uint32_t)C * 2;
+    const rsrc_t rx = make_rsrc(x + ((size_t)bf * N + n0) * C, (uint32_t)rows * rowb);
+    const rsrc_t rw = make_rsrc(wg + (size_t)m0 * C, (uint32_t)mrows * rowb);
+    f32x4 acc[OT][4];
+#pragma unroll
+    for (int o = 0; o < OT; ++o)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[o][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int nsup = C / 128;
+    for (int s = wave; s < nsup; s += kGateWaves) {
+        const uint32_t kb = (uint32_t)(128 * s + 32 * g) * 2;
+        u32x4 xa[4][4], wa[OT][4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) xa[t][j] = bload16(rx, (16 * t + r) * rowb + kb + 16 * j);
+#pragma unroll
+        for (int o = 0; o < OT; ++o)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) wa[o][j] = bload16(rw, (16 * o + r) * rowb + kb + 16 * j);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int o = 0; o < OT; ++o)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) acc[o][t] = mma(wa[o][j], xa[t][j], acc[o][t]);
+    }
+    // inputs past the last whole 128-wide step: 32-wide steps, lane group g
+    // taking the eight at k0 + 8g (zeros past C; C is a multiple of 8)
+    for (int k0 = nsup * 128 + 32 * wave; k0 < C; k0 += 32 * kGateWaves) {
+        const int k = k0 + 8 * g;
+        u32x4 xa[4], wa[OT];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            xa[t] = k < C ? bload16(rx, (16 * t + r) * rowb + (uint32_t)k * 2) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int o = 0; o < OT; ++o)
+            wa[o] = k < C ? bload16(rw, (16 * o + r) * rowb + (uint32_t)k * 2) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int o = 0; o < OT; ++o)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) acc[o][t] = mma(wa[o], xa[t], acc[o][t]);
+    }
+
+#pragma unroll
+    for (int o = 0; o < OT; ++o)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) red[wave][o * 4 + t][lane] = acc[o][t];
+    __syncthreads();
+    // tile q = 4o + t of lane l: gate rows 16o + 4g .. +3 of token 16t + r
+#pragma unroll
+    for (int i = 0; i < OT; ++i) {
+        const int q = wave + kGateWaves * i;
+        f32x4 z = red[0][q][lane];
+#pragma unroll
+        for (int w = 1; w < kGateWaves; ++w) z += red[w][q][lane];
+        const int o = q >> 2, t = q & 3;
+        *reinterpret_cast<f32x4*>(&zt[(16 * t + r) * ZS + 16 * o + 4 * g]) = z;
+    }
+    __syncthreads();
+    // beta logits: token-major rows of H, this slab's beta columns contiguous
+    const size_t tok0 = (size_t)bf * N + n0;
+    for (int idx = tid; idx < kGateTok * MW; idx += kGateThreads) {
+        const int n = idx / MW, m = idx % MW, mg = m0 + m;
+        if (n < rows && mg < H) beta_logit[(tok0 + n) * H + mg] = zt[n * ZS + m];
+    }
+    // alpha terms: one partial sum per chunk, tokens in order
+    if (tid < MW) {
+        const int mg = m0 + tid;
+        if (mg >= H && mg < 2 * H) {
+            float sum = 0.f;
+            for (int n = 0; n < rows; ++n) sum += zt[n * ZS + tid];
+            part[((size_t)bf * nchunk + c) * H + (mg - H)] = sum;
         }
+    }
+}
+
+// alpha_logit[bf][h] = (sum over the frame's chunks, in order, of the partial
+// sums) / N; one workgroup per (b, f).  With N == 0 there are no chunks and the
+// logit is 0.
+__global__ void alpha_mean_kernel(const float* __restrict__ part, float* __restrict__ alpha_logit, int nchunk,
+                                  int H, float inv_n) {
+    const int bf = blockIdx.x;
+    for (int h = threadIdx.x; h < H; h += blockDim.x) {
+        float s = 0.f;
+        for (int c = 0; c < nchunk; ++c) s += part[((size_t)bf * nchunk + c) * H + h];
         alpha_logit[(size_t)bf * H + h] = s * inv_n;
     }
 }
@@ -109,11 +237,17 @@ gdn_status check_block(const gdn_desc* d, int32_t C) {
     if (d->io_dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
     if (d->Dk != d->Dv) return GDN_ERR_UNSUPPORTED;
     if (C % 8 != 0 || ((int64_t)d->H * d->Dk) % 8 != 0) return GDN_ERR_UNSUPPORTED;   // 16-byte rows
+    if (C > kMaxWidth || (int64_t)d->H * d->Dk > kMaxWidth) return GDN_ERR_UNSUPPORTED;
+    // one gate workgroup per (b, f, 64-token chunk) in a one-dimensional grid
+    if ((int64_t)d->B * d->F * ((d->N + 63) / 64) > INT32_MAX) return GDN_ERR_UNSUPPORTED;
     return GDN_OK;
 }
 
+int gate_chunks(const gdn_desc* d) { return (d->N + kGateTok - 1) / kGateTok; }
+
+// fp32 partial sums of the alpha terms, [B*F][chunks][H]
 size_t gate_bytes(const gdn_desc* d) {
-    return ((size_t)d->B * d->F * d->N * 2 * d->H * sizeof(float) + 255) / 256 * 256;
+    return ((size_t)d->B * d->F * gate_chunks(d) * d->H * sizeof(float) + 255) / 256 * 256;
 }
 
 }  // namespace
@@ -157,20 +291,37 @@ gdn_status gdn_block_in_proj(const gdn_desc* d, int32_t C, const void* x, const 
     if ((st = lt_handle(&h)) != GDN_OK) return st;
     hipStream_t stream = reinterpret_cast<hipStream_t>(stream_v);
     unsigned char* ws = static_cast<unsigned char*>(workspace);
-    float* Z = reinterpret_cast<float*>(ws + kLtWorkspace);
-    // q, k, v: the three column blocks of w_qkv [C][3][H][D]
+    float* part = reinterpret_cast<float*>(ws + kLtWorkspace);
+    // q, k, v: the three row blocks of w_qkv [3][H][D][C]
     const unsigned char* w = static_cast<const unsigned char*>(w_qkv);
     void* outs_qkv[3] = {q, k, v};
     for (int j = 0; j < 3; ++j)
-        if ((st = gemm(h, M, HD, C, x, C, w + (size_t)j * HD * 2, 3 * HD, outs_qkv[j], HD, HIP_R_16BF, ws, stream)) !=
+        if ((st = gemm(h, M, HD, C, x, C, w + (size_t)j * HD * C * 2, C, outs_qkv[j], HD, HIP_R_16BF, ws, stream)) !=
             GDN_OK)
             return st;
-    // gate logits: Z = x w_gate ([C][2][H]: beta, then alpha), then the split and the frame means
-    if ((st = gemm(h, M, 2 * (int64_t)d->H, C, x, C, w_gate, 2 * d->H, Z, 2 * d->H, HIP_R_32F, ws, stream)) != GDN_OK)
-        return st;
-    if ((size_t)d->B * d->F > 0 && d->H > 0) {
-        hipLaunchKernelGGL(gate_split_kernel, dim3((unsigned)(d->B * d->F)), dim3(64), 0, stream, Z, beta_logit,
-                           alpha_logit, d->N, d->H);
+    // gate logits and the frame means of the alpha terms
+    const int nchunk = gate_chunks(d);
+    const int BF = d->B * d->F;
+    if (nchunk > 0 && BF > 0) {
+        const int H2 = 2 * d->H;
+        const unsigned slabs = (unsigned)((H2 + 63) / 64);
+        const dim3 grid((unsigned)((int64_t)nchunk * BF), 1u, H2 <= 32 ? 1u : slabs);
+        const uint16_t* xx = static_cast<const uint16_t*>(x);
+        const uint16_t* wg = static_cast<const uint16_t*>(w_gate);
+        if (H2 <= 16)
+            hipLaunchKernelGGL(gate_proj_kernel<1>, grid, dim3(kGateThreads), 0, stream, xx, wg, beta_logit, part,
+                               d->N, C, d->H, nchunk);
+        else if (H2 <= 32)
+            hipLaunchKernelGGL(gate_proj_kernel<2>, grid, dim3(kGateThreads), 0, stream, xx, wg, beta_logit, part,
+                               d->N, C, d->H, nchunk);
+        else
+            hipLaunchKernelGGL(gate_proj_kernel<4>, grid, dim3(kGateThreads), 0, stream, xx, wg, beta_logit, part,
+                               d->N, C, d->H, nchunk);
+        if (hipGetLastError() != hipSuccess) return GDN_ERR_LAUNCH;
+    }
+    if (BF > 0) {
+        hipLaunchKernelGGL(alpha_mean_kernel, dim3((unsigned)BF), dim3(64), 0, stream, part, alpha_logit, nchunk,
+                           d->H, d->N > 0 ? 1.0f / (float)d->N : 0.0f);
         if (hipGetLastError() != hipSuccess) return GDN_ERR_LAUNCH;
     }
     return GDN_OK;
@@ -194,7 +345,7 @@ gdn_status gdn_block_out_proj(const gdn_desc* d, int32_t C, const void* o, const
     if (M == 0 || C == 0) return GDN_OK;
     hipblasLtHandle_t h;
     if ((st = lt_handle(&h)) != GDN_OK) return st;
-    return gemm(h, M, C, HD, o, HD, w_out, C, y, C, HIP_R_16BF, workspace, reinterpret_cast<hipStream_t>(stream_v));
+    return gemm(h, M, C, HD, o, HD, w_out, HD, y, C, HIP_R_16BF, workspace, reinterpret_cast<hipStream_t>(stream_v));
 }
 
 }  // extern "C"

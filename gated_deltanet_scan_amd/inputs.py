@@ -209,9 +209,9 @@ class BlockWorkload:
     H: int
     D: int
     x: np.ndarray        # [B,F,N,C]
-    w_qkv: np.ndarray    # [C,3,H,D]
-    w_gate: np.ndarray   # [C,2,H]  (beta columns, then alpha columns)
-    w_out: np.ndarray    # [H*D,C]
+    w_qkv: np.ndarray    # [3,H,D,C]  (weights output-major: one row of inputs per output)
+    w_gate: np.ndarray   # [2,H,C]    (beta rows, then alpha rows)
+    w_out: np.ndarray    # [C,H*D]
 
 
 def make_block(B: int, F: int, N: int, C: int, H: int, D: int, *, seed: int = 0,
@@ -220,7 +220,7 @@ def make_block(B: int, F: int, N: int, C: int, H: int, D: int, *, seed: int = 0,
 
     Recipe (``default_rng((seed, 3))``, float32 standard normals in C order,
     drawn in this order): a per-frame component s [B,F,1,C], token noise
-    [B,F,N,C], w_qkv [C,3,H,D], w_gate [C,2,H], w_out [H*D,C].
+    [B,F,N,C], w_qkv [3,H,D,C], w_gate [2,H,C], w_out [C,H*D].
     x = frame_share * s + noise (tokens of one latent frame share content, so
     the frame-mean decay logits are not all near zero); the weights are scaled
     by 1/sqrt(fan-in) (C, or H*D for w_out).  Everything is rounded to bf16.
@@ -229,8 +229,8 @@ def make_block(B: int, F: int, N: int, C: int, H: int, D: int, *, seed: int = 0,
     s = rng.standard_normal((B, F, 1, C), dtype=np.float32)
     noise = rng.standard_normal((B, F, N, C), dtype=np.float32)
     x = noise + np.float32(frame_share) * s
-    w_qkv = rng.standard_normal((C, 3, H, D), dtype=np.float32) * np.float32(1.0 / np.sqrt(C))
-    w_gate = rng.standard_normal((C, 2, H), dtype=np.float32) * np.float32(1.0 / np.sqrt(C))
-    w_out = rng.standard_normal((H * D, C), dtype=np.float32) * np.float32(1.0 / np.sqrt(H * D))
+    w_qkv = rng.standard_normal((3, H, D, C), dtype=np.float32) * np.float32(1.0 / np.sqrt(C))
+    w_gate = rng.standard_normal((2, H, C), dtype=np.float32) * np.float32(1.0 / np.sqrt(C))
+    w_out = rng.standard_normal((C, H * D), dtype=np.float32) * np.float32(1.0 / np.sqrt(H * D))
     return BlockWorkload(B, F, N, C, H, D, round_bf16(x), round_bf16(w_qkv), round_bf16(w_gate),
                          round_bf16(w_out))

@@ -238,21 +238,24 @@ gdn_status gdn_frame_scan_bwd(const gdn_desc* d,
  * x [B][F][N][C] (bf16, C the model width) to the scan's inputs, and from the
  * scan's output back to width C.
  *
- * gdn_block_in_proj, with w_qkv [C][3][H][D] and w_gate [C][2][H] (bf16),
- *     q[b,f,n,h,:] = x[b,f,n,:] w_qkv[:,0,h,:]   (likewise k with 1, v with 2)
- *     beta_logit[b,f,n,h] = x[b,f,n,:] w_gate[:,0,h]
- *     alpha_logit[b,f,h]  = (1/N) sum_n x[b,f,n,:] w_gate[:,1,h]
+ * Weights are bf16 and stored output-major (one row of inputs per output, the
+ * layout of a torch.nn.Linear weight).  gdn_block_in_proj, with
+ * w_qkv [3][H][D][C] and w_gate [2][H][C],
+ *     q[b,f,n,h,e]        = sum_c x[b,f,n,c] w_qkv[0,h,e,c]   (k: 1, v: 2)
+ *     beta_logit[b,f,n,h] = sum_c x[b,f,n,c] w_gate[0,h,c]
+ *     alpha_logit[b,f,h]  = (1/N) sum_n sum_c x[b,f,n,c] w_gate[1,h,c]
  * so the decay gate is one per frame, taken from the frame's mean hidden
  * state.  q, k, v [B][F][N][H][D] are bf16; the logits are float32 and feed
  * the scan with GDN_FLAG_GATES_ARE_LOGITS.  N == 0 gives alpha_logit = 0.
- * gdn_block_out_proj, with w_out [H*D][C] (bf16),
- *     y[b,f,n,:] = o[b,f,n,:,:] (flattened to H*D) w_out          (bf16)
- * Products accumulate in float32 and round once to the output type.
+ * gdn_block_out_proj, with w_out [C][H*D],
+ *     y[b,f,n,c] = sum_{h,e} o[b,f,n,h,e] w_out[c, h*D + e]           (bf16)
+ * Products accumulate in float32 and round once to the output type; the
+ * results are bitwise reproducible on one device.
  *
  * d gives B, H, F, N and D = Dk (== Dv); io_dtype must be GDN_BF16 and the
  * flags are ignored.  B, F and N may be 0; H, D and C must be at least 1
- * (GDN_ERR_INVALID_ARG), and C and H*D multiples of 8 for 16-byte rows
- * (GDN_ERR_UNSUPPORTED, as are io_dtype != GDN_BF16 and Dk != Dv).  Pointers
+ * (GDN_ERR_INVALID_ARG), and C and H*D multiples of 8 for 16-byte rows and at
+ * most 2^20 (GDN_ERR_UNSUPPORTED, as are io_dtype != GDN_BF16 and Dk != Dv).  Pointers
  * are device pointers owned by the caller: bf16 tensors 16-byte aligned,
  * float32 tensors 4-byte aligned, workspace 256-byte aligned and at least
  * gdn_block_workspace_size bytes (both calls use the same size).  Outputs must

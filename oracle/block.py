@@ -23,20 +23,22 @@ import numpy as np
 
 
 def block_in_proj(x, w_qkv, w_gate):
-    """x [B,F,N,C], w_qkv [C,3,H,D], w_gate [C,2,H] -> (q, k, v [B,F,N,H,D],
-    beta_logit [B,F,N,H], alpha_logit [B,F,H]), float64."""
+    """x [B,F,N,C], w_qkv [3,H,D,C], w_gate [2,H,C] (weights stored output-major,
+    one row of C inputs per output) -> (q, k, v [B,F,N,H,D], beta_logit
+    [B,F,N,H], alpha_logit [B,F,H]), float64."""
     x = np.asarray(x, dtype=np.float64)
     w_qkv = np.asarray(w_qkv, dtype=np.float64)
     w_gate = np.asarray(w_gate, dtype=np.float64)
     B, F, N, C = x.shape
-    if w_qkv.shape[0] != C or w_qkv.shape[1] != 3 or w_gate.shape[:2] != (C, 2):
+    if w_qkv.ndim != 4 or w_qkv.shape[0] != 3 or w_qkv.shape[3] != C or w_gate.shape[0] != 2 \
+            or w_gate.shape[2] != C:
         raise ValueError("weight shapes disagree with x")
-    H, D = w_qkv.shape[2], w_qkv.shape[3]
-    if w_gate.shape[2] != H:
+    H, D = w_qkv.shape[1], w_qkv.shape[2]
+    if w_gate.shape[1] != H:
         raise ValueError("w_gate head count disagrees with w_qkv")
     rows = x.reshape(B * F * N, C)
-    qkv = (rows @ w_qkv.reshape(C, 3 * H * D)).reshape(B, F, N, 3, H, D)
-    gates = (rows @ w_gate.reshape(C, 2 * H)).reshape(B, F, N, 2, H)
+    qkv = (rows @ w_qkv.reshape(3 * H * D, C).T).reshape(B, F, N, 3, H, D)
+    gates = (rows @ w_gate.reshape(2 * H, C).T).reshape(B, F, N, 2, H)
     beta_logit = gates[:, :, :, 0, :]
     if N > 0:
         alpha_logit = gates[:, :, :, 1, :].mean(axis=2)
@@ -46,10 +48,10 @@ def block_in_proj(x, w_qkv, w_gate):
 
 
 def block_out_proj(o, w_out):
-    """o [B,F,N,H,D], w_out [H*D,C] -> y [B,F,N,C], float64."""
+    """o [B,F,N,H,D], w_out [C,H*D] (output-major) -> y [B,F,N,C], float64."""
     o = np.asarray(o, dtype=np.float64)
     w_out = np.asarray(w_out, dtype=np.float64)
     B, F, N, H, D = o.shape
-    if w_out.shape[0] != H * D:
-        raise ValueError("w_out rows must equal H*D")
-    return (o.reshape(B * F * N, H * D) @ w_out).reshape(B, F, N, w_out.shape[1])
+    if w_out.ndim != 2 or w_out.shape[1] != H * D:
+        raise ValueError("w_out columns must equal H*D")
+    return (o.reshape(B * F * N, H * D) @ w_out.T).reshape(B, F, N, w_out.shape[0])

@@ -298,8 +298,11 @@ def call_out(lib, d, C=64, ws_bytes=1 << 40, **over):
 
 def test_block_workspace_size(lib):
     d = desc(B=2, H=3, F=5, N=7, D=16)
-    # 32 MiB for the GEMM library plus the fp32 gate product [tokens][2H], rounded to 256 bytes
-    assert lib.gdn_block_workspace_size(ctypes.byref(d), 64) == (32 << 20) + (2 * 5 * 7 * 6 * 4 + 255) // 256 * 256
+    # 32 MiB for the GEMM library plus fp32 partial sums of the alpha terms per
+    # (b, f, 64-token chunk, h), rounded to 256 bytes
+    assert lib.gdn_block_workspace_size(ctypes.byref(d), 64) == (32 << 20) + 256
+    d = desc(B=1, H=16, F=121, N=880, D=128)
+    assert lib.gdn_block_workspace_size(ctypes.byref(d), 2048) == (32 << 20) + (121 * 14 * 16 * 4 + 255) // 256 * 256
     assert lib.gdn_block_workspace_size(ctypes.byref(d), 12) == 0          # C not a multiple of 8
     assert lib.gdn_block_workspace_size(None, 64) == 0
 
@@ -313,6 +316,7 @@ def test_block_workspace_size(lib):
     (desc(D=64, Dv=32), 64, UNSUPPORTED),
     (desc(), 60, UNSUPPORTED),                  # C not a multiple of 8
     (desc(H=1, D=12), 64, UNSUPPORTED),         # H*D not a multiple of 8
+    (desc(), (1 << 20) + 8, UNSUPPORTED),       # wider than 2^20
 ])
 def test_block_descriptor_errors(lib, d, C, expect):
     assert call_in(lib, d, C) == expect

@@ -75,6 +75,8 @@ SHAPES = [
     (1, 4, 100, 512, 4, 128),
     (1, 2, 1, 64, 1, 16),
     (2, 5, 23, 2048, 16, 128),
+    (1, 2, 130, 200, 24, 16),      # C not a multiple of 128; 48 gate rows (one 64-row slab)
+    (1, 2, 65, 72, 40, 8),         # C < 128; 80 gate rows (two slabs)
 ]
 
 

@@ -15,15 +15,15 @@ from oracle import block
 def selection_weights(C, H, D):
     """w_qkv copies x columns j*H*D + h*D + e into (j, h, e); w_gate copies
     column 3*H*D + j*H + h into gate (j, h)."""
-    w_qkv = np.zeros((C, 3, H, D))
-    w_gate = np.zeros((C, 2, H))
+    w_qkv = np.zeros((3, H, D, C))
+    w_gate = np.zeros((2, H, C))
     for j in range(3):
         for h in range(H):
             for e in range(D):
-                w_qkv[j * H * D + h * D + e, j, h, e] = 1.0
+                w_qkv[j, h, e, j * H * D + h * D + e] = 1.0
     for j in range(2):
         for h in range(H):
-            w_gate[3 * H * D + j * H + h, j, h] = 1.0
+            w_gate[j, h, 3 * H * D + j * H + h] = 1.0
     return w_qkv, w_gate
 
 
@@ -67,9 +67,9 @@ def test_brute_force_tiny():
     B, F, N, C, H, D = 1, 2, 3, 5, 2, 3
     rng = np.random.default_rng(1)
     x = rng.standard_normal((B, F, N, C))
-    w_qkv = rng.standard_normal((C, 3, H, D))
-    w_gate = rng.standard_normal((C, 2, H))
-    w_out = rng.standard_normal((H * D, C))
+    w_qkv = rng.standard_normal((3, H, D, C))
+    w_gate = rng.standard_normal((2, H, C))
+    w_out = rng.standard_normal((C, H * D))
     q, k, v, bl, al = block.block_in_proj(x, w_qkv, w_gate)
     outs = (q, k, v)
     for f in range(F):
@@ -78,28 +78,28 @@ def test_brute_force_tiny():
             for n in range(N):
                 for j in range(3):
                     for e in range(D):
-                        ref = math.fsum(x[0, f, n, c] * w_qkv[c, j, h, e] for c in range(C))
+                        ref = math.fsum(x[0, f, n, c] * w_qkv[j, h, e, c] for c in range(C))
                         assert abs(outs[j][0, f, n, h, e] - ref) < 1e-12
-                ref = math.fsum(x[0, f, n, c] * w_gate[c, 0, h] for c in range(C))
+                ref = math.fsum(x[0, f, n, c] * w_gate[0, h, c] for c in range(C))
                 assert abs(bl[0, f, n, h] - ref) < 1e-12
-                terms.append(math.fsum(x[0, f, n, c] * w_gate[c, 1, h] for c in range(C)))
+                terms.append(math.fsum(x[0, f, n, c] * w_gate[1, h, c] for c in range(C)))
             assert abs(al[0, f, h] - math.fsum(terms) / N) < 1e-12
     o = rng.standard_normal((B, F, N, H, D))
     y = block.block_out_proj(o, w_out)
     for f in range(F):
         for n in range(N):
             for c in range(C):
-                ref = math.fsum(o[0, f, n, h, e] * w_out[h * D + e, c] for h in range(H) for e in range(D))
+                ref = math.fsum(o[0, f, n, h, e] * w_out[c, h * D + e] for h in range(H) for e in range(D))
                 assert abs(y[0, f, n, c] - ref) < 1e-12
 
 
 def test_out_proj_permutation_weights():
-    # w_out picks row perm[c] of the flattened (h, e) axis, h major
+    # output c picks entry perm[c] of the flattened (h, e) axis, h major
     B, F, N, H, D = 1, 2, 3, 3, 4
     C = H * D
     perm = np.random.default_rng(2).permutation(H * D)
-    w_out = np.zeros((H * D, C))
-    w_out[perm, np.arange(C)] = 1.0
+    w_out = np.zeros((C, H * D))
+    w_out[np.arange(C), perm] = 1.0
     o = np.random.default_rng(3).standard_normal((B, F, N, H, D))
     y = block.block_out_proj(o, w_out)
     for c in range(C):
@@ -111,8 +111,8 @@ def test_linearity():
     B, F, N, C, H, D = 2, 2, 5, 8, 2, 4
     rng = np.random.default_rng(4)
     x1, x2 = rng.standard_normal((2, B, F, N, C))
-    w_qkv = rng.standard_normal((C, 3, H, D))
-    w_gate = rng.standard_normal((C, 2, H))
+    w_qkv = rng.standard_normal((3, H, D, C))
+    w_gate = rng.standard_normal((2, H, C))
     a = 0.75
     mix = block.block_in_proj(a * x1 + x2, w_qkv, w_gate)
     one = block.block_in_proj(x1, w_qkv, w_gate)
@@ -124,6 +124,6 @@ def test_linearity():
 def test_no_tokens():
     H, D, C = 2, 4, 16
     x = np.zeros((1, 3, 0, C))
-    q, k, v, bl, al = block.block_in_proj(x, np.ones((C, 3, H, D)), np.ones((C, 2, H)))
+    q, k, v, bl, al = block.block_in_proj(x, np.ones((3, H, D, C)), np.ones((2, H, C)))
     assert q.shape == (1, 3, 0, H, D) and bl.shape == (1, 3, 0, H)
     np.testing.assert_array_equal(al, np.zeros((1, 3, H)))
