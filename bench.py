@@ -299,12 +299,58 @@ def backward(w, q, k, v, beta, alpha, S0, steps: int, warmup: int, flush_buf):
     kernels = {name: {"avg_ms": round(t / n, 5), "launches_per_step": n / steps}
                for name, (t, n) in kern.items() if n > 0}
     gbs = nbytes / (ms * 1e-3) / 1e9
-    return {"workload": "the same workload, gdn_frame_scan_bwd", "ms_per_step": round(ms, 5),
-            "tokens_per_s": round(w.B * w.F * w.N / (ms * 1e-3), 1),
-            "alg_bytes_per_step": nbytes, "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-            "kernels": kernels, "steps": steps, "warmup": warmup,
-            "timing": "HIP events around %d calls (per-kernel figures from a second region with "
-                      "per-launch events)" % steps}
+    out = {"workload": "the same workload, gdn_frame_scan_bwd", "ms_per_step": round(ms, 5),
+           "tokens_per_s": round(w.B * w.F * w.N / (ms * 1e-3), 1),
+           "alg_bytes_per_step": nbytes, "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+           "kernels": kernels, "steps": steps, "warmup": warmup,
+           "timing": "HIP events around %d calls (per-kernel figures from a second region with "
+                     "per-launch events)" % steps}
+    del ws
+    out["saved_states"] = saved_states(w, q, k, v, beta, alpha, S0, dO, dS, steps, warmup, ms)
+    return out
+
+
+def saved_states(w, q, k, v, beta, alpha, S0, dO, dS, steps: int, warmup: int, recompute_ms: float):
+    """The training pair with saved states: gdn_frame_scan_fwd_save (the
+    forward that keeps every frame's operands) and gdn_frame_scan_bwd_saved
+    (the backward that reads them), each timed by HIP events over `steps`
+    calls, beside the recomputing backward's time."""
+    import torch
+    from gated_deltanet_scan_amd import api
+    desc = api.make_desc(w.B, w.H, w.F, w.N, w.Dk, q.dtype)
+    saved = torch.empty(api.saved_size(desc), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(api.workspace_size_bwd_saved(desc), dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(q)
+    S_final = torch.empty((w.B, w.H, w.Dv, w.Dk), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def fwd():
+        api.frame_scan_fwd_save(q, k, v, beta, alpha, S0, o=o, S_final=S_final, saved=saved, stream=stream)
+
+    def bwd():
+        api.frame_scan_bwd(q, k, v, beta, alpha, dO, None, dS, saved=saved, workspace=ws, stream=stream)
+
+    for _ in range(warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    fwd_ms = timed(fwd)
+    fwd()
+    bwd_ms = timed(bwd)
+    return {"fwd_save_ms": round(fwd_ms, 5), "bwd_saved_ms": round(bwd_ms, 5),
+            "bwd_speedup_vs_recompute": round(recompute_ms / bwd_ms, 3),
+            "saved_bytes": int(saved.numel()), "bwd_workspace_bytes": int(ws.numel()),
+            "timing": "HIP events around %d calls of each" % steps}
 
 
 def fp8_inputs(w, q, k, v, beta, alpha, S0, steps: int, warmup: int, flush_buf, bf16_ms: float):

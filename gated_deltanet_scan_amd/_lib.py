@@ -69,6 +69,15 @@ def load():
     lib.gdn_workspace_size_bwd.restype = sz
     lib.gdn_frame_scan_bwd.argtypes = [dp, vp, vp, vp, fp, fp, fp, vp, fp, vp, vp, vp, fp, fp, fp, vp, sz, vp]
     lib.gdn_frame_scan_bwd.restype = ctypes.c_int
+    lib.gdn_saved_size.argtypes = [dp]
+    lib.gdn_saved_size.restype = sz
+    lib.gdn_workspace_size_bwd_saved.argtypes = [dp]
+    lib.gdn_workspace_size_bwd_saved.restype = sz
+    lib.gdn_frame_scan_fwd_save.argtypes = [dp, vp, vp, vp, fp, fp, fp, vp, fp, vp, sz, vp]
+    lib.gdn_frame_scan_fwd_save.restype = ctypes.c_int
+    lib.gdn_frame_scan_bwd_saved.argtypes = [dp, vp, vp, vp, fp, fp, vp, fp, vp, vp, vp, fp, fp, fp, vp, sz, vp, sz,
+                                             vp]
+    lib.gdn_frame_scan_bwd_saved.restype = ctypes.c_int
     lib.gdn_frame_scan_fwd_fp8.argtypes = [dp, vp, vp, vp, vp, vp, vp, fp, fp, fp, vp, fp, vp, sz, vp]
     lib.gdn_frame_scan_fwd_fp8.restype = ctypes.c_int
     lib.gdn_block_workspace_size.argtypes = [dp, ctypes.c_int32]

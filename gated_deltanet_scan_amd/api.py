@@ -252,16 +252,62 @@ def workspace_size_bwd(desc: GdnDesc) -> int:
     return int(_lib.load().gdn_workspace_size_bwd(ctypes.byref(desc)))
 
 
+def saved_size(desc: GdnDesc) -> int:
+    return int(_lib.load().gdn_saved_size(ctypes.byref(desc)))
+
+
+def workspace_size_bwd_saved(desc: GdnDesc) -> int:
+    return int(_lib.load().gdn_workspace_size_bwd_saved(ctypes.byref(desc)))
+
+
+def frame_scan_fwd_save(q, k, v, beta, alpha, S0=None, *, gates_are_logits: bool = False,
+                        eps: float = 1e-6, normalize_keys: bool = True, reverse: bool = False,
+                        o=None, S_final=None, saved=None, return_state: bool = True, stream=None):
+    """frame_scan_fwd that also keeps, in `saved` (a uint8 device tensor of
+    gdn_saved_size bytes, allocated when None), what frame_scan_bwd(...,
+    saved=saved) reads instead of recomputing.  Returns (o, S_final, saved)."""
+    B, F, N, H, D = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check(t, name, q.dtype, (B, F, N, H, D))
+    _check(beta, "beta", torch.float32, (B, F, N, H))
+    _check(alpha, "alpha", torch.float32, (B, F, H))
+    if S0 is not None:
+        _check(S0, "S0", torch.float32, (B, H, D, D))
+    if o is not None:
+        _check(o, "o", q.dtype, (B, F, N, H, D))
+    if S_final is not None:
+        _check(S_final, "S_final", torch.float32, (B, H, D, D))
+    _check_workspace(saved, q.device)
+    desc = make_desc(B, H, F, N, D, q.dtype, gates_are_logits=gates_are_logits, eps=eps,
+                     normalize_keys=normalize_keys, reverse=reverse)
+    stream = _launch_stream(stream, q.device)
+    with torch.cuda.stream(stream):   # allocations belong to the launch stream
+        if o is None:
+            o = torch.empty_like(q)
+        if S_final is None and return_state:
+            S_final = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
+        if saved is None:
+            saved = torch.empty(max(saved_size(desc), 1), dtype=torch.uint8, device=q.device)
+        st = _lib.load().gdn_frame_scan_fwd_save(
+            ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha), _ptr(S0), _ptr(o),
+            _ptr(S_final), _ptr(saved), ctypes.c_size_t(saved.numel()), ctypes.c_void_p(stream.cuda_stream))
+    if st != 0:
+        raise GdnError(st, "gdn_frame_scan_fwd_save")
+    return o, S_final, saved
+
+
 def frame_scan_bwd(q, k, v, beta, alpha, dO, S0=None, dS_final=None, *, gates_are_logits: bool = False,
                    eps: float = 1e-6, normalize_keys: bool = True, reverse: bool = False,
-                   workspace=None, return_dS0: bool = True, stream=None):
+                   workspace=None, return_dS0: bool = True, saved=None, stream=None):
     """Gradients of frame_scan_fwd with respect to its inputs.
 
     q, k, v, beta, alpha, S0 and the flags as for frame_scan_fwd; dO: [B,F,N,H,D]
     in the q dtype (the loss gradient of o); dS_final: [B,H,D,D] fp32 or None
     (zeros).  Returns (dq, dk, dv, dbeta, dalpha, dS0): dq, dk, dv in the q
     dtype, the rest fp32 (dbeta and dalpha are logit gradients with
-    gates_are_logits; dS0 is None when return_dS0 is False).
+    gates_are_logits; dS0 is None when return_dS0 is False).  With `saved`
+    (from frame_scan_fwd_save on the same inputs) the per-frame operands of
+    the forward walk are read from it instead of recomputed, and S0 is unused.
     """
     B, F, N, H, D = q.shape
     _check(q, "q", q.dtype, (B, F, N, H, D))
@@ -282,16 +328,26 @@ def frame_scan_bwd(q, k, v, beta, alpha, dO, S0=None, dS_final=None, *, gates_ar
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
         dbeta, dalpha = torch.empty_like(beta), torch.empty_like(alpha)
         dS0 = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device) if return_dS0 else None
+        lib = _lib.load()
         if workspace is None:
-            n = workspace_size_bwd(desc)
+            n = workspace_size_bwd_saved(desc) if saved is not None else workspace_size_bwd(desc)
             workspace = torch.empty(n, dtype=torch.uint8, device=q.device) if n > 0 else None
         ws_bytes = 0 if workspace is None else workspace.numel()
-        st = _lib.load().gdn_frame_scan_bwd(
-            ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha), _ptr(S0), _ptr(dO),
-            _ptr(dS_final), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbeta), _ptr(dalpha), _ptr(dS0),
-            _ptr(workspace), ctypes.c_size_t(ws_bytes), ctypes.c_void_p(stream.cuda_stream))
+        if saved is not None:
+            name = "gdn_frame_scan_bwd_saved"
+            st = lib.gdn_frame_scan_bwd_saved(
+                ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha), _ptr(dO),
+                _ptr(dS_final), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbeta), _ptr(dalpha), _ptr(dS0),
+                _ptr(saved), ctypes.c_size_t(saved.numel()), _ptr(workspace), ctypes.c_size_t(ws_bytes),
+                ctypes.c_void_p(stream.cuda_stream))
+        else:
+            name = "gdn_frame_scan_bwd"
+            st = lib.gdn_frame_scan_bwd(
+                ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha), _ptr(S0), _ptr(dO),
+                _ptr(dS_final), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbeta), _ptr(dalpha), _ptr(dS0),
+                _ptr(workspace), ctypes.c_size_t(ws_bytes), ctypes.c_void_p(stream.cuda_stream))
     if st != 0:
-        raise GdnError(st, "gdn_frame_scan_bwd")
+        raise GdnError(st, name)
     return dq, dk, dv, dbeta, dalpha, dS0
 
 

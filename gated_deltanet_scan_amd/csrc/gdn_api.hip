@@ -577,28 +577,49 @@ gdn_status run_fp8(const gdn_desc* d, const void* q, const uint8_t* qs, const vo
 // items (Gm, U, S planes) and the backward items (W, X planes); the states
 // entering chunks 1.. of the forward walk; the state gradient carried between
 // chunks; every token's key scale (fp32 [B][F][N][H]).
+//
+// With saved states (gdn_frame_scan_fwd_save), the forward items of every
+// chunk, the states entering the chunks and the key scales live in the
+// caller's `saved` buffer instead: one item set per chunk (in the order the
+// walk visits them), then one state per chunk (the state entering it: S0 or
+// zeros for the first), then the key scales.  The backward workspace then
+// holds only the backward items and the carried state gradient.
 struct BwdPlan {
     Plan p;
     int nchunks = 0;
+    size_t set = 0;          // one item set (every (b, h) unit, Fc frames)
     size_t ws2_off = 0, enter_off = 0, state_bytes = 0, dcarry_off = 0, rho_off = 0, ws_bytes = 0;
+    // saved-state layout
+    size_t sv_enter_off = 0, sv_rho_off = 0, sv_bytes = 0;
 };
 
 size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
-gdn_status check_bwd(const gdn_desc* d, BwdPlan* bp) {
+gdn_status check_bwd(const gdn_desc* d, BwdPlan* bp, bool saved = false) {
     Plan& p = bp->p;
     gdn_status st = check_desc(d, false, &p);
     if (st != GDN_OK) return st;
     if (d->io_dtype == GDN_FP8_E4M3) return GDN_ERR_UNSUPPORTED;
     bp->nchunks = d->F > 0 ? (d->F + p.Fc - 1) / p.Fc : 0;
     const size_t set = round256((size_t)p.units * p.Fc * p.item_bytes);
+    bp->set = set;
     bp->state_bytes = round256((size_t)p.units * p.D * p.D * sizeof(float));
+    const size_t rho_bytes = round256((size_t)d->B * d->F * d->N * d->H * sizeof(float));
+    const bool any = p.units > 0 && d->F > 0;
+    bp->sv_enter_off = (size_t)bp->nchunks * set;
+    bp->sv_rho_off = bp->sv_enter_off + (size_t)bp->nchunks * bp->state_bytes;
+    bp->sv_bytes = any ? bp->sv_rho_off + rho_bytes : 0;
+    if (saved) {
+        bp->ws2_off = 0;
+        bp->dcarry_off = set;
+        bp->ws_bytes = any ? set + bp->state_bytes : 0;
+        return GDN_OK;
+    }
     bp->ws2_off = set;
     bp->enter_off = 2 * set;
     bp->dcarry_off = bp->enter_off + (size_t)(bp->nchunks > 1 ? bp->nchunks - 1 : 0) * bp->state_bytes;
     bp->rho_off = bp->dcarry_off + bp->state_bytes;
-    const size_t rho_bytes = round256((size_t)d->B * d->F * d->N * d->H * sizeof(float));
-    bp->ws_bytes = (p.units > 0 && d->F > 0) ? bp->rho_off + rho_bytes : 0;
+    bp->ws_bytes = any ? bp->rho_off + rho_bytes : 0;
     return GDN_OK;
 }
 
@@ -621,15 +642,23 @@ struct BwdIO {
 // way and leaves X_f (the state gradient carried in dS0 or the workspace);
 // frame_output in its transposed role forms dq; frame_dkv forms dk, dv, dbeta
 // and dalpha.
+//
+// With `saved` (not NULL) the forward items, the states entering the chunks
+// and the key scales come from the buffer gdn_frame_scan_fwd_save filled, and
+// the recomputation (the first walk and each chunk's frame_gram and
+// state_scan) is skipped.
 template <typename T, int D>
-gdn_status launch_bwd(const BwdPlan& bp, ScanArgs a, const BwdIO& g, hipStream_t stream, int cus) {
+gdn_status launch_bwd(const BwdPlan& bp, ScanArgs a, const BwdIO& g, hipStream_t stream, int cus,
+                      const unsigned char* saved = nullptr) {
     const Plan& p = bp.p;
     const int units = (int)p.units;
     unsigned char* ws = a.ws;
     unsigned char* ws2 = ws + bp.ws2_off;
     float* dcarry = reinterpret_cast<float*>(ws + bp.dcarry_off);
     const float* S0 = a.S_in;
+    unsigned char* sv = const_cast<unsigned char*>(saved);
     auto enter = [&](int v) -> float* {
+        if (sv) return reinterpret_cast<float*>(sv + bp.sv_enter_off + (size_t)v * bp.state_bytes);
         return v == 0 ? const_cast<float*>(S0) : reinterpret_cast<float*>(ws + bp.enter_off + (size_t)(v - 1) * bp.state_bytes);
     };
     auto chunk = [&](int v, ScanArgs& s) {
@@ -651,7 +680,7 @@ gdn_status launch_bwd(const BwdPlan& bp, ScanArgs a, const BwdIO& g, hipStream_t
         return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
     };
     gdn_status st = GDN_OK;
-    for (int v = 0; v + 1 < bp.nchunks; ++v) {      // states entering chunks 1..
+    for (int v = 0; !sv && v + 1 < bp.nchunks; ++v) {   // states entering chunks 1..
         ScanArgs s = a;
         chunk(v, s);
         s.S_in = enter(v);
@@ -664,9 +693,14 @@ gdn_status launch_bwd(const BwdPlan& bp, ScanArgs a, const BwdIO& g, hipStream_t
         chunk(v, s);
         s.S_in = enter(v);
         s.S_out = nullptr;
-        s.rho = reinterpret_cast<float*>(ws + bp.rho_off);       // unused with keys as given
-        if ((st = gram(s, a.raw_keys ? 0 : 1)) != GDN_OK) return st;
-        if ((st = launch_state<T, D>(s, stream)) != GDN_OK) return st;
+        if (sv) {                                    // the forward call's items and key scales
+            s.ws = sv + (size_t)v * bp.set;
+            s.rho = reinterpret_cast<float*>(sv + bp.sv_rho_off);
+        } else {                                     // recompute them
+            s.rho = reinterpret_cast<float*>(ws + bp.rho_off);   // unused with keys as given
+            if ((st = gram(s, a.raw_keys ? 0 : 1)) != GDN_OK) return st;
+            if ((st = launch_state<T, D>(s, stream)) != GDN_OK) return st;
+        }
         ScanArgs w = s;                              // W_f = dO_f^T Q_f into the backward items
         w.k = a.q;
         w.v = g.dO;
@@ -701,21 +735,24 @@ gdn_status launch_bwd(const BwdPlan& bp, ScanArgs a, const BwdIO& g, hipStream_t
 }
 
 template <typename T>
-gdn_status dispatch_bwd(const BwdPlan& bp, const ScanArgs& a, const BwdIO& g, hipStream_t s, int cus) {
+gdn_status dispatch_bwd(const BwdPlan& bp, const ScanArgs& a, const BwdIO& g, hipStream_t s, int cus,
+                        const unsigned char* saved) {
     switch (bp.p.D) {
-        case 16: return launch_bwd<T, 16>(bp, a, g, s, cus);
-        case 32: return launch_bwd<T, 32>(bp, a, g, s, cus);
-        case 64: return launch_bwd<T, 64>(bp, a, g, s, cus);
-        case 128: return launch_bwd<T, 128>(bp, a, g, s, cus);
+        case 16: return launch_bwd<T, 16>(bp, a, g, s, cus, saved);
+        case 32: return launch_bwd<T, 32>(bp, a, g, s, cus, saved);
+        case 64: return launch_bwd<T, 64>(bp, a, g, s, cus, saved);
+        case 128: return launch_bwd<T, 128>(bp, a, g, s, cus, saved);
         default: return GDN_ERR_UNSUPPORTED;
     }
 }
 
+// saved_mode: gdn_frame_scan_bwd_saved (S0 is not an argument; `saved` holds
+// what the forward call left)
 gdn_status run_bwd(const gdn_desc* d, const void* q, const void* k, const void* v, const float* beta,
                    const float* alpha, const float* S0, const BwdIO& g, void* workspace, size_t workspace_bytes,
-                   void* stream_v) {
+                   void* stream_v, bool saved_mode = false, const void* saved = nullptr, size_t saved_bytes = 0) {
     BwdPlan bp;
-    gdn_status st = check_bwd(d, &bp);
+    gdn_status st = check_bwd(d, &bp, saved_mode);
     if (st != GDN_OK) return st;
     const Plan& p = bp.p;
     const size_t ntok = (size_t)d->B * d->F * d->N * d->H;
@@ -737,11 +774,17 @@ gdn_status run_bwd(const gdn_desc* d, const void* q, const void* k, const void* 
         if (!workspace || workspace_bytes < bp.ws_bytes) return GDN_ERR_WORKSPACE;
         if (!aligned(workspace, 256)) return GDN_ERR_ALIGNMENT;
     }
+    if (saved_mode && bp.sv_bytes > 0) {
+        if (!saved || saved_bytes < bp.sv_bytes) return GDN_ERR_WORKSPACE;
+        if (!aligned(saved, 256)) return GDN_ERR_ALIGNMENT;
+    }
     // aliasing: outputs overlap no input, no other output and not the workspace
-    // (dS0 == dS_final exactly is allowed)
+    // (dS0 == dS_final exactly is allowed); `saved` is an input
     auto R = [](const void* ptr, size_t n) { return rng(ptr, ptr ? n : 0); };
-    const Range ins[] = {R(q, tok_bytes), R(k, tok_bytes),     R(v, tok_bytes),   R(beta, beta_bytes),
-                         R(alpha, alpha_bytes), R(S0, state_bytes), R(g.dO, tok_bytes), R(g.dS_final, state_bytes)};
+    const Range ins[] = {R(q, tok_bytes),      R(k, tok_bytes),     R(v, tok_bytes),
+                         R(beta, beta_bytes),  R(alpha, alpha_bytes), R(S0, state_bytes),
+                         R(g.dO, tok_bytes),   R(g.dS_final, state_bytes),
+                         R(saved_mode ? saved : nullptr, bp.sv_bytes)};
     const Range outs[] = {R(g.dq, tok_bytes),        R(g.dk, tok_bytes),         R(g.dv, tok_bytes),
                           R(g.dbeta, beta_bytes),    R(g.dalpha, alpha_bytes),   R(g.dS0, state_bytes),
                           R(workspace, workspace ? bp.ws_bytes : 0)};
@@ -791,8 +834,139 @@ gdn_status run_bwd(const gdn_desc* d, const void* q, const void* k, const void* 
     a.tchunk = 16;
     a.parts = 1;
     a.tpart = d->N;
-    return d->io_dtype == GDN_BF16 ? dispatch_bwd<uint16_t>(bp, a, g, stream, cus)
-                                   : dispatch_bwd<float>(bp, a, g, stream, cus);
+    const unsigned char* sv = saved_mode ? static_cast<const unsigned char*>(saved) : nullptr;
+    return d->io_dtype == GDN_BF16 ? dispatch_bwd<uint16_t>(bp, a, g, stream, cus, sv)
+                                   : dispatch_bwd<float>(bp, a, g, stream, cus, sv);
+}
+
+// ---------------------------------------------------------------- forward with saved states
+// gdn_frame_scan_fwd's launches with the saved buffer as the workspace: chunk
+// v (in visit order) builds its items in item set v, reads the state entering
+// it from slot v and leaves the state after it in slot v + 1 (S_final after
+// the last chunk); frame_gram also writes the key scales.  Slot 0 first
+// receives S0 (or zeros), so the backward call needs no S0 even when S_final
+// overwrote it.
+template <typename T, int D>
+gdn_status launch_save(const BwdPlan& bp, ScanArgs a, unsigned char* sv, hipStream_t stream, int cus) {
+    const Plan& p = bp.p;
+    const int units = (int)p.units;
+    auto slot = [&](int v) { return reinterpret_cast<float*>(sv + bp.sv_enter_off + (size_t)v * bp.state_bytes); };
+    {
+        const size_t n = (size_t)units * D * D;
+        ProfScope ps(K_COPY, stream);
+        hipLaunchKernelGGL(gdn::state_copy_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a.S_in,
+                           slot(0), n);
+        if (hipGetLastError() != hipSuccess) return GDN_ERR_LAUNCH;
+    }
+    float* const S_final = a.S_out;
+    gdn_status st = GDN_OK;
+    for (int v = 0; v < bp.nchunks; ++v) {
+        ScanArgs s = a;
+        const int ci = a.reverse ? bp.nchunks - 1 - v : v;
+        s.f0 = ci * p.Fc;
+        s.Fc = a.F - s.f0 < p.Fc ? a.F - s.f0 : p.Fc;
+        s.ws = sv + (size_t)v * bp.set;
+        s.S_in = slot(v);
+        s.S_out = v + 1 < bp.nchunks ? slot(v + 1) : S_final;
+        s.rho = reinterpret_cast<float*>(sv + bp.sv_rho_off);
+        {
+            const int items = units * s.Fc;
+            const int grid = items < cus ? items : (cus > 0 ? cus : 256);
+            ProfScope ps(K_GRAM, stream);
+            if (a.raw_keys)
+                hipLaunchKernelGGL((gdn::frame_gram_kernel<T, D, false>), dim3(grid), dim3(1024), 0, stream, s);
+            else
+                hipLaunchKernelGGL((gdn::frame_gram_kernel<T, D, false, false, true>), dim3(grid), dim3(1024), 0,
+                                   stream, s);
+            if (hipGetLastError() != hipSuccess) return GDN_ERR_LAUNCH;
+        }
+        if ((st = launch_state<T, D>(s, stream)) != GDN_OK) return st;
+        if ((st = launch_output<T, D>(s, stream, cus)) != GDN_OK) return st;
+    }
+    return GDN_OK;
+}
+
+template <typename T>
+gdn_status dispatch_save(const BwdPlan& bp, const ScanArgs& a, unsigned char* sv, hipStream_t s, int cus) {
+    switch (bp.p.D) {
+        case 16: return launch_save<T, 16>(bp, a, sv, s, cus);
+        case 32: return launch_save<T, 32>(bp, a, sv, s, cus);
+        case 64: return launch_save<T, 64>(bp, a, sv, s, cus);
+        case 128: return launch_save<T, 128>(bp, a, sv, s, cus);
+        default: return GDN_ERR_UNSUPPORTED;
+    }
+}
+
+gdn_status run_save(const gdn_desc* d, const void* q, const void* k, const void* v, const float* beta,
+                    const float* alpha, const float* S0, void* o, float* S_final, void* saved, size_t saved_bytes,
+                    void* stream_v) {
+    BwdPlan bp;
+    gdn_status st = check_bwd(d, &bp, true);
+    if (st != GDN_OK) return st;
+    const Plan& p = bp.p;
+    const size_t ntok = (size_t)d->B * d->F * d->N * d->H;
+    const size_t tok_bytes = ntok * (size_t)p.D * p.esz;
+    const size_t beta_bytes = ntok * sizeof(float);
+    const size_t alpha_bytes = (size_t)d->B * d->F * d->H * sizeof(float);
+    const size_t state_bytes = (size_t)p.units * p.D * p.D * sizeof(float);
+    if (ntok > 0 && (!q || !k || !v || !beta || !o)) return GDN_ERR_INVALID_ARG;
+    if (alpha_bytes > 0 && !alpha) return GDN_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return GDN_ERR_ALIGNMENT;
+    if (!aligned(beta, 4) || !aligned(alpha, 4)) return GDN_ERR_ALIGNMENT;
+    if (!aligned(S0, 16) || !aligned(S_final, 16)) return GDN_ERR_ALIGNMENT;
+    if (bp.sv_bytes > 0) {
+        if (!saved || saved_bytes < bp.sv_bytes) return GDN_ERR_WORKSPACE;
+        if (!aligned(saved, 256)) return GDN_ERR_ALIGNMENT;
+    }
+    auto R = [](const void* ptr, size_t n) { return rng(ptr, ptr ? n : 0); };
+    const Range ins[] = {R(q, tok_bytes), R(k, tok_bytes), R(v, tok_bytes), R(beta, beta_bytes), R(alpha, alpha_bytes),
+                         R(S0, state_bytes)};
+    const Range ro = R(o, tok_bytes), rsf = R(S_final, state_bytes), rs = R(saved, bp.sv_bytes);
+    for (int i = 0; i < 6; ++i) {
+        if (overlap(ro, ins[i]) || overlap(rs, ins[i])) return GDN_ERR_ALIAS;
+        if (i < 5 && overlap(rsf, ins[i])) return GDN_ERR_ALIAS;
+    }
+    if (overlap(rsf, ins[5]) && S_final != S0) return GDN_ERR_ALIAS;
+    if (overlap(ro, rsf) || overlap(ro, rs) || overlap(rsf, rs)) return GDN_ERR_ALIAS;
+
+    if (p.units == 0) return GDN_OK;
+    if (d->F == 0 && !S_final) return GDN_OK;
+    int cus = 0;
+    if ((st = check_device(&cus)) != GDN_OK) return st;
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_v);
+    if (d->F == 0) {  // S_final <- S0 (or zeros); nothing to save
+        if (S_final == S0) return GDN_OK;
+        const size_t n = (size_t)p.units * p.D * p.D;
+        ProfScope ps(K_COPY, stream);
+        hipLaunchKernelGGL(gdn::state_copy_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, S0,
+                           S_final, n);
+        return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+    }
+    ScanArgs a;
+    memset(&a, 0, sizeof(a));
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.beta = beta;
+    a.alpha = alpha;
+    a.S_in = S0;
+    a.o = o;
+    a.S_out = S_final;
+    a.B = d->B;
+    a.H = d->H;
+    a.F = d->F;
+    a.N = d->N;
+    a.logits = (d->flags & GDN_FLAG_GATES_ARE_LOGITS) ? 1 : 0;
+    a.raw_keys = (d->flags & GDN_FLAG_NO_KEY_NORM) ? 1 : 0;
+    a.reverse = (d->flags & GDN_FLAG_REVERSE) ? 1 : 0;
+    a.eps = d->eps;
+    a.tsplit = 1;
+    a.tchunk = 16;
+    a.parts = 1;
+    a.tpart = d->N;
+    unsigned char* sv = static_cast<unsigned char*>(saved);
+    return d->io_dtype == GDN_BF16 ? dispatch_save<uint16_t>(bp, a, sv, stream, cus)
+                                   : dispatch_save<float>(bp, a, sv, stream, cus);
 }
 
 }  // namespace
@@ -847,6 +1021,33 @@ gdn_status gdn_frame_scan_bwd(const gdn_desc* d, const void* q, const void* k, c
                               void* stream) {
     const BwdIO g{dO, dS_final, dq, dk, dv, dbeta, dalpha, dS0};
     return run_bwd(d, q, k, v, beta, alpha, S0, g, workspace, workspace_bytes, stream);
+}
+
+size_t gdn_saved_size(const gdn_desc* d) {
+    BwdPlan bp;
+    if (check_bwd(d, &bp, true) != GDN_OK) return 0;
+    return bp.sv_bytes;
+}
+
+size_t gdn_workspace_size_bwd_saved(const gdn_desc* d) {
+    BwdPlan bp;
+    if (check_bwd(d, &bp, true) != GDN_OK) return 0;
+    return bp.ws_bytes;
+}
+
+gdn_status gdn_frame_scan_fwd_save(const gdn_desc* d, const void* q, const void* k, const void* v,
+                                   const float* beta, const float* alpha, const float* S0, void* o, float* S_final,
+                                   void* saved, size_t saved_bytes, void* stream) {
+    return run_save(d, q, k, v, beta, alpha, S0, o, S_final, saved, saved_bytes, stream);
+}
+
+gdn_status gdn_frame_scan_bwd_saved(const gdn_desc* d, const void* q, const void* k, const void* v,
+                                    const float* beta, const float* alpha, const void* dO, const float* dS_final,
+                                    void* dq, void* dk, void* dv, float* dbeta, float* dalpha, float* dS0,
+                                    const void* saved, size_t saved_bytes, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+    const BwdIO g{dO, dS_final, dq, dk, dv, dbeta, dalpha, dS0};
+    return run_bwd(d, q, k, v, beta, alpha, nullptr, g, workspace, workspace_bytes, stream, true, saved, saved_bytes);
 }
 
 const char* gdn_status_string(gdn_status s) {

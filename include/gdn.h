@@ -32,8 +32,9 @@
  * Ownership and execution.  Every pointer is a device pointer owned by the
  * caller; the library keeps none after a call returns, and the scan calls
  * allocate no device memory (the block projections' GEMM library handle is the
- * one exception, see gdn_block_in_proj).  Calls are asynchronous on `stream` (a hipStream_t; NULL is the
- * default stream) and never synchronise it.  Scratch memory comes from the
+ * one exception, see gdn_block_in_proj).  Calls are asynchronous on `stream`
+ * (a hipStream_t; NULL is the default stream) and never synchronise it.
+ * Scratch memory comes from the
  * caller's workspace (see gdn_workspace_size); calls that share a workspace
  * must be ordered on one stream.
  *
@@ -227,6 +228,44 @@ gdn_status gdn_frame_scan_bwd(const gdn_desc* d,
                               float* dbeta, float* dalpha, float* dS0,
                               void* workspace, size_t workspace_bytes,
                               void* stream);
+
+/* Training with saved states.  gdn_frame_scan_bwd recomputes every per-frame
+ * operand of the forward walk (the Gram products, U and the states S_f),
+ * which costs about two thirds of a forward call on each backward call.  A
+ * caller with the memory to spare (gdn_saved_size bytes per call: at B1 H16
+ * F121 N880 d128 about 325 MB) can keep them instead:
+ * gdn_frame_scan_fwd_save is gdn_frame_scan_fwd (the same o and S_final, bit
+ * for bit when F > 1; a one-frame gdn_frame_scan_fwd call runs the streaming
+ * step's kernels, which add in another order, so there the two agree to
+ * rounding) that leaves in `saved` every frame's operands, the states entering
+ * its launch chunks (S0 or zeros first) and every token's key scale, and
+ * gdn_frame_scan_bwd_saved is gdn_frame_scan_bwd (the same gradients, bit for
+ * bit) that reads them instead of recomputing, so it takes no S0 and needs
+ * only gdn_workspace_size_bwd_saved bytes of workspace (about half of
+ * gdn_workspace_size_bwd's).  The backward call must see the same descriptor
+ * and inputs as the forward call that filled `saved`, which it reads and does
+ * not change; `saved` is owned by the caller, must be 256-byte aligned and
+ * disjoint from every other argument of both calls.  bf16 and fp32 only
+ * (block-scaled inputs: GDN_ERR_UNSUPPORTED).  Sizes are 0 for an invalid
+ * descriptor and when there is nothing to save (F == 0 or no (b, h) units). */
+size_t gdn_saved_size(const gdn_desc* d);
+size_t gdn_workspace_size_bwd_saved(const gdn_desc* d);
+gdn_status gdn_frame_scan_fwd_save(const gdn_desc* d,
+                                   const void* q, const void* k, const void* v,
+                                   const float* beta, const float* alpha,
+                                   const float* S0,
+                                   void* o, float* S_final,
+                                   void* saved, size_t saved_bytes,
+                                   void* stream);
+gdn_status gdn_frame_scan_bwd_saved(const gdn_desc* d,
+                                    const void* q, const void* k, const void* v,
+                                    const float* beta, const float* alpha,
+                                    const void* dO, const float* dS_final,
+                                    void* dq, void* dk, void* dv,
+                                    float* dbeta, float* dalpha, float* dS0,
+                                    const void* saved, size_t saved_bytes,
+                                    void* workspace, size_t workspace_bytes,
+                                    void* stream);
 
 /* ---------------------------------------------------------- block projections
  * The steps either side of the scan inside a GDN block ("NVIDIA's New 2.6B

@@ -343,3 +343,71 @@ def test_block_pointer_checks(lib):
     assert call_out(lib, d, y=BP["o"]) == ALIAS
     assert call_out(lib, d, y=BP["ws"] + 4096) == ALIAS
     assert call_out(lib, d, ws_bytes=need - 1) == WORKSPACE
+
+
+# ------------------------------------------------------------ saved states
+def test_saved_sizes(lib):
+    d = desc(B=2, H=3, F=5, N=7, D=64)
+    item = 10 * 64 * 64                                   # bf16 item: Gm, U, S planes
+    per_set = (2 * 3 * 5 * item + 255) // 256 * 256       # one chunk of items
+    state = (2 * 3 * 64 * 64 * 4 + 255) // 256 * 256
+    rho = (2 * 5 * 7 * 3 * 4 + 255) // 256 * 256
+    assert lib.gdn_saved_size(ctypes.byref(d)) == per_set + state + rho
+    assert lib.gdn_workspace_size_bwd_saved(ctypes.byref(d)) == per_set + state
+    # two chunks of at most 256 frames: two item sets and two entering states
+    d = desc(B=1, H=2, F=300, N=5, D=16)
+    item16 = lib.gdn_saved_size(ctypes.byref(desc(B=1, H=1, F=1, N=0, D=16))) - 16 * 16 * 4
+    assert item16 > 0
+    s2 = lib.gdn_saved_size(ctypes.byref(d))
+    assert s2 == 2 * ((2 * 256 * item16 + 255) // 256 * 256) + 2 * ((2 * 16 * 16 * 4 + 255) // 256 * 256) + \
+        (300 * 5 * 2 * 4 + 255) // 256 * 256
+    assert lib.gdn_saved_size(ctypes.byref(desc(F=0))) == 0
+    assert lib.gdn_saved_size(ctypes.byref(desc(io=_lib.GDN_FP8_E4M3, D=32))) == 0
+    assert lib.gdn_saved_size(None) == 0
+
+
+SV = {n: BASE + i * (1 << 32) for i, n in enumerate(["q", "k", "v", "beta", "alpha", "S0", "o", "S_final", "saved",
+                                                       "dO", "dS", "dq", "dk", "dv", "db", "da", "dS0", "ws"])}
+
+
+def call_save(lib, d, sv_bytes=1 << 40, **over):
+    p = dict(SV)
+    p.update(over)
+    return lib.gdn_frame_scan_fwd_save(None if d is None else ctypes.byref(d),
+                                       *[p[n] for n in ["q", "k", "v", "beta", "alpha", "S0", "o", "S_final", "saved"]],
+                                       ctypes.c_size_t(sv_bytes), None)
+
+
+def call_bwd_saved(lib, d, sv_bytes=1 << 40, ws_bytes=1 << 40, **over):
+    p = dict(SV)
+    p.update(over)
+    return lib.gdn_frame_scan_bwd_saved(None if d is None else ctypes.byref(d),
+                                        *[p[n] for n in ["q", "k", "v", "beta", "alpha", "dO", "dS", "dq", "dk", "dv",
+                                                         "db", "da", "dS0", "saved"]],
+                                        ctypes.c_size_t(sv_bytes), p["ws"], ctypes.c_size_t(ws_bytes), None)
+
+
+def test_saved_entry_checks(lib):
+    d = desc()
+    need = lib.gdn_saved_size(ctypes.byref(d))
+    assert call_save(lib, None) == INVALID
+    assert call_save(lib, desc(io=_lib.GDN_FP8_E4M3, D=32)) == UNSUPPORTED
+    assert call_save(lib, d, saved=None) == WORKSPACE
+    assert call_save(lib, d, sv_bytes=need - 1) == WORKSPACE
+    assert call_save(lib, d, saved=SV["saved"] + 16) == ALIGN
+    assert call_save(lib, d, q=None) == INVALID
+    assert call_save(lib, d, o=SV["o"] + 8) == ALIGN
+    assert call_save(lib, d, saved=SV["q"]) == ALIAS
+    assert call_save(lib, d, o=SV["saved"] + 4096) == ALIAS
+    assert call_save(lib, d, S_final=SV["saved"]) == ALIAS
+    assert call_bwd_saved(lib, None) == INVALID
+    assert call_bwd_saved(lib, desc(io=_lib.GDN_FP8_E4M3, D=32)) == UNSUPPORTED
+    assert call_bwd_saved(lib, d, saved=None) == WORKSPACE
+    assert call_bwd_saved(lib, d, sv_bytes=need - 1) == WORKSPACE
+    wneed = lib.gdn_workspace_size_bwd_saved(ctypes.byref(d))
+    assert call_bwd_saved(lib, d, ws_bytes=wneed - 1) == WORKSPACE
+    assert call_bwd_saved(lib, d, ws=None) == WORKSPACE
+    assert call_bwd_saved(lib, d, saved=SV["saved"] + 16) == ALIGN
+    assert call_bwd_saved(lib, d, dq=SV["saved"]) == ALIAS          # saved is an input
+    assert call_bwd_saved(lib, d, ws=SV["saved"] + 256) == ALIAS
+    assert call_bwd_saved(lib, d, dk=SV["q"]) == ALIAS
