@@ -6,7 +6,7 @@ workloads and is importable without a GPU.
 """
 from . import inputs  # noqa: F401
 
-__all__ = ["frame_scan_fwd", "frame_scan_fwd_static", "frame_scan_fwd_fp8", "frame_scan_bwd", "frame_scan_fwd_save", "frame_step", "block_in_proj", "block_out_proj", "profile_begin", "profile_end", "workspace_size",
+__all__ = ["frame_scan", "frame_scan_fwd", "frame_scan_fwd_static", "frame_scan_fwd_fp8", "frame_scan_bwd", "frame_scan_fwd_save", "frame_step", "block_in_proj", "block_out_proj", "profile_begin", "profile_end", "workspace_size",
            "make_desc", "GdnError", "inputs"]
 
 
@@ -17,6 +17,9 @@ def __getattr__(name):
                 "workspace_size", "make_desc", "alloc_workspace"):
         from . import api
         return getattr(api, name)
+    if name == "frame_scan":
+        from .autograd import frame_scan
+        return frame_scan
     if name == "GdnError":
         from ._lib import GdnError
         return GdnError
