@@ -1018,12 +1018,17 @@ __global__ __launch_bounds__(256, 1) void state_scan_kernel(ScanArgs a) {   // N
         frag gm[C::KS][C::BPW];
         f32x4 u[C::BPW];
     };
-    auto load_ops = [&](int fl, Ops& o) {             // fl is always a valid step
+    // loads [j0, j1) of a frame's operands, in the order Gm^T fragments
+    // (kk, q), then U blocks q: the recurrence issues them in three groups
+    // spread over a step
+    constexpr int NOPS = C::KS * C::BPW + C::BPW;
+    auto load_ops = [&](int fl, Ops& o, int j0, int j1) {   // fl is always a valid step
         const uint32_t base = (uint32_t)phys(fl) * (uint32_t)W::item_bytes;
 #pragma unroll
         for (int kk = 0; kk < C::KS; ++kk)
 #pragma unroll
             for (int q = 0; q < C::BPW; ++q) {
+                if (kk * C::BPW + q < j0 || kk * C::BPW + q >= j1) continue;
                 const int jb = c * C::BPW + q;
                 const uint32_t off = base + (uint32_t)(W::gm_off + (size_t)(jb * C::KS + kk) * W::FRAG);
                 if constexpr (C::B16) {
@@ -1039,6 +1044,7 @@ __global__ __launch_bounds__(256, 1) void state_scan_kernel(ScanArgs a) {   // N
         const uint32_t ubase = !BWD ? base : (fl + 1 < Fc ? (uint32_t)phys(fl + 1) * (uint32_t)W::item_bytes : 0x80000000u);
 #pragma unroll
         for (int q = 0; q < C::BPW; ++q) {
+            if (C::KS * C::BPW + q < j0 || C::KS * C::BPW + q >= j1) continue;
             const int jb = c * C::BPW + q;
             o.u[q] = __builtin_bit_cast(
                 f32x4, __builtin_amdgcn_raw_buffer_load_b128(
@@ -1077,7 +1083,13 @@ __global__ __launch_bounds__(256, 1) void state_scan_kernel(ScanArgs a) {   // N
         frag bs[C::KS];
 #pragma unroll
         for (int kk = 0; kk < C::KS; ++kk) bs[kk] = get_x(xb, kk);
-        if (reload) load_ops(nx, prev);                 // the slot frame fl-1 used
+        // the slot frame fl-1 used takes frame nx, in three groups of loads
+        // (at the start, after the encoding, after the products): issued
+        // together, the four waves' loads back up the CU's memory pipeline
+        // and stall the step's critical path at issue (78.0 against 83.4 us
+        // at the full-minute shape; a group just before the barrier delays
+        // the barrier instead)
+        if (reload) load_ops(nx, prev, 0, NOPS / 3);
         // the state entering step fl, its bf16 fragment (the one exchanged:
         // bs[c]) and remainder codes, encoded while the exchange reads are in
         // flight and stored after the products are issued (measured 81.9
@@ -1086,6 +1098,8 @@ __global__ __launch_bounds__(256, 1) void state_scan_kernel(ScanArgs a) {   // N
         const f32x4 e0 = S[0], e1 = C::BPW > 1 ? S[C::BPW - 1] : f32x4{0, 0, 0, 0};
         const frag ehi = own_frag();
         const u32x2 ecodes = encode(ehi, e0, e1);
+        __builtin_amdgcn_sched_barrier(0);
+        if (reload) load_ops(nx, prev, NOPS / 3, 2 * NOPS / 3);
         __builtin_amdgcn_sched_barrier(0);
         const float al = sAlpha[fl];
         f32x4 acc[C::BPW];
@@ -1106,6 +1120,7 @@ __global__ __launch_bounds__(256, 1) void state_scan_kernel(ScanArgs a) {   // N
                 }
                 io::mma(acc[q], ga, bs[kk]);            // (S Gm)^T += Gm^T S^T
             }
+        if (reload) load_ops(nx, prev, 2 * NOPS / 3, NOPS);
         store_state(BWD ? fl : fl - 1, ehi, e0, e1, ecodes);
 #pragma unroll
         for (int q = 0; q < C::BPW; ++q) S[q] = acc[q];
@@ -1118,7 +1133,7 @@ __global__ __launch_bounds__(256, 1) void state_scan_kernel(ScanArgs a) {   // N
     Ops ring[C::PD];
 #pragma unroll
     for (int j = 0; j < C::PD - 1; ++j) {
-        load_ops(j < Fc ? j : Fc - 1, ring[j]);
+        load_ops(j < Fc ? j : Fc - 1, ring[j], 0, NOPS);
         __builtin_amdgcn_sched_barrier(0);              // keep the frames in issue order
     }
     __syncthreads();                                    // alphas and S_0 fragments staged
