@@ -216,6 +216,12 @@ int gdn_oracle_scan_bwd(int B, int H, int F, int N, int Dk, int Dv,
         return -1;
     const size_t sB = (size_t)F * N * H, sF = (size_t)N * H, sN = (size_t)H;
     const size_t SS = (size_t)Dv * Dk;
+    int status = 0;
+    /* The (b, h) units are independent: each thread takes whole units, with
+     * scratch of its own; the arithmetic of a unit is the same as in a plain
+     * loop over the units. */
+#pragma omp parallel
+    {
     double *Sall = (double *)malloc(sizeof(double) * SS * ((size_t)F + 1));
     double *G = (double *)malloc(sizeof(double) * (size_t)Dk * Dk);
     double *U = (double *)malloc(sizeof(double) * SS);
@@ -227,14 +233,16 @@ int gdn_oracle_scan_bwd(int B, int H, int F, int N, int Dk, int Dv,
     double *nrm = (double *)malloc(sizeof(double) * ((size_t)N + 1));
     double *bt = (double *)malloc(sizeof(double) * ((size_t)N + 1));
     double *dkh = (double *)malloc(sizeof(double) * ((size_t)Dk + 1));
-    if (!Sall || !G || !U || !T || !Dm || !Dn || !dG || !kh || !nrm || !bt || !dkh) {
-        free(Sall); free(G); free(U); free(T); free(Dm); free(Dn); free(dG);
-        free(kh); free(nrm); free(bt); free(dkh);
-        return -2;
+    const int ok = Sall && G && U && T && Dm && Dn && dG && kh && nrm && bt && dkh;
+    if (!ok) {
+#pragma omp atomic write
+        status = -2;
     }
 
+#pragma omp for collapse(2) schedule(dynamic)
     for (int b = 0; b < B; ++b) {
         for (int h = 0; h < H; ++h) {
+            if (!ok) continue;
             /* ---- forward, keeping every state: Sall[s] is the state after step s */
             for (size_t x = 0; x < SS; ++x)
                 Sall[x] = S0 ? S0[((size_t)b * H + h) * SS + x] : 0.0;
@@ -388,5 +396,6 @@ int gdn_oracle_scan_bwd(int B, int H, int F, int N, int Dk, int Dv,
     }
     free(Sall); free(G); free(U); free(T); free(Dm); free(Dn); free(dG);
     free(kh); free(nrm); free(bt); free(dkh);
-    return 0;
+    }
+    return status;
 }

@@ -12,7 +12,8 @@ M + M^T) enters as a high and a low bf16 part, so the products add no more.
 Measured worst cases: 2.7e-3 (dalpha) in bf16 and 8e-7 in fp32.
 Cases span several 64-token blocks with ragged tails, every supported D, both
 directions, gate logits, unnormalised keys, a zero key (the eps branch of the
-key normalisation), no tokens, one frame and more than one launch chunk.
+key normalisation), no tokens, one frame, more than one launch chunk and
+every unit of the full-minute workload.
 """
 import numpy as np
 import pytest
@@ -185,16 +186,18 @@ def test_bitwise_reproducible():
         assert np.array_equal(x, y), name
 
 
-@pytest.mark.parametrize("seed", [0])
-def test_full_minute_sampled_units(seed):
-    """The full-minute workload (B1 H16 F121 N880 d128 bf16) in one launch;
-    the oracle runs three of its (b, h) units (units are independent)."""
-    w = inputs.make_config("full_minute", seed=seed)
-    dO, dS = inputs.make_grads(w, seed=seed)
+def test_full_minute_every_unit():
+    """The full-minute workload (B1 H16 F121 N880 d128 bf16) in one launch, every
+    gradient of every (b, h) unit against the oracle (each unit must meet the
+    bar on its own, so that a wrong unit mapping cannot hide in a whole-tensor
+    norm)."""
+    w = inputs.make_config("full_minute", seed=0)
+    dO, dS = inputs.make_grads(w, seed=0)
     got = run_bwd(w, dO, dS)
-    for h in (0, 7, 15):
+    ref = oracle.scan_bwd(w.q, w.k, w.v, w.beta, w.alpha, None, dO, dS)
+    compare(got, ref, "bf16", "full_minute")
+    for h in range(w.H):
         sl = (slice(0, 1), slice(None), slice(None), slice(h, h + 1))
-        ref = oracle.scan_bwd(w.q[sl], w.k[sl], w.v[sl], w.beta[sl], w.alpha[:, :, h:h + 1], None, dO[sl],
-                              dS[:, h:h + 1])
         mine = [got[0][sl], got[1][sl], got[2][sl], got[3][sl], got[4][:, :, h:h + 1], got[5][:, h:h + 1]]
-        compare(mine, ref, "bf16", "full_minute unit h=%d" % h)
+        theirs = [ref[0][sl], ref[1][sl], ref[2][sl], ref[3][sl], ref[4][:, :, h:h + 1], ref[5][:, h:h + 1]]
+        compare(mine, theirs, "bf16", "full_minute unit h=%d" % h)
