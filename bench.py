@@ -8,8 +8,8 @@ roofline of the dominant kernel (HIP events recorded by the library around
 every launch in a second timed region of K steps), and the fp64 CPU oracle
 timed on a bounded sample of the same workload; also the per-step GPU time of
 gdn_frame_step at the streaming workload's shape and the backward pass
-(gdn_frame_scan_bwd) and of the block-scaled FP8 input mode
-(gdn_frame_scan_fwd_fp8) on the same workload.
+(gdn_frame_scan_bwd) and of the block-scaled input modes
+(gdn_frame_scan_fwd_fp8, gdn_frame_scan_fwd_fp4) on the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload full_minute]
 """
@@ -353,23 +353,26 @@ def saved_states(w, q, k, v, beta, alpha, S0, dO, dS, steps: int, warmup: int, r
             "timing": "HIP events around %d calls of each" % steps}
 
 
-def fp8_inputs(w, q, k, v, beta, alpha, S0, steps: int, warmup: int, flush_buf, bf16_ms: float):
-    """gdn_frame_scan_fwd_fp8 on the workload with q, k and v encoded as MXFP8
-    on the device (E4M3 values, one E8M0 scale per 32 features); o in bf16.
-    Algorithmic bytes: q, k, v at one byte per value plus their scales, beta,
-    alpha and S0 read once, o (bf16) and S_final written once."""
+def mx_inputs(fmt: str, w, q, k, v, beta, alpha, S0, steps: int, warmup: int, flush_buf, bf16_ms: float):
+    """gdn_frame_scan_fwd_fp8 (fmt "fp8") or gdn_frame_scan_fwd_fp4 (fmt
+    "fp4") on the workload with q, k and v encoded on the device in the OCP
+    microscaling layout (E4M3 or E2M1 values, one E8M0 scale per 32
+    features); o in bf16.  Algorithmic bytes: q, k, v at one byte (fp8) or
+    half a byte (fp4) per value plus their scales, beta, alpha and S0 read
+    once, o (bf16) and S_final written once."""
     import torch
     from gated_deltanet_scan_amd import api, inputs
-    enc = [inputs.to_mxfp8_device(x) for x in (q, k, v)]
+    enc = [(inputs.to_mxfp8_device if fmt == "fp8" else inputs.to_mxfp4_device)(x) for x in (q, k, v)]
+    fn = api.frame_scan_fwd_fp8 if fmt == "fp8" else api.frame_scan_fwd_fp4
     o = torch.empty((w.B, w.F, w.N, w.H, w.Dv), dtype=torch.bfloat16, device="cuda")
     S_final = torch.empty((w.B, w.H, w.Dv, w.Dk), dtype=torch.float32, device="cuda")
-    desc = api.make_desc(w.B, w.H, w.F, w.N, w.Dk, torch.float8_e4m3fn)
-    ws = api.alloc_workspace(desc, q.device)
+    desc = api.make_desc(w.B, w.H, w.F, w.N, w.Dk, torch.bfloat16)
+    ws = api.alloc_workspace(desc, q.device)          # the same size in every input format
     stream = torch.cuda.current_stream()
 
     def step():
-        api.frame_scan_fwd_fp8(enc[0][0], enc[0][1], enc[1][0], enc[1][1], enc[2][0], enc[2][1], beta, alpha, S0,
-                               o=o, S_final=S_final, workspace=ws, stream=stream)
+        fn(enc[0][0], enc[0][1], enc[1][0], enc[1][1], enc[2][0], enc[2][1], beta, alpha, S0,
+           o=o, S_final=S_final, workspace=ws, stream=stream)
 
     for _ in range(warmup):
         step()
@@ -401,11 +404,13 @@ def fp8_inputs(w, q, k, v, beta, alpha, S0, steps: int, warmup: int, flush_buf, 
     ms = gpu_ms / steps
     tok = w.B * w.F * w.N * w.H
     state = w.B * w.H * w.Dv * w.Dk * 4
-    nbytes = 3 * tok * w.Dk + 3 * tok * (w.Dk // 32) + tok * w.Dv * 2 + tok * 4 + w.B * w.F * w.H * 4 + 2 * state
+    code_bytes = 3 * tok * w.Dk if fmt == "fp8" else 3 * tok * w.Dk // 2
+    nbytes = code_bytes + 3 * tok * (w.Dk // 32) + tok * w.Dv * 2 + tok * 4 + w.B * w.F * w.H * 4 + 2 * state
     gbs = nbytes / (ms * 1e-3) / 1e9
     kernels = {name: {"avg_ms": round(t / n, 5), "launches_per_step": n / steps}
                for name, (t, n) in kern.items() if n > 0}
-    return {"workload": "the same workload, q/k/v as MXFP8 (E4M3, E8M0 scale per 32 features), o bf16",
+    name = "MXFP8 (E4M3" if fmt == "fp8" else "MXFP4 (E2M1, two per byte"
+    return {"workload": "the same workload, q/k/v as %s, E8M0 scale per 32 features), o bf16" % name,
             "ms_per_step": round(ms, 5), "tokens_per_s": round(w.B * w.F * w.N / (ms * 1e-3), 1),
             "speedup_vs_bf16": round(bf16_ms / ms, 3), "alg_bytes_per_step": nbytes,
             "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "kernels": kernels,
@@ -501,7 +506,7 @@ def main():
     ap.add_argument("--bwd-steps", type=int, default=20,
                     help="timed calls of the backward pass (0: skip)")
     ap.add_argument("--fp8-steps", type=int, default=20,
-                    help="timed calls of the block-scaled FP8 input mode (0: skip)")
+                    help="timed calls of each block-scaled input mode, MXFP8 and MXFP4 (0: skip)")
     ap.add_argument("--block-steps", type=int, default=10,
                     help="timed calls of the block around the scan: projections at model width "
                          "--block-width, the scan, the output projection (0: skip)")
@@ -643,9 +648,10 @@ def main():
     }
     line["backward"] = (backward(w, q, k, v, beta, alpha, S0, args.bwd_steps, min(args.warmup, 5), junk)
                         if args.bwd_steps > 0 else None)
-    line["fp8_inputs"] = (fp8_inputs(w, q, k, v, beta, alpha, S0, args.fp8_steps, min(args.warmup, 5), junk,
-                                     ms_per_step)
-                          if args.fp8_steps > 0 and w.Dk % 32 == 0 and w.dtype == "bf16" else None)
+    for fmt in ("fp8", "fp4"):
+        line[fmt + "_inputs"] = (mx_inputs(fmt, w, q, k, v, beta, alpha, S0, args.fp8_steps, min(args.warmup, 5),
+                                           junk, ms_per_step)
+                                 if args.fp8_steps > 0 and w.Dk % 32 == 0 and w.dtype == "bf16" else None)
     line["block"] = (block_projections(w, args.block_steps, min(args.warmup, 3), args.block_width, args.seed)
                      if args.block_steps > 0 and w.dtype == "bf16" else None)
     line["streaming_step"] = streaming_step(args.stream_frames) if args.stream_frames > 0 else None

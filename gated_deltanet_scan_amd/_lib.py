@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(_PKG, "libgdn.so")
 GDN_BF16 = 0
 GDN_F32 = 1
 GDN_FP8_E4M3 = 2
+GDN_FP4_E2M1 = 3
 GDN_FLAG_GATES_ARE_LOGITS = 0x1
 GDN_FLAG_NO_KEY_NORM = 0x2
 GDN_FLAG_REVERSE = 0x4
@@ -80,6 +81,8 @@ def load():
     lib.gdn_frame_scan_bwd_saved.restype = ctypes.c_int
     lib.gdn_frame_scan_fwd_fp8.argtypes = [dp, vp, vp, vp, vp, vp, vp, fp, fp, fp, vp, fp, vp, sz, vp]
     lib.gdn_frame_scan_fwd_fp8.restype = ctypes.c_int
+    lib.gdn_frame_scan_fwd_fp4.argtypes = [dp, vp, vp, vp, vp, vp, vp, fp, fp, fp, vp, fp, vp, sz, vp]
+    lib.gdn_frame_scan_fwd_fp4.restype = ctypes.c_int
     lib.gdn_block_workspace_size.argtypes = [dp, ctypes.c_int32]
     lib.gdn_block_workspace_size.restype = sz
     lib.gdn_block_in_proj.argtypes = [dp, ctypes.c_int32, vp, vp, vp, vp, vp, vp, fp, fp, vp, sz, vp]

@@ -205,6 +205,54 @@ def frame_scan_fwd_fp8(q, q_scale, k, k_scale, v, v_scale, beta, alpha, S0=None,
     return o, S_final
 
 
+def frame_scan_fwd_fp4(q, q_scale, k, k_scale, v, v_scale, beta, alpha, S0=None, *,
+                       gates_are_logits: bool = False, eps: float = 1e-6, normalize_keys: bool = True,
+                       reverse: bool = False, o=None, S_final=None, workspace=None,
+                       return_state: bool = True, stream=None):
+    """frame_scan_fwd on block-scaled FP4 inputs (OCP MXFP4, E2M1 elements).
+
+    q, k, v: [B,F,N,H,D/2] torch.uint8, two E2M1 codes per byte (feature 2j
+    in the lower four bits of byte j); q_scale, k_scale, v_scale:
+    [B,F,N,H,D/32] torch.uint8 E8M0 exponents; D in {32, 64, 128}.  Returns
+    (o [B,F,N,H,D] bfloat16, S_final fp32 or None).
+    """
+    B, F, N, H, D2 = q.shape
+    D = 2 * D2
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check(t, name, torch.uint8, (B, F, N, H, D2))
+    nb = D // 32
+    for name, t in (("q_scale", q_scale), ("k_scale", k_scale), ("v_scale", v_scale)):
+        _check(t, name, torch.uint8, (B, F, N, H, nb))
+    _check(beta, "beta", torch.float32, (B, F, N, H))
+    _check(alpha, "alpha", torch.float32, (B, F, H))
+    if S0 is not None:
+        _check(S0, "S0", torch.float32, (B, H, D, D))
+    if o is not None:
+        _check(o, "o", torch.bfloat16, (B, F, N, H, D))
+    if S_final is not None:
+        _check(S_final, "S_final", torch.float32, (B, H, D, D))
+    _check_workspace(workspace, q.device)
+    desc = make_desc(B, H, F, N, D, torch.bfloat16, gates_are_logits=gates_are_logits, eps=eps,
+                     normalize_keys=normalize_keys, reverse=reverse)
+    desc.io_dtype = _lib.GDN_FP4_E2M1
+    stream = _launch_stream(stream, q.device)
+    with torch.cuda.stream(stream):   # allocations belong to the launch stream
+        if o is None:
+            o = torch.empty((B, F, N, H, D), dtype=torch.bfloat16, device=q.device)
+        if S_final is None and return_state:
+            S_final = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
+        if workspace is None:
+            workspace = alloc_workspace(desc, q.device)
+        ws_bytes = 0 if workspace is None else workspace.numel()
+        st = _lib.load().gdn_frame_scan_fwd_fp4(
+            ctypes.byref(desc), _ptr(q), _ptr(q_scale), _ptr(k), _ptr(k_scale), _ptr(v), _ptr(v_scale),
+            _ptr(beta), _ptr(alpha), _ptr(S0), _ptr(o), _ptr(S_final), _ptr(workspace),
+            ctypes.c_size_t(ws_bytes), ctypes.c_void_p(stream.cuda_stream))
+    if st != 0:
+        raise GdnError(st, "gdn_frame_scan_fwd_fp4")
+    return o, S_final
+
+
 def frame_step(q, k, v, beta, alpha, S_in=None, *, gates_are_logits: bool = False,
                eps: float = 1e-6, normalize_keys: bool = True, o=None, S_out=None, workspace=None, stream=None):
     """One frame of the scan for streaming use.

@@ -133,14 +133,15 @@ bool dim_ok(int D) { return D == 16 || D == 32 || D == 64 || D == 128; }
 gdn_status check_desc(const gdn_desc* d, bool step, Plan* p, int fc_cap = gdn::kMaxChunkFrames) {
     if (!d) return GDN_ERR_INVALID_ARG;
     if (d->B < 0 || d->H < 0 || d->F < 0 || d->N < 0) return GDN_ERR_INVALID_ARG;
-    if (d->io_dtype != GDN_BF16 && d->io_dtype != GDN_F32 && d->io_dtype != GDN_FP8_E4M3) return GDN_ERR_INVALID_ARG;
+    const bool mx = d->io_dtype == GDN_FP8_E4M3 || d->io_dtype == GDN_FP4_E2M1;   // block-scaled inputs
+    if (d->io_dtype != GDN_BF16 && d->io_dtype != GDN_F32 && !mx) return GDN_ERR_INVALID_ARG;
     if ((d->flags & ~(GDN_FLAG_GATES_ARE_LOGITS | GDN_FLAG_NO_KEY_NORM | GDN_FLAG_REVERSE)) != 0)
         return GDN_ERR_INVALID_ARG;
     if (!(d->eps > 0.0f) || !isfinite(d->eps)) return GDN_ERR_INVALID_ARG;
     if (step && d->F != 1) return GDN_ERR_INVALID_ARG;
     if (d->Dk < 1 || d->Dv < 1) return GDN_ERR_INVALID_ARG;
     if (d->Dk != d->Dv || !dim_ok(d->Dk)) return GDN_ERR_UNSUPPORTED;
-    if (d->io_dtype == GDN_FP8_E4M3 && d->Dk < gdn::kMxBlock) return GDN_ERR_UNSUPPORTED;   // one scale block
+    if (mx && d->Dk < gdn::kMxBlock) return GDN_ERR_UNSUPPORTED;   // one scale block
     // element counts must fit comfortably in 64-bit byte offsets, and one
     // frame of one tensor in the 32-bit offsets of a buffer resource
     const double tok = (double)d->B * d->F * d->N * d->H * d->Dk;
@@ -153,7 +154,7 @@ gdn_status check_desc(const gdn_desc* d, bool step, Plan* p, int fc_cap = gdn::k
     // frames per launch chunk (state_scan stages the chunk's gates in LDS)
     p->Fc = d->F < fc_cap ? d->F : fc_cap;
     p->item_bytes = gdn::ws_item_bytes(p->esz, p->D);
-    if (d->F == 1 && d->io_dtype != GDN_FP8_E4M3) {   // (block-scaled inputs take the scan path)
+    if (d->F == 1 && !mx) {   // (block-scaled inputs take the scan path)
         int tpart = 0;
         step_ranges(p->units, d->N, gram_stage_tokens(p->esz, p->D), kSizingCUs, &p->parts_max, &tpart);
         p->scopy_off = ((size_t)p->units * p->parts_max * gdn::part_bytes(p->D) + 255) / 256 * 256;
@@ -385,7 +386,8 @@ gdn_status run(const gdn_desc* d, bool step, const void* q, const void* k, const
     }
     gdn_status st = check_desc(d, step, &p, fc_cap);
     if (st != GDN_OK) return st;
-    if (d->io_dtype == GDN_FP8_E4M3) return GDN_ERR_INVALID_ARG;   // needs the scales: gdn_frame_scan_fwd_fp8
+    if (d->io_dtype == GDN_FP8_E4M3 || d->io_dtype == GDN_FP4_E2M1)
+        return GDN_ERR_INVALID_ARG;   // needs the scales: gdn_frame_scan_fwd_fp8 / _fp4
     if (static_ws) {
         if (p.ws_bytes > kScratchBytes) return GDN_ERR_WORKSPACE;
         workspace = nullptr;
@@ -484,20 +486,26 @@ gdn_status run(const gdn_desc* d, bool step, const void* q, const void* k, const
 }
 
 // ---------------------------------------------------------------- block-scaled inputs
-template <int D>
-gdn_status launch_fp8(const Plan& p, const ScanArgs& a, hipStream_t s, int cus, float* carry) {
-    return launch_all<gdn::fp8e4m3, D>(p, a, s, cus, carry);
+template <typename TIN>
+gdn_status launch_mx(const Plan& p, const ScanArgs& a, hipStream_t s, int cus, float* carry) {
+    switch (p.D) {
+        case 32: return launch_all<TIN, 32>(p, a, s, cus, carry);
+        case 64: return launch_all<TIN, 64>(p, a, s, cus, carry);
+        case 128: return launch_all<TIN, 128>(p, a, s, cus, carry);
+        default: return GDN_ERR_UNSUPPORTED;
+    }
 }
 
-gdn_status run_fp8(const gdn_desc* d, const void* q, const uint8_t* qs, const void* k, const uint8_t* ks,
-                   const void* v, const uint8_t* vs, const float* beta, const float* alpha, const float* S0, void* o,
-                   float* S_final, void* workspace, size_t workspace_bytes, void* stream_v) {
+// Block-scaled inputs: want is GDN_FP8_E4M3 or GDN_FP4_E2M1 (the entry point's format).
+gdn_status run_mx(int want, const gdn_desc* d, const void* q, const uint8_t* qs, const void* k, const uint8_t* ks,
+                  const void* v, const uint8_t* vs, const float* beta, const float* alpha, const float* S0, void* o,
+                  float* S_final, void* workspace, size_t workspace_bytes, void* stream_v) {
     Plan p;
     gdn_status st = check_desc(d, false, &p);
     if (st != GDN_OK) return st;
-    if (d->io_dtype != GDN_FP8_E4M3) return GDN_ERR_INVALID_ARG;
+    if (d->io_dtype != want) return GDN_ERR_INVALID_ARG;
     const size_t ntok = (size_t)d->B * d->F * d->N * d->H;
-    const size_t in_bytes = ntok * (size_t)p.D;                       // one byte per value
+    const size_t in_bytes = want == GDN_FP8_E4M3 ? ntok * (size_t)p.D : ntok * (size_t)p.D / 2;   // 8 or 4 bits
     const size_t sc_bytes = ntok * (size_t)(p.D / gdn::kMxBlock);     // one E8M0 byte per 32 values
     const size_t o_bytes = ntok * (size_t)p.D * 2;                    // bf16
     const size_t beta_bytes = ntok * sizeof(float);
@@ -564,12 +572,8 @@ gdn_status run_fp8(const gdn_desc* d, const void* q, const uint8_t* qs, const vo
     a.parts = 1;
     a.tpart = d->N;
     float* carry = S_final ? S_final : reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + p.carry_off);
-    switch (p.D) {
-        case 32: return launch_fp8<32>(p, a, stream, cus, carry);
-        case 64: return launch_fp8<64>(p, a, stream, cus, carry);
-        case 128: return launch_fp8<128>(p, a, stream, cus, carry);
-        default: return GDN_ERR_UNSUPPORTED;
-    }
+    return want == GDN_FP8_E4M3 ? launch_mx<gdn::fp8e4m3>(p, a, stream, cus, carry)
+                                : launch_mx<gdn::fp4e2m1>(p, a, stream, cus, carry);
 }
 
 // ---------------------------------------------------------------- backward pass
@@ -599,7 +603,7 @@ gdn_status check_bwd(const gdn_desc* d, BwdPlan* bp, bool saved = false) {
     Plan& p = bp->p;
     gdn_status st = check_desc(d, false, &p);
     if (st != GDN_OK) return st;
-    if (d->io_dtype == GDN_FP8_E4M3) return GDN_ERR_UNSUPPORTED;
+    if (d->io_dtype == GDN_FP8_E4M3 || d->io_dtype == GDN_FP4_E2M1) return GDN_ERR_UNSUPPORTED;
     bp->nchunks = d->F > 0 ? (d->F + p.Fc - 1) / p.Fc : 0;
     const size_t set = round256((size_t)p.units * p.Fc * p.item_bytes);
     bp->set = set;
@@ -997,8 +1001,16 @@ gdn_status gdn_frame_scan_fwd_fp8(const gdn_desc* d, const void* q, const uint8_
                                   const uint8_t* k_scale, const void* v, const uint8_t* v_scale, const float* beta,
                                   const float* alpha, const float* S0, void* o, float* S_final, void* workspace,
                                   size_t workspace_bytes, void* stream) {
-    return run_fp8(d, q, q_scale, k, k_scale, v, v_scale, beta, alpha, S0, o, S_final, workspace, workspace_bytes,
-                   stream);
+    return run_mx(GDN_FP8_E4M3, d, q, q_scale, k, k_scale, v, v_scale, beta, alpha, S0, o, S_final, workspace,
+                  workspace_bytes, stream);
+}
+
+gdn_status gdn_frame_scan_fwd_fp4(const gdn_desc* d, const void* q, const uint8_t* q_scale, const void* k,
+                                  const uint8_t* k_scale, const void* v, const uint8_t* v_scale, const float* beta,
+                                  const float* alpha, const float* S0, void* o, float* S_final, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+    return run_mx(GDN_FP4_E2M1, d, q, q_scale, k, k_scale, v, v_scale, beta, alpha, S0, o, S_final, workspace,
+                  workspace_bytes, stream);
 }
 
 gdn_status gdn_frame_step(const gdn_desc* d, const void* q, const void* k, const void* v,

@@ -157,17 +157,35 @@ __device__ __forceinline__ void bstore16(rsrc_t r, uint32_t off, u32x4 v) {
 // 2^(e - 127) (the OCP microscaling "MXFP8" layout), and the kernels turn
 // them into bf16 on load (exact: an E4M3 value times a power of two fits
 // bf16), so everything after the load, the output included, is the bf16 mode.
+// fp4e2m1 is the same layout with OCP FP4 E2M1 values, two per byte (the
+// lower four bits hold the feature of even index): the "MXFP4" layout.
 struct fp8e4m3 {
     uint8_t bits;
 };
+struct fp4e2m1 {
+    uint8_t bits;                                      // two values
+};
 template <typename T> struct Elem {
     using C = T;                                       // compute (and output) type
-    static constexpr int GB = sizeof(T);               // bytes per input element in HBM
+    static constexpr int G2 = 2 * (int)sizeof(T);      // half-bytes per input element in HBM
 };
 template <> struct Elem<fp8e4m3> {
     using C = uint16_t;
-    static constexpr int GB = 1;
+    static constexpr int G2 = 2;
 };
+template <> struct Elem<fp4e2m1> {
+    using C = uint16_t;
+    static constexpr int G2 = 1;
+};
+// Bytes of n input elements (n even) and the address of element n of a tensor.
+template <typename TIN>
+__device__ __forceinline__ constexpr size_t elem_bytes(size_t n) {
+    return n * Elem<TIN>::G2 / 2;
+}
+template <typename TIN>
+__device__ __forceinline__ const unsigned char* elem_ptr(const void* p, size_t n) {
+    return static_cast<const unsigned char*>(p) + elem_bytes<TIN>(n);
+}
 constexpr int kMxBlock = 32;                           // features per E8M0 scale
 // Eight E4M3 values (two dwords) times 2^(e - 127), as eight bf16 values.
 __device__ __forceinline__ u32x4 mx_to_bf16(u32x2 raw, uint32_t e) {
@@ -176,6 +194,15 @@ __device__ __forceinline__ u32x4 mx_to_bf16(u32x2 raw, uint32_t e) {
                  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[0], sc, true)),
                  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[1], sc, false)),
                  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[1], sc, true))};
+}
+// Eight E2M1 values (one dword, byte j holding features 2j and 2j+1) times
+// 2^(e - 127), as eight bf16 values (exact: two significant bits).
+__device__ __forceinline__ u32x4 mx_to_bf16(uint32_t raw, uint32_t e) {
+    const float sc = __builtin_amdgcn_ldexpf(1.0f, (int)e - 127);
+    return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(raw, sc, 0)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(raw, sc, 1)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(raw, sc, 2)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(raw, sc, 3))};
 }
 
 template <typename T> struct IO;
@@ -411,6 +438,12 @@ template <> struct Quad<fp8e4m3> {                     // the same eight feature
         return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kNonTemporal);
     }
 };
+template <> struct Quad<fp4e2m1> {                     // ... and as half a byte each
+    using type = uint32_t;
+    __device__ static __forceinline__ type load(rsrc_t r, uint32_t off) {
+        return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kNonTemporal);
+    }
+};
 template <> struct Quad<float> {
     using type = u32x4;
     __device__ static __forceinline__ type load(rsrc_t r, uint32_t off) { return bload16_nt(r, off); }
@@ -457,7 +490,7 @@ template <typename TIN, int D, bool PART, bool WPASS = false, bool RHO = false>
 __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
     using T = typename Elem<TIN>::C;
     constexpr bool MX = !__is_same(T, TIN);
-    constexpr int GB = Elem<TIN>::GB;               // input bytes per element
+    constexpr int GB2 = Elem<TIN>::G2;              // input half-bytes per element
     using C = GramCfg<T, D>;
     using io = IO<T>;
     using frag = typename io::frag;
@@ -508,8 +541,8 @@ __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
     const int s = ptid % C::SL;                     // features s*FPT .. s*FPT+3
     const int tl = ptid / C::SL;                    // tokens tl*TPT .. tl*TPT+TPT-1
     const size_t rowstride = (size_t)H * D;         // elements between tokens
-    const uint32_t row_bytes = (uint32_t)(H * D * GB);
-    const uint32_t kv_off0 = (uint32_t)(tl * C::TPT) * row_bytes + (uint32_t)(s * C::FPT * GB);
+    const uint32_t row_bytes = (uint32_t)(H * D * GB2 / 2);
+    const uint32_t kv_off0 = (uint32_t)(tl * C::TPT) * row_bytes + (uint32_t)(s * C::FPT * GB2 / 2);
     // block-scaled inputs: each token row has D/32 scale bytes; this thread's
     // eight features lie in block s*FPT/32
     constexpr int NB = D / kMxBlock;
@@ -547,10 +580,10 @@ __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
         const Item it = item_of(kk);
         const size_t tok0 = ((size_t)it.b * a.F + it.f) * (size_t)N + (size_t)it.p * tpart;
         const int nt = range_tokens(it);
-        const uint32_t kv_bytes = nt > 0 ? (uint32_t)(((size_t)(nt - 1) * H * D + D) * GB) : 0u;
+        const uint32_t kv_bytes = nt > 0 ? (uint32_t)elem_bytes<TIN>((size_t)(nt - 1) * H * D + D) : 0u;
         const uint32_t beta_bytes = nt > 0 ? (uint32_t)(((nt - 1) * H + 1) * 4) : 0u;
-        L.rk = make_rsrc(static_cast<const TIN*>(a.k) + tok0 * rowstride + (size_t)it.h * D, kv_bytes);
-        L.rv = make_rsrc(static_cast<const TIN*>(a.v) + tok0 * rowstride + (size_t)it.h * D, kv_bytes);
+        L.rk = make_rsrc(elem_ptr<TIN>(a.k, tok0 * rowstride + (size_t)it.h * D), kv_bytes);
+        L.rv = make_rsrc(elem_ptr<TIN>(a.v, tok0 * rowstride + (size_t)it.h * D), kv_bytes);
         if constexpr (MX) {
             const uint32_t sc_bytes = nt > 0 ? (uint32_t)((nt - 1) * H * NB + NB) : 0u;
             L.rks = make_rsrc(a.ks + tok0 * H * NB + (size_t)it.h * NB, sc_bytes);
@@ -1322,7 +1355,7 @@ template <typename TIN, int D, bool TRS = false>
 __global__ __launch_bounds__(256, 2) void frame_output_kernel(ScanArgs a) {
     using T = typename Elem<TIN>::C;
     constexpr bool MX = !__is_same(T, TIN);
-    constexpr int GB = Elem<TIN>::GB;
+    constexpr int GB2 = Elem<TIN>::G2;
     using C = OutCfg<T, D>;
     using io = IO<T>;
     using frag = typename io::frag;
@@ -1368,11 +1401,11 @@ __global__ __launch_bounds__(256, 2) void frame_output_kernel(ScanArgs a) {
     const size_t rowstride = (size_t)H * D;
     const size_t tok0 = ((size_t)b * a.F + f) * (size_t)N + nbeg;
     const uint32_t rbytes = (uint32_t)(((size_t)(nend - nbeg - 1) * rowstride + D) * C::SZ);
-    const uint32_t qbytes = (uint32_t)(((size_t)(nend - nbeg - 1) * rowstride + D) * GB);
-    const rsrc_t rq = make_rsrc(static_cast<const TIN*>(a.q) + tok0 * rowstride + (size_t)h * D, qbytes);
+    const uint32_t qbytes = (uint32_t)elem_bytes<TIN>((size_t)(nend - nbeg - 1) * rowstride + D);
+    const rsrc_t rq = make_rsrc(elem_ptr<TIN>(a.q, tok0 * rowstride + (size_t)h * D), qbytes);
     const rsrc_t ro = make_rsrc(static_cast<T*>(a.o) + tok0 * rowstride + (size_t)h * D, rbytes);
     const uint32_t row_bytes = (uint32_t)(H * D * C::SZ);     // o (and q unless block-scaled)
-    const uint32_t qrow_bytes = (uint32_t)(H * D * GB);
+    const uint32_t qrow_bytes = (uint32_t)(H * D * GB2 / 2);
     const int nloc = nend - nbeg;
     const int nblk = (nloc + C::BT - 1) / C::BT;
     // block-scaled q: D/32 scale bytes per token row
@@ -1390,7 +1423,7 @@ __global__ __launch_bounds__(256, 2) void frame_output_kernel(ScanArgs a) {
     };
     auto load_blk = [&](int blk, QStage& R) {
         constexpr int FPC = 16 / C::SZ;             // features per 16-byte chunk of the LDS row
-        const uint32_t base = (uint32_t)(blk * C::BT + lr) * qrow_bytes + (uint32_t)(lc * FPC * GB);
+        const uint32_t base = (uint32_t)(blk * C::BT + lr) * qrow_bytes + (uint32_t)(lc * FPC * GB2 / 2);
 #pragma unroll
         for (int i = 0; i < C::NLD; ++i) R.v[i] = Quad<TIN>::load(rq, base + (uint32_t)(i * C::RPP) * qrow_bytes);
         if constexpr (MX) {

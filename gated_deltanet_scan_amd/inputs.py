@@ -177,6 +177,84 @@ def make_fp8(w: Workload):
     return tuple((c, s) for c, s, _ in enc), deq
 
 
+# E2M1 magnitudes by code (bit 3 is the sign), the midpoints between
+# neighbouring magnitudes, and the midpoints where a tie goes up to the even
+# code (ties between codes 2i+1 and 2i+2)
+_E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+_E2M1_MID = (_E2M1[1:] + _E2M1[:-1]) / 2
+_E2M1_TIE_UP = _E2M1_MID[1::2]
+
+
+def to_mxfp4(x: np.ndarray):
+    """Encode x ([..., D], D a multiple of 32) in the OCP microscaling MXFP4
+    layout: per block of 32 consecutive values of the last axis one E8M0 scale
+    2^e with e = floor(log2(max |x|)) - 2 (2 is the largest exponent of an
+    E2M1 value; all-zero blocks take e = 0), and per value the E2M1 code of
+    x / 2^e rounded to the nearest representable magnitude (ties to the even
+    code), saturated at +-6.  Two codes per byte, value 2j in the lower four
+    bits of byte j.  Returns (packed uint8 [..., D/2], scale bytes e + 127
+    uint8 [..., D/32], the dequantised values as float32)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    lead, D = x.shape[:-1], x.shape[-1]
+    if D % 32:
+        raise ValueError("the last axis must be a multiple of 32")
+    blk = x.reshape(lead + (D // 32, 32))
+    amax = np.abs(blk).max(axis=-1).astype(np.float64)
+    e = np.floor(np.log2(np.where(amax > 0, amax, 4.0))) - 2
+    e = np.clip(e, -127, 127)
+    sc = np.exp2(e).astype(np.float32)                 # 2^-127 .. 2^127, exact in float32
+    y = blk / sc[..., None]                            # exact: |y| < 8 and a power-of-two divisor
+    a = np.abs(y)
+    code = np.zeros(a.shape, np.uint8)
+    for m in _E2M1_MID.astype(np.float32):             # count the midpoints below a ...
+        code += a > m
+    for m in _E2M1_TIE_UP.astype(np.float32):          # ... and ties go to the even code
+        code += a == m
+    code |= (np.signbit(y) & (code > 0)).astype(np.uint8) << 3            # -0 encodes as +0
+    signed = np.concatenate([_E2M1, -_E2M1]).astype(np.float32)
+    deq = signed[code] * sc[..., None]
+    code = code.reshape(x.shape)
+    packed = (code[..., 0::2] | (code[..., 1::2] << 4)).astype(np.uint8)
+    return packed, (e + 127).astype(np.uint8), deq.reshape(x.shape).astype(np.float32)
+
+
+def to_mxfp4_device(x, chunk_blocks: int = 1 << 24):
+    """to_mxfp4 on a device tensor (the same recipe, in torch, in pieces of
+    chunk_blocks scale blocks to bound the float64 temporaries): returns
+    (packed codes torch.uint8 [..., D/2], scale bytes torch.uint8) on x's
+    device."""
+    import torch
+    lead, D = x.shape[:-1], x.shape[-1]
+    blk = x.reshape(-1, 32)
+    codes = torch.empty((blk.shape[0], 16), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((blk.shape[0],), dtype=torch.uint8, device=x.device)
+    mid = torch.tensor(_E2M1_MID, dtype=torch.float64, device=x.device)
+    up = torch.tensor(_E2M1_TIE_UP, dtype=torch.float64, device=x.device)
+    for i in range(0, blk.shape[0], chunk_blocks):
+        b = blk[i:i + chunk_blocks].float()
+        amax = b.abs().amax(dim=-1)
+        e = torch.floor(torch.log2(torch.where(amax > 0, amax, torch.full_like(amax, 4.0)))) - 2
+        e = e.clamp(-127, 127)
+        y = b.double() / torch.exp2(e.double()).unsqueeze(-1)          # exact: a power-of-two scale
+        a = y.abs()
+        code = torch.bucketize(a, mid, right=False).to(torch.uint8)    # midpoints below a
+        code += torch.isin(a, up).to(torch.uint8)                      # ties go to the even code
+        code = code | ((y < 0) & (code > 0)).to(torch.uint8) << 3
+        codes[i:i + chunk_blocks] = code[:, 0::2] | (code[:, 1::2] << 4)
+        scales[i:i + chunk_blocks] = (e + 127).to(torch.uint8)
+    return codes.reshape(*lead, D // 2), scales.reshape(*lead, D // 32)
+
+
+def make_fp4(w: Workload):
+    """MXFP4 encodings of a workload's q, k and v, and a copy of the workload
+    holding their dequantised values.  Returns (((q codes, q scales), ...),
+    dequantised workload)."""
+    from dataclasses import replace
+    enc = [to_mxfp4(x) for x in (w.q, w.k, w.v)]
+    deq = replace(w, q=enc[0][2], k=enc[1][2], v=enc[2][2], dtype="bf16")
+    return tuple((c, s) for c, s, _ in enc), deq
+
+
 def make_config(name: str, seed: int = 0, **overrides) -> Workload:
     """Draw one of the named workloads in CONFIGS (fields may be overridden)."""
     c = dict(CONFIGS[name])

@@ -68,7 +68,7 @@ typedef enum gdn_status {
     GDN_ERR_NO_DEVICE = 7     /* no current HIP device could be queried            */
 } gdn_status;
 
-typedef enum gdn_dtype { GDN_BF16 = 0, GDN_F32 = 1, GDN_FP8_E4M3 = 2 } gdn_dtype;
+typedef enum gdn_dtype { GDN_BF16 = 0, GDN_F32 = 1, GDN_FP8_E4M3 = 2, GDN_FP4_E2M1 = 3 } gdn_dtype;
 
 /* beta and alpha hold logits; the library applies sigmoid(.)/N and sigmoid(.). */
 #define GDN_FLAG_GATES_ARE_LOGITS 0x1u
@@ -185,6 +185,26 @@ size_t gdn_static_scratch_bytes(void);
  * dtype (GDN_ERR_INVALID_ARG), and so does the backward pass
  * (GDN_ERR_UNSUPPORTED). */
 gdn_status gdn_frame_scan_fwd_fp8(const gdn_desc* d,
+                                  const void* q, const uint8_t* q_scale,
+                                  const void* k, const uint8_t* k_scale,
+                                  const void* v, const uint8_t* v_scale,
+                                  const float* beta, const float* alpha,
+                                  const float* S0,
+                                  void* o, float* S_final,
+                                  void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
+/* Block-scaled FP4 inputs (io_dtype GDN_FP4_E2M1, Dk = Dv in {32, 64, 128}):
+ * as gdn_frame_scan_fwd_fp8 with OCP FP4 E2M1 elements (sign, 2 exponent bits
+ * with bias 1, 1 mantissa bit: 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their
+ * negatives), two per byte: q, k, v are [B][F][N][H][D/2] bytes, byte j of a
+ * row holding feature 2j in its lower four bits and feature 2j + 1 in its
+ * upper four; the E8M0 scales are laid out as for FP8 (the OCP microscaling
+ * MXFP4 layout).  The input streams shrink to a quarter of bf16's; every
+ * value is exact in bf16, so the result equals gdn_frame_scan_fwd's on bf16
+ * inputs holding the dequantised values.  Each block-scaled entry point
+ * accepts its own dtype only (GDN_ERR_INVALID_ARG otherwise). */
+gdn_status gdn_frame_scan_fwd_fp4(const gdn_desc* d,
                                   const void* q, const uint8_t* q_scale,
                                   const void* k, const uint8_t* k_scale,
                                   const void* v, const uint8_t* v_scale,

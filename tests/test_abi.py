@@ -276,6 +276,31 @@ def test_fp8_entry_point_checks(lib):
     assert call_bwd(lib, desc(D=64, io=f8)) == UNSUPPORTED
 
 
+def call_fp4(lib, d, ws_bytes=1 << 40, **over):
+    p = dict(P8)
+    p.update(over)
+    return lib.gdn_frame_scan_fwd_fp4(None if d is None else ctypes.byref(d), *[p[n] for n in FP8_NAMES[:-1]],
+                                      p["ws"], ctypes.c_size_t(ws_bytes), None)
+
+
+def test_fp4_entry_point_checks(lib):
+    f4 = _lib.GDN_FP4_E2M1
+    assert call_fp4(lib, desc(D=16, io=f4)) == UNSUPPORTED
+    assert call_fp4(lib, desc(D=64, io=_lib.GDN_FP8_E4M3)) == INVALID   # each MX entry point takes its own format
+    assert call_fp8(lib, desc(D=64, io=f4)) == INVALID
+    for n in ["q", "qs", "k", "ks", "v", "vs", "beta", "alpha", "o"]:
+        assert call_fp4(lib, desc(D=64, io=f4), **{n: None}) == INVALID, n
+    # q holds 2*3*5 tokens of 64 features at half a byte each: 960 bytes
+    assert call_fp4(lib, desc(D=64, io=f4), o=P8["q"] + 944) == ALIAS      # 16-byte aligned, inside q
+    assert call_fp4(lib, desc(D=64, io=f4), S_final=P8["vs"]) == ALIAS
+    assert call_fp4(lib, desc(D=64, io=f4), ws=P8["ks"]) == ALIAS
+    need = lib.gdn_workspace_size(ctypes.byref(desc(D=64, io=f4)))
+    assert need == lib.gdn_workspace_size(ctypes.byref(desc(D=64, io=_lib.GDN_BF16)))
+    assert call_fp4(lib, desc(D=64, io=f4), ws_bytes=need - 1) == WORKSPACE
+    assert call(lib, desc(D=64, io=f4)) == INVALID
+    assert call_bwd(lib, desc(D=64, io=f4)) == UNSUPPORTED
+
+
 # ----------------------------------------------------------- block projections
 BP = {n: BASE + i * (1 << 32) for i, n in enumerate(["x", "w_qkv", "w_gate", "q", "k", "v", "bl", "al", "ws",
                                                        "o", "w_out", "y"])}

@@ -83,3 +83,78 @@ def test_mxfp8_blocks_scales_and_rounding():
     # values already on the grid come back exactly
     c2, s2, d2 = inputs.to_mxfp8(deq)
     np.testing.assert_array_equal(d2, deq)
+
+
+# ------------------------------------------------------------------ MXFP4 (E2M1)
+def e2m1_value(code):
+    """An E2M1 code's value from its bit fields (sign, 2 exponent bits with
+    bias 1, 1 mantissa bit; exponent 0 is subnormal)."""
+    s, e, m = (code >> 3) & 1, (code >> 1) & 3, code & 1
+    mag = (m / 2.0) if e == 0 else 2.0 ** (e - 1) * (1.0 + m / 2.0)
+    return -mag if s else mag
+
+
+def unpack4(packed):
+    return np.stack([packed & 15, packed >> 4], axis=-1).reshape(packed.shape[:-1] + (2 * packed.shape[-1],))
+
+
+def test_mxfp4_decode_matches_the_bit_fields():
+    # every representable magnitude times a block scale encodes to itself
+    vals = np.array([e2m1_value(c) for c in range(16)])
+    assert sorted(set(np.abs(vals))) == [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    x = np.zeros((1, 32), np.float32)
+    x[0, :16] = vals * 4.0
+    x[0, 16:] = 6.0 * 4.0                       # amax 24 -> e = floor(log2 24) - 2 = 2
+    packed, sc, deq = inputs.to_mxfp4(x)
+    assert sc[0, 0] == 127 + 2
+    codes = unpack4(packed)
+    np.testing.assert_array_equal(deq, x)
+    for c in range(16):
+        if vals[c] != 0.0 or c == 0:
+            assert codes[0, c] == c, (c, codes[0, c])
+
+
+def test_mxfp4_rounding_ties_even_and_saturation():
+    # with amax = 6 (scale 2^0): midpoints go to the even code, values past 6 saturate
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    want = [0.0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0]
+    x = np.zeros((1, 32), np.float32)
+    x[0, :7] = mids
+    x[0, 7:14] = [-m for m in mids]
+    x[0, 14] = 6.0
+    x[0, 15] = 7.9                              # amax < 8 keeps e = 0, saturates to 6
+    x[0, 16] = 0.26                             # just past a midpoint: rounds up
+    _, sc, deq = inputs.to_mxfp4(x)
+    assert sc[0, 0] == 127
+    np.testing.assert_array_equal(deq[0, :7], want)
+    np.testing.assert_array_equal(deq[0, 7:14], [-w for w in want])
+    assert deq[0, 14] == 6.0 and deq[0, 15] == 6.0 and deq[0, 16] == 0.5
+
+
+def test_mxfp4_scale_rule_and_error_bound():
+    rng = np.random.default_rng(7)
+    x = (rng.standard_normal((64, 128)) * np.exp2(rng.integers(-6, 6, (64, 1)))).astype(np.float32)
+    packed, sc, deq = inputs.to_mxfp4(x)
+    assert packed.shape == (64, 64) and sc.shape == (64, 4)
+    blk = np.abs(x.reshape(64, 4, 32)).max(-1)
+    e = sc.astype(np.int64) - 127
+    # amax lies in [4, 8) * 2^e, so every value fits below the saturation point 6 * 2^e except the top ones
+    assert np.all(blk >= 4.0 * np.exp2(e)) and np.all(blk < 8.0 * np.exp2(e))
+    # below saturation the error is at most half the local spacing (1 * 2^e above 4, 0.25 * 2^e below 0.5 ...)
+    err = np.abs(deq - x).reshape(64, 4, 32)
+    sat = np.abs(x.reshape(64, 4, 32)) > 6.0 * np.exp2(e)[..., None]
+    assert np.all(err[~sat] <= np.exp2(e)[..., None].repeat(32, -1)[~sat] + 1e-30)
+
+
+def test_mxfp4_device_recipe_equals_host_recipe():
+    # the torch encoder (run here on CPU tensors, in small pieces) against the
+    # numpy one, over scales from 2^-20 to 2^20 and an all-zero block
+    import torch
+    rng = np.random.default_rng(7)
+    x = (rng.standard_normal((3, 5, 7, 64)) * np.exp2(rng.integers(-20, 20, (3, 5, 7, 1)))).astype(np.float32)
+    x[0, 0, 0, :32] = 0.0
+    c, s, _ = inputs.to_mxfp4(x)
+    for chunk in (7, 1 << 22):
+        dc, ds = inputs.to_mxfp4_device(torch.from_numpy(x), chunk_blocks=chunk)
+        np.testing.assert_array_equal(dc.numpy(), c)
+        np.testing.assert_array_equal(ds.numpy(), s)
