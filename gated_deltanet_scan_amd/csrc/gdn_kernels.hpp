@@ -73,6 +73,18 @@ __device__ __forceinline__ float group_sum(float x) {
 __device__ __forceinline__ uint32_t pack_bf16x2(float x, float y) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x, y}, bf16x2));
 }
+// Hold a value read from LDS in registers at this point.  hipcc sinks LDS
+// reads whose first use lies past a later __syncthreads() below that barrier
+// (nothing in the barrier's lowering stops it), where other waves may already
+// be overwriting the memory; an empty asm statement that consumes the value
+// keeps the read (and its wait) above the barrier.
+template <typename V>
+__device__ __forceinline__ void hold(const V& x) {
+    static_assert(sizeof(V) % 4 == 0, "whole dwords");
+    const auto d = __builtin_bit_cast(uint32_t __attribute__((ext_vector_type(sizeof(V) / 4))), x);
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(V) / 4); ++i) asm volatile("" ::"v"(d[i]));
+}
 // Remainder code of x against its bf16 rounding h (bits in the low half of
 // hb): x - h is at most half a bf16 ulp, 2^(E-134) for h's biased exponent E;
 // the code counts it in 1/256 ulps, rounded to nearest and clamped to int8.
@@ -1966,6 +1978,8 @@ __global__ __launch_bounds__(64 * (D / 16), 2) void frame_step_kernel(ScanArgs a
             ah[ks] = io::zero();
             alw[ks] = io::zero();
         }
+        hold(ah[ks]);                               // read before the barrier, not after it
+        if constexpr (sizeof(T) == 2) hold(alw[ks]);
     }
     __syncthreads();                                // LDS is reused for Q and O below
     if (nbeg >= nend) return;
