@@ -148,7 +148,8 @@ def measured_peaks():
     """What this GPU reaches on plain work, as a second yardstick next to the
     published peaks: a 1 GiB device-to-device copy (torch copy_, bytes read
     plus written per second) and a 8192^3 bf16 matrix product (torch.matmul,
-    hipBLASLt).  Run before the warm-up, so they also bring the clocks up."""
+    hipBLASLt).  Run after the timed regions: the products draw enough power
+    to slow a scan timed right after them."""
     import torch
     n = 1 << 28
     x = torch.ones(n, dtype=torch.float32, device="cuda")
