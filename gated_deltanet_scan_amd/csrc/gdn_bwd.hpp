@@ -302,6 +302,13 @@ __global__ __launch_bounds__(512, 1) void frame_dkv_kernel(DkvArgs da) {
             }
         }
     }
+#pragma unroll
+    for (int kk = 0; kk < C::KS; ++kk) {                         // formed before the barrier, not after it
+        hold(xt_h[kk]);
+        hold(xt_l[kk]);
+        hold(ms_h[kk]);
+        hold(ms_l[kk]);
+    }
     __syncthreads();                                             // staging read before the token tiles reuse it
 
     // ---- token loop

@@ -1472,7 +1472,11 @@ __global__ __launch_bounds__(256, 2) void frame_output_kernel(ScanArgs a) {
 #pragma unroll
         for (int i = 0; i < C::RPW; ++i)
 #pragma unroll
-            for (int ks = 0; ks < C::KS; ++ks) get_transposed<T, D>(smem, wr * C::RPW + i, ks, lane, ah[i][ks], alw[i][ks]);
+            for (int ks = 0; ks < C::KS; ++ks) {
+                get_transposed<T, D>(smem, wr * C::RPW + i, ks, lane, ah[i][ks], alw[i][ks]);
+                hold(ah[i][ks]);                        // read before the barrier, not after it
+                hold(alw[i][ks]);
+            }
         __syncthreads();                                // before the Q tiles overwrite the staging
     }
 #pragma unroll

@@ -160,3 +160,28 @@ def test_full_minute_units_and_bitwise_bf16():
         check(S4[:, h:h + 1].cpu().numpy(), S_ref, "S unit %d" % h)
     o16, S16 = bf16_path(deq)
     assert torch.equal(o4, o16) and torch.equal(S4, S16)
+
+
+def run_fp8(enc, w):
+    (qc, qs), (kc, ks), (vc, vs) = enc
+    f8 = lambda x: dev(x).view(torch.float8_e4m3fn)
+    s0 = None if w.S0 is None else dev(w.S0, torch.float32)
+    o, S = api.frame_scan_fwd_fp8(f8(qc), dev(qs), f8(kc), dev(ks), f8(vc), dev(vs), dev(w.beta, torch.float32),
+                                  dev(w.alpha, torch.float32), s0)
+    torch.cuda.synchronize()
+    return o, S
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "fp4"])
+@pytest.mark.parametrize("F,N", [(3, 0), (0, 40), (1, 0)])
+def test_empty_frames_or_tokens(fmt, F, N):
+    """No tokens: the state only decays, S_final = (prod alpha) S0 and o is
+    empty; no frames: S_final = S0.  Both MX entry points, against the oracle."""
+    w = inputs.make(2, 3, F, N, 64, dtype="f32", seed=38, s0_std=0.1)
+    enc, deq = (inputs.make_fp8 if fmt == "fp8" else inputs.make_fp4)(w)
+    o, S = (run_fp8 if fmt == "fp8" else run_fp4)(enc, w)
+    o_ref, S_ref = ref(deq)
+    assert o.shape == (2, F, N, 3, 64) and o.numel() == 0
+    check(S.cpu().numpy(), S_ref, "S %s F%d N%d" % (fmt, F, N))
+    if F == 0:
+        assert np.array_equal(S.cpu().numpy(), w.S0)
