@@ -1,0 +1,75 @@
+"""Scans with many (b, h) units: more recurrence workgroups (one per 16-row
+slab of a state) than the GPU has CUs, so the slabs of several heads share
+each XCD, and the Gram and output passes walk many items per workgroup.
+
+Against the oracle in both directions, bf16 and fp32, the forward and the
+backward (whose adjoint recurrence is the same kernel); and bit for bit
+across unit counts: heads 0..15 of a B1 H17 d128 scan equal a B1 H16 d128
+scan of the same heads, since each unit's arithmetic does not depend on how
+many units share the launch.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gated_deltanet_scan_amd import api, inputs
+from test_gpu_bwd import compare, ref_bwd, run_bwd
+from test_gpu_parity import check, oracle_ref
+
+pytestmark = pytest.mark.gpu
+
+
+def run(w, **kw):
+    q, k, v, b, a, s0 = inputs.to_torch(w, "cuda")
+    o, S = api.frame_scan_fwd(q, k, v, b, a, s0, **kw)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), S.cpu().numpy()
+
+
+FWD = [  # B, H, F, N, D, dtype, reverse; every one has more than 128 slab workgroups
+    (2, 12, 4, 40, 128, "bf16", False),
+    (2, 12, 3, 70, 128, "bf16", True),
+    (3, 30, 3, 30, 64, "bf16", False),
+    (1, 70, 3, 20, 32, "bf16", True),
+    (1, 20, 3, 24, 128, "f32", False),
+    (2, 36, 2, 17, 64, "f32", True),
+]
+
+
+@pytest.mark.parametrize("shape", FWD, ids=lambda s: "B%dH%dF%dN%dD%d_%s_%s" % (s[:6] + ("rev" if s[6] else "fwd",)))
+def test_forward_against_oracle(shape):
+    B, H, F, N, D, dtype, reverse = shape
+    assert B * H * D // 16 > 128
+    w = inputs.make(B, H, F, N, D, dtype=dtype, seed=81, s0_std=0.05)
+    o, S = run(w, reverse=reverse)
+    ro, rS = oracle_ref(w, reverse=reverse)
+    check(o, ro, dtype, "O")
+    check(S, rS, dtype, "S_F")
+
+
+@pytest.mark.parametrize("shape", [(2, 12, 3, 40, 128, "bf16"), (2, 40, 3, 20, 64, "bf16"), (1, 80, 2, 12, 32, "f32")],
+                         ids=lambda s: "B%dH%dF%dN%dD%d_%s" % s)
+@pytest.mark.parametrize("reverse", [False, True])
+def test_backward_against_oracle(shape, reverse):
+    B, H, F, N, D, dtype = shape
+    w = inputs.make(B, H, F, N, D, dtype=dtype, seed=82, s0_std=0.05)
+    dO, dS = inputs.make_grads(w, seed=82)
+    got = run_bwd(w, dO, dS, reverse=reverse)
+    ref = ref_bwd(w, dO, dS, reverse=reverse)
+    compare(got, ref, dtype, "B%dH%dD%d" % (B, H, D))
+
+
+def test_units_do_not_depend_on_the_unit_count():
+    w17 = inputs.make(1, 17, 5, 100, 128, dtype="bf16", seed=83, s0_std=0.05)
+    sl = lambda x: np.ascontiguousarray(x[..., :16, :]) if x.ndim == 5 else x
+    w16 = inputs.make(1, 16, 5, 100, 128, dtype="bf16", seed=83, s0_std=0.05)
+    w16.q, w16.k, w16.v = sl(w17.q), sl(w17.k), sl(w17.v)
+    w16.beta = np.ascontiguousarray(w17.beta[..., :16])
+    w16.alpha = np.ascontiguousarray(w17.alpha[..., :16])
+    w16.S0 = np.ascontiguousarray(w17.S0[:, :16])
+    o17, S17 = run(w17)
+    o16, S16 = run(w16)
+    assert np.array_equal(o17[..., :16, :], o16) and np.array_equal(S17[:, :16], S16)
+    ro, rS = oracle_ref(w17)
+    check(o17, ro, "bf16", "O H17")
+    check(S17, rS, "bf16", "S_F H17")
