@@ -499,6 +499,9 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="full_minute")
+    ap.add_argument("--settle-ms", type=float, default=40.0,
+                    help="after the W warm-up steps, keep stepping (untimed) until this many "
+                         "milliseconds have passed since the first warm-up step ended (0: off)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0: skip)")
@@ -552,9 +555,28 @@ def main():
     flush = args.flush == "on" or (args.flush == "auto" and total_bytes < (1 << 30))
     junk = torch.empty(1 << 28, dtype=torch.float32, device="cuda") if flush else None
 
-    for _ in range(args.warmup):
+    # (the first call loads the kernels' code; the settle clock starts after it)
+    for i in range(args.warmup):
         step()
+        if i == 0:
+            torch.cuda.synchronize()
+            t_settle = time.perf_counter()
+    if args.warmup == 0:
+        t_settle = time.perf_counter()
     torch.cuda.synchronize()
+    # Clock settle.  A GPU that was idle runs the first milliseconds of this
+    # load through a clock transient (every kernel slows alike, by up to a
+    # quarter, from about 2 ms to about 15 ms into the load, then steadies);
+    # a few warm-up steps end inside it.  So warm-up continues, whole steps,
+    # until --settle-ms of wall time have passed since its first step ended;
+    # the timed steps then see the steady clock.  Reported as "settle".
+    settle_steps = 0
+    while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
+        for _ in range(4):
+            step()
+        settle_steps += 4
+        torch.cuda.synchronize()
+    settle_ms = (time.perf_counter() - t_settle) * 1e3
 
     def timed(profiled: bool):
         # K steps bracketed by synchronisation; with `profiled` the library
@@ -621,7 +643,12 @@ def main():
     peaks = measured_peaks()
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "steps": args.steps, "warmup": args.warmup,
+        "settle": {"steps": settle_steps, "ms": round(settle_ms, 2),
+                   "why": "untimed whole steps after the warm-up until --settle-ms have passed, so "
+                          "that the timed steps run at the steady clock, not in the transient that "
+                          "follows an idle GPU"},
+        "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic (seeded Gaussians in the workload's shapes; no trained weights)",
         "config": {"workload": args.workload, "B": w.B, "H": w.H, "F": w.F, "N": w.N, "Dk": w.Dk,
