@@ -149,6 +149,25 @@ constexpr int kStreamStore = 2 | 16;
 // for frame_gram than the default policy, with no cost to the recurrence that
 // reads them; the non-temporal bit instead slowed those reads by half.
 constexpr int kWorkspaceStore = 16;
+// Buffer stores, each followed by a pad of wait states during which its data
+// registers stay unchanged.  A VALU write to a buffer store's data registers
+// in the cycles right after the store issues can change the stored value on
+// gfx950, and the compiler pads that case only for stores without a scalar
+// offset register (every store here has one).  Seen before this pad: one or
+// two corrupted values per ~30 M stored when the instruction after the
+// state planes' 16-byte store rewrote its first data register.  The asm
+// consumes the data after the store, so the registers cannot be reused
+// before the pad ends.
+template <int AUX>
+__device__ __forceinline__ void store_b128(u32x4 v, rsrc_t r, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, soff, AUX);
+    asm volatile("s_nop 2" ::"v"(v));
+}
+template <int AUX>
+__device__ __forceinline__ void store_b64(u32x2 v, rsrc_t r, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, voff, soff, AUX);
+    asm volatile("s_nop 2" ::"v"(v));
+}
 __device__ __forceinline__ u32x4 bload16_nt(rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNonTemporal);
 }
@@ -156,10 +175,10 @@ __device__ __forceinline__ float bload4f(rsrc_t r, uint32_t off) {
     return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
 __device__ __forceinline__ void bstore8(rsrc_t r, uint32_t off, u32x2 v) {
-    __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
+    store_b64<0>(v, r, off, 0);
 }
 __device__ __forceinline__ void bstore16(rsrc_t r, uint32_t off, u32x4 v) {
-    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+    store_b128<0>(v, r, off, 0);
 }
 
 // ---------------------------------------------------------------- I/O type traits
@@ -295,6 +314,13 @@ template <typename T, int D> struct WS {
     // byte offset of lane `lane`'s slot in operand fragment (tile, kt), half h (fp32)
     __device__ static __forceinline__ uint32_t frag_off(int tile, int kt, int h, int lane) {
         return (uint32_t)((tile * KS + kt) * FRAG) + (uint32_t)(h * 1024 + lane * 16);
+    }
+    // bf16 U (the forward scan at larger shapes): block pair (e blocks 2ep and
+    // 2ep + 1, a block ga), lane 16g + r: the four values of each block as above,
+    // rounded to bf16, in one 16-byte slot; the pairs fill the first half of
+    // the U region
+    __device__ static __forceinline__ size_t up_off(int ep, int ga) {
+        return ut_off + (size_t)(ep * RT + ga) * 1024;
     }
     // the same slot's 8 remainder codes in the code plane of S_f (bf16)
     __device__ static __forceinline__ uint32_t code_off(int tile, int kt, int lane) {
@@ -498,10 +524,11 @@ __device__ __forceinline__ float lane_group_sum(float x) {
 // to a.rho.  TIN is the input element type (fp8e4m3: block-scaled bytes,
 // turned into bf16 as each stage is written to LDS; everything else is the
 // bf16 mode).
-template <typename TIN, int D, bool PART, bool WPASS = false, bool RHO = false>
+template <typename TIN, int D, bool PART, bool WPASS = false, bool RHO = false, bool LP = false>
 __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
     using T = typename Elem<TIN>::C;
     constexpr bool MX = !__is_same(T, TIN);
+    static_assert(!LP || (sizeof(T) == 2 && !PART && !WPASS && !RHO && D >= 64), "bf16 U: the scan path only");
     constexpr int GB2 = Elem<TIN>::G2;              // input half-bytes per element
     using C = GramCfg<T, D>;
     using io = IO<T>;
@@ -775,8 +802,7 @@ __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
                     for (int j = 0; j < C::TC; ++j) {
                         const int gb = a_row0 + i, jb = b_row0 + j;
                         const uint32_t blk = (uint32_t)(PL::g_off + (size_t)(jb * PL::KS + (gb >> 1)) * 2048 + 512 * (gb & 1));
-                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][j]), rp, g32_lane, blk,
-                                                               kWorkspaceStore);
+                        store_b128<kWorkspaceStore>(__builtin_bit_cast(u32x4, acc[i][j]), rp, g32_lane, blk);
                     }
             } else {
 #pragma unroll
@@ -785,8 +811,7 @@ __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
                     for (int j = 0; j < C::TC; ++j) {
                         const int eb = a_row0 + i, ga = b_row0 + j;
                         const uint32_t blk = (uint32_t)(PL::u_off + (size_t)(eb * PL::RT + ga) * 1024);
-                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][j]), rp, u_lane, blk,
-                                                               kWorkspaceStore);
+                        store_b128<kWorkspaceStore>(__builtin_bit_cast(u32x4, acc[i][j]), rp, u_lane, blk);
                     }
             }
             return;
@@ -816,25 +841,39 @@ __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
                     if constexpr (RSTEP == 2) {
                         const f32x4 m1 = acc[i + RSTEP - 1][j] * (-al);
                         if constexpr (sizeof(T) == 2) {
-                            __builtin_amdgcn_raw_buffer_store_b128(
+                            store_b128<kWorkspaceStore>(
                                 u32x4{pack_bf16x2(m[0], m[1]), pack_bf16x2(m[2], m[3]), pack_bf16x2(m1[0], m1[1]),
                                       pack_bf16x2(m1[2], m1[3])},
-                                rw, u_lane, blk, kWorkspaceStore);
+                                rw, u_lane, blk);
                         } else {
-                            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, m), rw, u_lane, blk,
-                                                                   kWorkspaceStore);
-                            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, m1), rw, u_lane,
-                                                                   blk + 1024, kWorkspaceStore);
+                            store_b128<kWorkspaceStore>(__builtin_bit_cast(u32x4, m), rw, u_lane, blk);
+                            store_b128<kWorkspaceStore>(__builtin_bit_cast(u32x4, m1), rw, u_lane,
+                                                                   blk + 1024);
                         }
                     } else if constexpr (sizeof(T) == 2) {
-                        __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf16x2(m[0], m[1]), pack_bf16x2(m[2], m[3])},
-                                                              rw, u_lane, blk + 8 * (gb & 1), kWorkspaceStore);
+                        store_b64<kWorkspaceStore>(u32x2{pack_bf16x2(m[0], m[1]), pack_bf16x2(m[2], m[3])},
+                                                              rw, u_lane, blk + 8 * (gb & 1));
                     } else {
-                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, m), rw, u_lane,
-                                                               blk + 1024 * (gb & 1), kWorkspaceStore);
+                        store_b128<kWorkspaceStore>(__builtin_bit_cast(u32x4, m), rw, u_lane,
+                                                               blk + 1024 * (gb & 1));
                     }
                 }
             }
+        } else if constexpr (LP) {
+            // U in bf16: the blocks of e blocks eb and eb + 1 (eb even, rows 2i and
+            // 2i + 1 of this wave's tile) share one 16-byte lane slot, the layout
+            // the recurrence loads (WS::up_off)
+#pragma unroll
+            for (int i = 0; i < C::TR; i += 2)
+#pragma unroll
+                for (int j = 0; j < C::TC; ++j) {
+                    const int eb = a_row0 + i, ga = b_row0 + j;
+                    const f32x4 x = acc[i][j], y = acc[i + 1][j];
+                    store_b128<kWorkspaceStore>(
+                        u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(y[0], y[1]),
+                              pack_bf16x2(y[2], y[3])},
+                        rw, u_lane, (uint32_t)W::up_off(eb >> 1, ga));
+                }
         } else {
 #pragma unroll
             for (int i = 0; i < C::TR; ++i)
@@ -844,7 +883,7 @@ __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
                     // b_row0 + j); lane (r, g) holds U[16ga + r][16eb + 4g + t], slot 16g + r
                     const int eb = a_row0 + i, ga = b_row0 + j;
                     const uint32_t blk = (uint32_t)(W::ut_off + (size_t)(eb * W::RT + ga) * 1024);
-                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][j]), rw, u_lane, blk, kWorkspaceStore);
+                    store_b128<kWorkspaceStore>(__builtin_bit_cast(u32x4, acc[i][j]), rw, u_lane, blk);
                 }
         }
     };
@@ -997,13 +1036,17 @@ template <typename T, int D> struct StateCfg {
 // planes of X_f live in the second item set (ws2): W_f where frame_gram's U
 // would be, the planes of X_f, stored at the step that enters with it, where
 // S_f would be.
-template <typename T, int D, bool BWD = false>
+// LP: the forward scan's lighter intermediates at larger shapes: U arrives in
+// bf16 (frame_gram's packed block pairs) and S_f is stored as its bf16 plane
+// alone (no remainder codes).
+template <typename T, int D, bool BWD = false, bool LP = false>
 __global__ __launch_bounds__(256, 1) void state_scan_kernel(ScanArgs a) {   // NTH <= 256 threads
     using C = StateCfg<T, D>;
     using io = IO<T>;
     using frag = typename io::frag;
     using W = WS<T, D>;
     static_assert(C::NTH <= 256, "block size");
+    static_assert(!LP || (!BWD && C::B16 && C::BPW == 2), "bf16 U and planes: the forward scan, D >= 64");
     __shared__ __attribute__((aligned(16))) unsigned char sX[2][C::KS][64 * sizeof(frag)];
     __shared__ float sAlpha[kMaxChunkFrames];
 
@@ -1062,6 +1105,7 @@ __global__ __launch_bounds__(256, 1) void state_scan_kernel(ScanArgs a) {   // N
     struct Ops {
         frag gm[C::KS][C::BPW];
         f32x4 u[C::BPW];
+        u32x4 up;                                       // LP: this wave's two U blocks in bf16
     };
     // loads [j0, j1) of a frame's operands, in the order Gm^T fragments
     // (kk, q), then U blocks q: the recurrence issues them in three groups
@@ -1087,6 +1131,11 @@ __global__ __launch_bounds__(256, 1) void state_scan_kernel(ScanArgs a) {   // N
         // BWD: W of the frame visited next; after the last frame an offset past
         // the resource, which loads zeros
         const uint32_t ubase = !BWD ? base : (fl + 1 < Fc ? (uint32_t)phys(fl + 1) * (uint32_t)W::item_bytes : 0x80000000u);
+        if constexpr (LP) {
+            if (C::KS * C::BPW >= j0 && C::KS * C::BPW < j1)
+                o.up = __builtin_amdgcn_raw_buffer_load_b128(rout, lo16, ubase + (uint32_t)W::up_off(c, at), 0);
+            return;
+        }
 #pragma unroll
         for (int q = 0; q < C::BPW; ++q) {
             if (C::KS * C::BPW + q < j0 || C::KS * C::BPW + q >= j1) continue;
@@ -1102,7 +1151,7 @@ __global__ __launch_bounds__(256, 1) void state_scan_kernel(ScanArgs a) {   // N
     // Frame -1 maps past the resource (at most 256 frames of at most 192 KiB)
     // and is dropped, so the first call needs no branch.
     auto encode = [&](const frag& hi, const f32x4& x, const f32x4& y) {
-        if constexpr (C::B16)
+        if constexpr (C::B16 && !LP)
             return u32x2{codes4(x, hi[0], hi[1]), C::BPW > 1 ? codes4(y, hi[2], hi[3]) : 0u};
         else
             return u32x2{0u, 0u};
@@ -1110,13 +1159,14 @@ __global__ __launch_bounds__(256, 1) void state_scan_kernel(ScanArgs a) {   // N
     auto store_state = [&](int fl, const frag& hi, const f32x4& x, const f32x4& y, const u32x2& codes) {
         const uint32_t base = fl >= 0 ? (uint32_t)phys(fl) * (uint32_t)W::item_bytes + (uint32_t)W::sp_off : 0x80000000u;
         if constexpr (C::B16) {
-            __builtin_amdgcn_raw_buffer_store_b128(hi, rout, lo16, base + (uint32_t)((at * C::KS + c) * 1024), kStreamStore);
-            __builtin_amdgcn_raw_buffer_store_b64(codes, rout, (uint32_t)(lane * 8),
-                                                  base + (uint32_t)(W::sc_rel + (at * C::KS + c) * 512), kStreamStore);
+            store_b128<kStreamStore>(hi, rout, lo16, base + (uint32_t)((at * C::KS + c) * 1024));
+            if constexpr (!LP)
+                store_b64<kStreamStore>(codes, rout, (uint32_t)(lane * 8),
+                                                      base + (uint32_t)(W::sc_rel + (at * C::KS + c) * 512));
         } else {
             const uint32_t off = base + (uint32_t)((at * C::KS + c) * 2048);
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), rout, lo16, off, kStreamStore);
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, y), rout, lo16, off + 1024, kStreamStore);
+            store_b128<kStreamStore>(__builtin_bit_cast(u32x4, x), rout, lo16, off);
+            store_b128<kStreamStore>(__builtin_bit_cast(u32x4, y), rout, lo16, off + 1024);
         }
     };
     // One frame.  Every fragment of S_{fl-1}, this wave's own included, is read
@@ -1149,7 +1199,16 @@ __global__ __launch_bounds__(256, 1) void state_scan_kernel(ScanArgs a) {   // N
         const float al = sAlpha[fl];
         f32x4 acc[C::BPW];
 #pragma unroll
-        for (int q = 0; q < C::BPW; ++q) acc[q] = S[q] * al + o.u[q];
+        for (int q = 0; q < C::BPW; ++q) {
+            if constexpr (LP) {                         // bf16 pair: block q in words 2q, 2q + 1
+                const uint32_t w0 = o.up[2 * q], w1 = o.up[2 * q + 1];
+                const f32x4 u{__uint_as_float(w0 << 16), __uint_as_float(w0 & 0xffff0000u),
+                              __uint_as_float(w1 << 16), __uint_as_float(w1 & 0xffff0000u)};
+                acc[q] = S[q] * al + u;
+            } else {
+                acc[q] = S[q] * al + o.u[q];
+            }
+        }
 #pragma unroll
         for (int kk = 0; kk < C::KS; ++kk)
 #pragma unroll
@@ -1363,9 +1422,12 @@ template <typename T, int D> struct OutCfg {
 // o := dQ and the transposed state, staged through LDS before the pipeline.
 // TIN is q's element type (fp8e4m3: block-scaled bytes, turned into bf16 as
 // each block is written to LDS; o is then bf16).
-template <typename TIN, int D, bool TRS = false>
+// LP: the state planes are bf16 alone (see state_scan_kernel), one product
+// per fragment.
+template <typename TIN, int D, bool TRS = false, bool LP = false>
 __global__ __launch_bounds__(256, 2) void frame_output_kernel(ScanArgs a) {
     using T = typename Elem<TIN>::C;
+    static_assert(!LP || (!TRS && sizeof(T) == 2), "bf16 state planes: the forward scan");
     constexpr bool MX = !__is_same(T, TIN);
     constexpr int GB2 = Elem<TIN>::G2;
     using C = OutCfg<T, D>;
@@ -1484,7 +1546,9 @@ __global__ __launch_bounds__(256, 2) void frame_output_kernel(ScanArgs a) {
         const int rt = wr * C::RPW + i;
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
-            if constexpr (sizeof(T) == 2) {             // high plane and the low part from the codes
+            if constexpr (LP) {                         // the bf16 plane alone
+                ah[i][ks] = *reinterpret_cast<const u32x4*>(sp + W::frag_off(rt, ks, 0, lane));
+            } else if constexpr (sizeof(T) == 2) {      // high plane and the low part from the codes
                 ah[i][ks] = *reinterpret_cast<const u32x4*>(sp + W::frag_off(rt, ks, 0, lane));
                 alw[i][ks] = rem_frag(ah[i][ks], *reinterpret_cast<const u32x2*>(sp + W::sc_rel + W::code_off(rt, ks, lane)));
             } else {
@@ -1520,7 +1584,7 @@ __global__ __launch_bounds__(256, 2) void frame_output_kernel(ScanArgs a) {
 #pragma unroll
                 for (int ks = 0; ks < C::KS; ++ks) {
                     io::mma(acc[i], ah[i][ks], bq[ks]);
-                    if constexpr (sizeof(T) == 2) io::mma(acc[i], alw[i][ks], bq[ks]);
+                    if constexpr (sizeof(T) == 2 && !LP) io::mma(acc[i], alw[i][ks], bq[ks]);
                 }
             }
             unsigned char* orow = obuf + (sb * 16 + r) * C::ROWO;          // token sb*16 + r of the block

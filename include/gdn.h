@@ -105,7 +105,8 @@ typedef struct gdn_desc {
  * d x d operands to each other through this memory: per (b, h, frame) about
  * 10*Dk*Dv bytes in bf16 mode (12*Dk*Dv in fp32 mode), for at most 256 frames
  * per launch, plus one fp32 state per (b, h).  At B1 H16 d128 and 121 frames
- * that is 318 MB.  A single persistent kernel holding the state on chip would
+ * that is 318 MB (the bf16 intermediates described at gdn_frame_scan_fwd move
+ * about 6*Dk*Dv of those bytes per item).  A single persistent kernel holding the state on chip would
  * need none, but it would run on B*H*Dv/16 workgroups (128 at that shape, half
  * the GPU) and re-read every token of K once per row tile of the state; the
  * split design streams each token byte once on every compute unit. */
@@ -114,7 +115,17 @@ size_t gdn_workspace_size(const gdn_desc* d);
 /* Whole-clip scan: frames 1..F of every (b, h) from S0 (NULL means zeros).
  * Writes o and, when S_final is not NULL, the state after frame F.  S_final
  * may be the same pointer as S0 (in-place carry).  F == 0 copies S0 (or
- * zeros) to S_final; N == 0 applies the decay only. */
+ * zeros) to S_final; N == 0 applies the decay only.
+ *
+ * Intermediate precision.  The state is fp32 throughout its recurrence.  With
+ * bf16 or block-scaled inputs, Dk >= 64 and N >= 128, the per-frame U_f and
+ * the per-frame states handed to the output products are stored in the
+ * workspace as bf16 (otherwise U_f as fp32 and the states as bf16 plus an
+ * 8-bit remainder, about 16 bits): each adds one bf16 rounding to a value the
+ * bf16 products already carry at that precision, and at B1 H16 F121 N880
+ * d128 the results stay at about 3.3e-3 (o) and 2.4e-3 (S_final) relative
+ * Frobenius error against an fp64 reference.  Small frames keep the finer
+ * forms: there a single token's rounding is not averaged with others. */
 gdn_status gdn_frame_scan_fwd(const gdn_desc* d,
                               const void* q, const void* k, const void* v,
                               const float* beta, const float* alpha,
@@ -255,9 +266,13 @@ gdn_status gdn_frame_scan_bwd(const gdn_desc* d,
  * caller with the memory to spare (gdn_saved_size bytes per call: at B1 H16
  * F121 N880 d128 about 325 MB) can keep them instead:
  * gdn_frame_scan_fwd_save is gdn_frame_scan_fwd (the same o and S_final, bit
- * for bit when F > 1; a one-frame gdn_frame_scan_fwd call runs the streaming
- * step's kernels, which add in another order, so there the two agree to
- * rounding) that leaves in `saved` every frame's operands, the states entering
+ * for bit when F > 1 and the plain forward keeps full-precision intermediates,
+ * i.e. below Dk 64 or 128 tokens per frame; at larger shapes the plain forward
+ * hands U and the state planes on in bf16 (see gdn_frame_scan_fwd) while this
+ * call keeps the full forms the backward reads, and a one-frame
+ * gdn_frame_scan_fwd call runs the streaming step's kernels, which add in
+ * another order: in both cases the two agree to rounding, within the
+ * forward's tolerance) that leaves in `saved` every frame's operands, the states entering
  * its launch chunks (S0 or zeros first) and every token's key scale, and
  * gdn_frame_scan_bwd_saved is gdn_frame_scan_bwd (the same gradients, bit for
  * bit) that reads them instead of recomputing, so it takes no S0 and needs

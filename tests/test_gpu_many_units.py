@@ -14,7 +14,7 @@ import torch
 
 from gated_deltanet_scan_amd import api, inputs
 from test_gpu_bwd import compare, ref_bwd, run_bwd
-from test_gpu_parity import check, oracle_ref
+from test_gpu_parity import check, check_every_unit, oracle_ref
 
 pytestmark = pytest.mark.gpu
 
@@ -73,3 +73,39 @@ def test_units_do_not_depend_on_the_unit_count():
     ro, rS = oracle_ref(w17)
     check(o17, ro, "bf16", "O H17")
     check(S17, rS, "bf16", "S_F H17")
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("D", [128, 64])
+def test_many_units_of_whole_frames(D):
+    """128 (b, h) units of 880-token frames (B4 H32 F16): several recurrence
+    workgroups share each CU.  The workspace starts as all-ones bytes (NaN in
+    bf16, so any value read before it is written shows), and every unit must
+    meet the tolerances.  At this shape the state planes once came back with
+    one or two corrupted values per call: a buffer store's data registers were
+    rewritten by the next instruction (now padded; see store_b128)."""
+    w = inputs.make(4, 32, 16, 880, D, dtype="bf16", seed=84, s0_std=0.02)
+    q, k, v, b, a, s0 = inputs.to_torch(w, "cuda")
+    desc = api.make_desc(w.B, w.H, w.F, w.N, w.Dk, q.dtype)
+    ws = api.alloc_workspace(desc, q.device)
+    for rep in range(2):
+        ws.fill_(255)
+        o, S = api.frame_scan_fwd(q, k, v, b, a, s0, workspace=ws)
+        torch.cuda.synchronize()
+        o, S = o.float().cpu().numpy(), S.cpu().numpy()
+        if rep == 0:
+            ro, rS = oracle_ref(w)
+        check_every_unit(w, o, S, ro, rS)
+
+
+@pytest.mark.parametrize("N", [127, 128])
+def test_both_sides_of_the_intermediate_precision_threshold(N):
+    """d 64 with 127 tokens per frame keeps U in fp32 and the state planes with
+    remainder codes; with 128 the forward scan hands both on in bf16.  Both
+    meet the oracle's tolerance, in both directions."""
+    w = inputs.make(2, 3, 6, N, 64, dtype="bf16", seed=85, s0_std=0.05)
+    for reverse in (False, True):
+        o, S = run(w, reverse=reverse)
+        ro, rS = oracle_ref(w, reverse=reverse)
+        check(o, ro, "bf16", "O N%d" % N)
+        check(S, rS, "bf16", "S_F N%d" % N)

@@ -1,9 +1,13 @@
 """Training with saved states (gdn_frame_scan_fwd_save, gdn_frame_scan_bwd_saved).
 
 The saved forward runs the scan's own kernels into the caller's buffer, so for
-F > 1 its o and S_final must equal gdn_frame_scan_fwd's bit for bit (a
-one-frame gdn_frame_scan_fwd call takes the streaming step's kernels, so
-F == 1 is compared with the oracle at the forward's bar instead).  The
+F > 1 its o and S_final must equal gdn_frame_scan_fwd's bit for bit where the
+plain forward keeps full-precision intermediates (below d 64 or 128 tokens per
+frame; a one-frame gdn_frame_scan_fwd call takes the streaming step's kernels,
+so F == 1 is compared with the oracle at the forward's bar instead).  At larger
+shapes the plain forward hands U and the state planes between its kernels in
+bf16 while the saved forward keeps the full forms the backward reads, so there
+the two forwards agree to rounding and both are checked against the oracle.  The
 backward from saved states reads exactly the operands the recomputing
 backward rebuilds with the same kernels, so its gradients must equal
 gdn_frame_scan_bwd's bit for bit; that path is itself checked against the
@@ -132,9 +136,15 @@ def test_full_minute_saved_equals_recompute():
     o_ref, S_ref = api.frame_scan_fwd(q, k, v, b, a, S0)
     o, S, saved = api.frame_scan_fwd_save(q, k, v, b, a, S0)
     torch.cuda.synchronize()
-    same(o, o_ref, "o")
-    same(S, S_ref, "S_final")
-    del o_ref, S_ref
+    # the plain forward's bf16 intermediates against the saved forward's full
+    # ones, and the saved forward against the oracle
+    ro, rS = oracle.scan(w.q, w.k, w.v, w.beta, w.alpha, w.S0)
+    for got, ref, what in ((o, ro, "o"), (S, rS, "S_final"), (o_ref, ro, "o (plain)"), (S_ref, rS, "S_final (plain)")):
+        got = got.float().cpu().numpy().astype(np.float64)
+        mx, rel = np.abs(got - ref).max(), np.linalg.norm(got - ref) / np.linalg.norm(ref)
+        print("%s: max %.3e rel %.3e" % (what, mx, rel))
+        assert mx <= 2e-2 and rel <= 5e-3, what
+    del o_ref, S_ref, ro, rS
     g = api.frame_scan_bwd(q, k, v, b, a, dO, None, dS, saved=saved)
     g_ref = api.frame_scan_bwd(q, k, v, b, a, dO, S0, dS)
     torch.cuda.synchronize()

@@ -54,3 +54,50 @@ def test_no_back_to_back_barriers(asm):
         if j < len(asm) and asm[j].strip() == "s_barrier":
             bad.append((fn, i + 1))
     assert not bad, "code sunk below a barrier in: %s" % bad
+
+
+def _vgprs(spec):
+    m = re.match(r"v\[(\d+):(\d+)\]$", spec)
+    if m:
+        return set(range(int(m.group(1)), int(m.group(2)) + 1))
+    m = re.match(r"v(\d+)$", spec)
+    return {int(m.group(1))} if m else set()
+
+
+def test_buffer_store_data_is_not_rewritten_at_once(asm):
+    """A buffer store of 8 or 16 bytes keeps its data registers unchanged for
+    at least three wait states after it issues.  A write to them right after
+    the store once corrupted single stored values of the state planes (the
+    compiler pads this only for buffer stores without a scalar offset
+    register); every such store now goes through store_b64 / store_b128,
+    which hold the data through an s_nop pad.  Counted: instructions after
+    the store (an s_nop n counts n + 1) up to the first one that writes one
+    of the data registers."""
+    bad = []
+    fn = None
+    for i, line in enumerate(asm):
+        m = re.match(r"^(_Z\w+):", line)
+        if m:
+            fn = m.group(1)
+        t = line.strip()
+        m = re.match(r"buffer_store_dwordx(2|4)\s+(v\[\d+:\d+\]),", t)
+        if not m:
+            continue
+        data = _vgprs(m.group(2))
+        waits = 0
+        for nxt in asm[i + 1:i + 12]:
+            u = nxt.strip()
+            if not u or u.startswith((";", ".")) or u.endswith(":"):
+                continue
+            if u.startswith("s_nop"):
+                waits += int(re.findall(r"\d+", u)[0]) + 1
+                continue
+            dst = u.split(None, 1)[1].split(",")[0].strip() if " " in u else ""
+            writes = u.startswith(("v_", "ds_read", "buffer_load", "global_load")) and _vgprs(dst) & data
+            if writes and waits < 3:
+                bad.append((fn, i + 1, t))
+                break
+            waits += 1
+            if waits >= 3:
+                break
+    assert not bad, "store data rewritten within three wait states: %s" % bad[:5]
