@@ -542,12 +542,24 @@ __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
     const int items = a.B * a.H * a.Fc * parts;
     // Round k of the persistent loop covers items [k*G, (k+1)*G) (G = grid),
     // so the heads of a frame are read together; within a round, workgroup b
-    // takes item k*G + (b + k) mod G.  The rotation walks every workgroup
-    // through all heads: a head's 256-byte rows sit at one fixed offset of
-    // every token row, and with a fixed head per workgroup the workgroups of
-    // the slower heads (measured up to 15% slower) set the kernel's time.
+    // takes item k*G + slot(k).  The slot rotates with k, which walks every
+    // workgroup through all heads: a head's 256-byte rows sit at one fixed
+    // offset of every token row, and with a fixed head per workgroup the
+    // workgroups of the slower heads (measured up to 15% slower) set the
+    // kernel's time.  When a round's items per XCD (G/8; workgroup b runs on
+    // XCD b mod 8) hold whole frames, the XCD of workgroup b takes slots
+    // [G/8 * (b mod 8), G/8 * (b mod 8 + 1)), so every frame's heads share one
+    // L2: their betas interleave in the same lines ([.., token, head]), and
+    // with a frame's heads spread over all eight XCDs each XCD fetched those
+    // lines again (54 MB of the full-minute scan's 58 MB of beta traffic).
     const int G = (int)gridDim.x, rounds = items / G;
-    const int nmine = rounds + (((int)blockIdx.x + rounds) % G < items - rounds * G ? 1 : 0);
+    const int per = G / 8;
+    const bool xcd_frames = !PART && G % 8 == 0 && per % H == 0;
+    auto slot = [&](int k) {
+        const int bx = (int)blockIdx.x;
+        return xcd_frames ? per * (bx & 7) + ((bx >> 3) + k) % per : (bx + k) % G;
+    };
+    const int nmine = rounds + (slot(rounds) < items - rounds * G ? 1 : 0);
     const int nst = (tpart + C::TS - 1) / C::TS;    // stages per item (token range)
     const int total = nmine * nst;                  // stages of this workgroup
     const int tid = threadIdx.x, lane = tid & 63;
@@ -561,7 +573,7 @@ __global__ __launch_bounds__(1024, 1) void frame_gram_kernel(ScanArgs a) {
     };
     // item x: head fastest, then token range, frame, batch
     auto item_of = [&](int k) {
-        const int x = k * G + ((int)blockIdx.x + k) % G;
+        const int x = k * G + slot(k);
         Item it;
         it.h = x % H;
         const int y = x / H;
