@@ -46,6 +46,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------- scalar helpers
 __device__ __forceinline__ uint16_t f2bf(float x) {
@@ -405,6 +406,34 @@ __device__ __forceinline__ int xcd_remap(int id, int per, int total) {
     const int group = (slot / per) * 8 + xcd;
     const int logical = group * per + slot % per;
     return logical < total ? logical : -1;
+}
+
+// ---------------------------------------------------------------- LDS transpose reads
+// gfx950's ds_read_b64_tr_b16 works on groups of 16 lanes: lane s of a group
+// reads four 16-bit values w[s][0..3] (8 bytes at its own address), and lane
+// i of the group receives w[i/4][i%4], w[4 + i/4][i%4], w[8 + i/4][i%4],
+// w[12 + i/4][i%4] (layout checked on the device).  So if lane s points at
+// row kb + s/4, columns c0 + 4(s%4) .. +3 of a row-major 16-bit array, lane i
+// receives column c0 + i of rows kb .. kb+3: a column slice, i.e. the MFMA
+// operand fragment of the transposed array, read from its natural layout.
+// Token-major tiles (one row per token, D features of 2 bytes, 16-byte
+// chunks XOR-permuted by (2 row) mod 8 so that the four rows one group reads
+// fall in distinct banks, and each row's eight chunks in distinct banks for
+// the 16-byte writes) give the fragment for features f0 + r, tokens
+// kb .. kb + 7 of a 32-token step as two such reads.
+template <int ROWT>
+__device__ __forceinline__ int tok_off(int row, int f) {      // byte offset of feature f of token `row`
+    return row * ROWT + ((((f >> 3) ^ (2 * row)) & 7) << 4) + ((f & 7) << 1);
+}
+template <int ROWT>
+__device__ __forceinline__ u32x4 tr_frag(const unsigned char* arr, int f0, int kb, int r) {
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const int f = f0 + 4 * (r & 3);
+    const lds_i16x4* p0 = (const lds_i16x4*)(arr + tok_off<ROWT>(kb + (r >> 2), f));
+    const lds_i16x4* p1 = (const lds_i16x4*)(arr + tok_off<ROWT>(kb + 4 + (r >> 2), f));
+    const u32x2 a = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_i16x4*>(p0)));
+    const u32x2 b = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_i16x4*>(p1)));
+    return u32x4{a[0], a[1], b[0], b[1]};
 }
 
 // ================================================================== frame_gram
@@ -1729,6 +1758,11 @@ __global__ __launch_bounds__(64 * (D / 16), 2) void frame_step_kernel(ScanArgs a
     using PL = PartLayout<D>;
     static_assert(!FUSED || (sizeof(T) == 2 && D <= 64), "the one-launch step is bf16, D <= 64");
     constexpr int BTA = 64;                          // phase A: tokens per block
+    // D = 64: K, V tiles token-major, operand fragments through transpose
+    // reads (tr_frag); smaller D: feature-major tiles written transposed
+    constexpr bool TRK = FUSED && D == 64;
+    constexpr int ROWT = D * 2;                      //   token-major: bytes per LDS row (one token)
+    static_assert(!TRK || BTA * ROWT == D * BTA * 2, "the token-major tile fills the same array");
     constexpr int ROWA = BTA * 2;                    //   bytes per LDS row (one feature)
     constexpr int ARRA = D * ROWA;                   //   one transposed array
     constexpr int LDSA = FUSED ? 2 * 3 * ARRA : 0;   //   rho K, beta rho K, V; double-buffered
@@ -1897,6 +1931,25 @@ __global__ __launch_bounds__(64 * (D / 16), 2) void frame_step_kernel(ScanArgs a
             const float be1 = a.logits ? sigmoid_f(q2.b1) * inv_n : q2.b1;
             const float s0b = be0 * r0, s1b = be1 * r1;
             const int t = 2 * tp;
+            if constexpr (TRK) {                     // token-major rows, one 16-byte chunk per array and token
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const u32x4 x = u ? q2.k1 : q2.k0;
+                    const float rr = u ? r1 : r0, ss = u ? s1b : s0b;
+                    u32x4 pk, bk;
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        const float lo = bf2f((uint16_t)(x[d] & 0xffffu)), hi = bf2f((uint16_t)(x[d] >> 16));
+                        pk[d] = pack_bf16x2(rr * lo, rr * hi);
+                        bk[d] = pack_bf16x2(ss * lo, ss * hi);
+                    }
+                    const int off = tok_off<ROWT>(t + u, 8 * fgrp);
+                    *reinterpret_cast<u32x4*>(buf + off) = pk;
+                    *reinterpret_cast<u32x4*>(buf + ARRA + off) = bk;
+                    *reinterpret_cast<u32x4*>(buf + 2 * ARRA + off) = u ? q2.v1 : q2.v0;
+                }
+                return;
+            }
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int sh = 16 * (e & 1);
@@ -1916,6 +1969,20 @@ __global__ __launch_bounds__(64 * (D / 16), 2) void frame_step_kernel(ScanArgs a
             accu[i] = f32x4{0, 0, 0, 0};
         }
         auto mfma_blk = [&](const unsigned char* buf) {
+            if constexpr (TRK) {
+#pragma unroll
+                for (int ks = 0; ks < BTA / 32; ++ks) {
+                    const int kb = 32 * ks + 8 * g;
+                    const frag bx = tr_frag<ROWT>(buf + ARRA, 16 * wave, kb, r);       // beta rho K^T, rows e
+#pragma unroll
+                    for (int mt = 0; mt < RT; ++mt)                                    // G[c][e]
+                        io::mma(accg[mt], tr_frag<ROWT>(buf, 16 * mt, kb, r), bx);
+#pragma unroll
+                    for (int i = 0; i < RT; ++i)                                       // U^T[e][a]
+                        io::mma(accu[i], bx, tr_frag<ROWT>(buf + 2 * ARRA, 16 * i, kb, r));
+                }
+                return;
+            }
 #pragma unroll
             for (int ks = 0; ks < BTA / 32; ++ks) {
                 const frag bx = lds_frag<T, ROWA>(buf + ARRA, 16 * wave + r, ks, g);        // beta rho K^T, rows e
