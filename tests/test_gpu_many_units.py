@@ -109,3 +109,25 @@ def test_both_sides_of_the_intermediate_precision_threshold(N):
         ro, rS = oracle_ref(w, reverse=reverse)
         check(o, ro, "bf16", "O N%d" % N)
         check(S, rS, "bf16", "S_F N%d" % N)
+
+
+def test_bf16_intermediates_with_every_option():
+    """The bf16-intermediate regime (d 64, 150 tokens per frame) with gate
+    logits (beta = sigmoid / N summing to ~0.6 per frame), 300 frames (two
+    launch chunks, the state carried between them) and the state updated in
+    place, forward and reverse, against the oracle."""
+    w = inputs.make(1, 4, 300, 150, 64, dtype="bf16", seed=86, s0_std=0.05)
+    rng = np.random.default_rng(87)
+    beta_logit = rng.standard_normal(w.beta.shape).astype(np.float32) + 0.6
+    alpha_logit = (rng.standard_normal(w.alpha.shape) + 3.0).astype(np.float32)
+    q, k, v, _, _, s0 = inputs.to_torch(w, "cuda")
+    b = torch.from_numpy(beta_logit).cuda()
+    a = torch.from_numpy(alpha_logit).cuda()
+    for reverse in (False, True):
+        carry = s0.clone()
+        o, S = api.frame_scan_fwd(q, k, v, b, a, carry, S_final=carry, gates_are_logits=True, reverse=reverse)
+        torch.cuda.synchronize()
+        assert S.data_ptr() == carry.data_ptr()
+        ro, rS = oracle_ref(w, logits=True, beta=beta_logit, alpha=alpha_logit, reverse=reverse)
+        check(o.float().cpu().numpy(), ro, "bf16", "O rev=%d" % reverse)
+        check(S.cpu().numpy(), rS, "bf16", "S_F rev=%d" % reverse)
