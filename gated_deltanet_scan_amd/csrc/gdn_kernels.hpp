@@ -417,10 +417,11 @@ __device__ __forceinline__ int xcd_remap(int id, int per, int total) {
 // receives column c0 + i of rows kb .. kb+3: a column slice, i.e. the MFMA
 // operand fragment of the transposed array, read from its natural layout.
 // Token-major tiles (one row per token, D features of 2 bytes, 16-byte
-// chunks XOR-permuted by (2 row) mod 8 so that the four rows one group reads
-// fall in distinct banks, and each row's eight chunks in distinct banks for
-// the 16-byte writes) give the fragment for features f0 + r, tokens
-// kb .. kb + 7 of a 32-token step as two such reads.
+// chunks XOR-permuted by (2 row) mod 8, which spreads the four rows one group
+// reads over distinct chunk positions and keeps each row's eight chunks apart
+// for the 16-byte writes; the counters still show more bank-conflict cycles
+// than the transposing writes had) give the fragment for features f0 + r,
+// tokens kb .. kb + 7 of a 32-token step as two such reads.
 template <int ROWT>
 __device__ __forceinline__ int tok_off(int row, int f) {      // byte offset of feature f of token `row`
     return row * ROWT + ((((f >> 3) ^ (2 * row)) & 7) << 4) + ((f & 7) << 1);
