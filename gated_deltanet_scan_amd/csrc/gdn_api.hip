@@ -164,11 +164,12 @@ gdn_status check_desc(const gdn_desc* d, bool step, Plan* p, int fc_cap = gdn::k
     }
     // The forward scan's intermediates at larger shapes: U (frame_gram to the
     // recurrence) and the state planes (recurrence to the output pass) are
-    // stored in bf16 instead of fp32 and bf16 plus remainder codes, 25% fewer
-    // workspace bytes.  Each adds about one bf16 rounding (2^-9 relative) to
-    // a value the products already carry at that precision; at d >= 64 with
-    // at least 128 tokens per frame the measured error stays well inside the
-    // tolerance (O 3.3e-3, S_F 2.4e-3 relative at the full-minute shape, the
+    // stored in bf16 instead of fp32 and bf16 plus remainder codes: a third
+    // fewer workspace bytes touched.  Each adds about one bf16 rounding (2^-9
+    // relative) to a value the products already carry at that precision; at
+    // d >= 64 with at least 128 tokens per frame the error stays well inside
+    // the tolerance (measured against the fp64 reference at the full-minute
+    // shape: O 3.3e-3, S_F 2.3e-3 relative, every (b, h) within 3.4e-3; the
     // budget 5e-3).  Tiny frames keep the finer forms: there one token's
     // rounding is not averaged with others.
     p->lp = d->io_dtype != GDN_F32 && d->Dk >= 64 && d->N >= 128;
